@@ -1,0 +1,238 @@
+"""CPU oracle for the packed-MoE 4-bit decode FFN and the dense packed INT4 GEMV.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links this
+module; only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` do.  It shares no code with the HIP library under ``dequant_gemv_amd/``.
+
+Plain, slow and deliberately unfused: every step is the textbook definition, evaluated in
+float64 with numpy, one expert and one token at a time.  A matrix product is the only
+library primitive used.  Because every dequantized weight is exact (a code with at most
+3 significant bits times a bf16 scale with 8), the GPU path computes the same products;
+it differs from this oracle only in fp32 summation order and the final bf16 rounding.
+
+What each function follows (page titles as printed at the head of each page):
+
+* packed layout and nibble order -- FireEcho, "The Goliath Kernel: Why It's Fast": all
+  experts of a layer in one contiguous ``[E, K//2, N]`` buffer; the low nibble (``& 0xF``)
+  is taken before the high nibble (``>> 4``), dequantized by multiplying with a scale.
+* FP4 values -- FireEcho, "Quantization Formats" names the FP4 format only; its element
+  type is read as OCP Microscaling E2M1 (sign bit, 2 exponent bits with bias 1, 1 mantissa
+  bit; exponent field 0 is subnormal).
+* INT4 values -- symmetric, ``nibble - 8``; the page's simplified snippet multiplies the
+  raw nibble by the scale, which is not used (it is labelled a simplification).
+* group scales -- one bf16 scale per ``group`` consecutive K indices and per column.
+* expert IDs read per token -- FireEcho, "The Goliath Kernel" (a launch reads the expert
+  IDs and indexes the packed buffer); top-k on the raw logits, ties to the lower index,
+  weights = softmax over the selected k.
+* fused gate_up then SiLU(gate) * up -- FireEcho, "Speed Optimization History" step 2
+  (gate and up as one matmul); FastInfer, "Confirmed elementwise SwiGLU scheduling"
+  (the fused operation is SiLU(gate) * up).  Columns ``[0, I)`` are gate, ``[I, 2I)`` up.
+* dense GEMV -- FastInfer, "Specialized matrix-vector result" (a vector times a stored
+  weight matrix, FP32-or-better products and reductions); the weight is the packed INT4
+  ``[K/2, N]`` layout above with group 128.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against hand-worked decode
+tables, closed forms, library special cases, invariants and exact-rational brute force.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+FMT_INT4 = 0
+FMT_FP4 = 1
+
+
+# ------------------------------------------------------------------------------------
+# element decode
+# ------------------------------------------------------------------------------------
+def e2m1_value(code: int) -> float:
+    """OCP MX E2M1: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa.
+    Exponent field 0 is subnormal: value = mantissa * 0.5."""
+    sign = (code >> 3) & 1
+    exp = (code >> 1) & 3
+    man = code & 1
+    if exp == 0:
+        mag = 0.5 * man
+    else:
+        mag = (2.0 ** (exp - 1)) * (1.0 + 0.5 * man)
+    return math.copysign(mag, -1.0 if sign else 1.0)
+
+
+def int4_value(code: int) -> float:
+    """Symmetric INT4: stored nibble n means n - 8."""
+    return float(code - 8)
+
+
+def decode_table(fmt: int) -> np.ndarray:
+    fn = e2m1_value if fmt == FMT_FP4 else int4_value
+    if fmt not in (FMT_FP4, FMT_INT4):
+        raise ValueError(fmt)
+    return np.array([fn(c) for c in range(16)], dtype=np.float64)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact: bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round_to_bits(v) -> np.ndarray:
+    """Round float64 values to bfloat16, nearest-even, straight from float64 (one
+    rounding); return uint16 bit patterns.  Used only to form a chained layer's input."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                       # v = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                  # below 2**-126 the bf16 quantum is fixed
+    quantum = np.ldexp(1.0, e - 8)           # 8 significant bits
+    r = np.rint(v / quantum) * quantum       # exact scaling; rint is ties-to-even
+    f32 = r.astype(np.float32)               # exact: r fits bf16 (finite inputs)
+    return (f32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """Bytes ``[..., K/2, N]`` -> codes ``[..., K, N]``: byte row r gives K index 2r from
+    its low nibble and 2r+1 from its high nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    shape = p.shape[:-2] + (2 * p.shape[-2], p.shape[-1])
+    codes = np.empty(shape, dtype=np.uint8)
+    codes[..., 0::2, :] = p & 0x0F
+    codes[..., 1::2, :] = p >> 4
+    return codes
+
+
+def dequant(packed: np.ndarray, scale_bits: np.ndarray, group: int, fmt: int,
+            cols: Optional[np.ndarray] = None) -> np.ndarray:
+    """Dequantize one packed matrix ``[K/2, N]`` with scales ``[K/G, N]`` into float64
+    ``[K, N]``: ``W[k, n] = value(code[k, n]) * scale[k // group, n]``.
+    ``cols`` optionally selects output columns (for sampled checks of large N)."""
+    if cols is not None:
+        packed = packed[:, cols]
+        scale_bits = scale_bits[:, cols]
+    codes = unpack_codes(packed)
+    K = codes.shape[0]
+    assert K % group == 0 and scale_bits.shape[0] == K // group
+    vals = decode_table(fmt)[codes]
+    scales = np.repeat(bf16_to_f64(scale_bits), group, axis=0)
+    return vals * scales
+
+
+# ------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------
+def topk_route(logits: np.ndarray, k: int):
+    """Per token: the k largest raw logits (ties to the lower expert index; -0.0 and +0.0
+    tie), in rank order, and weights = softmax over those k logits.
+    Returns ``(ids int32 [T, k], weights float64 [T, k])``."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    if not np.all(np.isfinite(lg)):
+        raise ValueError("logits must be finite")
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    for t in range(T):
+        row = [float(v) for v in lg[t]]
+        order = sorted(range(E), key=lambda e: (-row[e], e))[:k]
+        sel = np.array([row[e] for e in order], dtype=np.float64)
+        ex = np.exp(sel - sel[0])
+        ids[t] = order
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
+# ------------------------------------------------------------------------------------
+# expert FFN
+# ------------------------------------------------------------------------------------
+def silu(g: np.ndarray) -> np.ndarray:
+    """SiLU(g) = g / (1 + exp(-g)); for very negative g exp overflows to inf and the
+    quotient is (-)0, which is the correctly rounded limit."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+class ExpertCache:
+    """Dequantized experts of one layer, built on first use (the oracle never fuses)."""
+
+    def __init__(self, w_gu, s_gu, w_d, s_d, group: int, fmt: int):
+        self.w_gu, self.s_gu, self.w_d, self.s_d = w_gu, s_gu, w_d, s_d
+        self.group, self.fmt = group, fmt
+        self._gu: Dict[int, np.ndarray] = {}
+        self._d: Dict[int, np.ndarray] = {}
+
+    def gate_up(self, e: int) -> np.ndarray:
+        if e not in self._gu:
+            self._gu[e] = dequant(self.w_gu[e], self.s_gu[e], self.group, self.fmt)
+        return self._gu[e]
+
+    def down(self, e: int) -> np.ndarray:
+        if e not in self._d:
+            self._d[e] = dequant(self.w_d[e], self.s_d[e], self.group, self.fmt)
+        return self._d[e]
+
+
+def expert_ffn(x_row: np.ndarray, W_gu: np.ndarray, W_d: np.ndarray) -> np.ndarray:
+    """One expert on one token: [g | u] = x W_gu; h = SiLU(g) * u; y = h W_d."""
+    I = W_gu.shape[1] // 2
+    gu = x_row @ W_gu
+    g, u = gu[:I], gu[I:]
+    h = silu(g) * u
+    return h @ W_d
+
+
+def moe_ffn(x_bits, ids, weights, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
+            residual_bits=None, cache: Optional[ExpertCache] = None) -> np.ndarray:
+    """out[t] = residual[t] + sum_j weights[t, j] * FFN_{ids[t, j]}(x[t]), j ascending.
+    Returns the unrounded float64 ``[T, H]``."""
+    x = bf16_to_f64(x_bits)
+    T, H = x.shape
+    ids = np.asarray(ids)
+    wts = np.asarray(weights, dtype=np.float64)
+    c = cache or ExpertCache(w_gu, s_gu, w_d, s_d, group, fmt)
+    out = np.zeros((T, H), dtype=np.float64) if residual_bits is None else \
+        bf16_to_f64(residual_bits).copy()
+    for t in range(T):
+        acc = np.zeros(H, dtype=np.float64)
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            acc += wts[t, j] * expert_ffn(x[t], c.gate_up(e), c.down(e))
+        out[t] += acc
+    return out
+
+
+def moe_layer(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
+              residual_bits=None, cache: Optional[ExpertCache] = None):
+    """Route, then the expert FFN and the weighted combine.
+    Returns ``(out float64 [T, H], ids, weights)``."""
+    ids, w = topk_route(logits, k)
+    out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache)
+    return out, ids, w
+
+
+def moe_stack(x_bits, layers: Sequence, k: int, group: int, fmt: int):
+    """Chained layers with a residual stream: x_{l+1} = bf16(x_l + MoE_l(x_l)).
+    ``layers`` yields objects with ``logits, w_gu, s_gu, w_d, s_d``.
+    Returns ``(bits of the last layer's input, float64 output of the last layer)``."""
+    x = np.asarray(x_bits, dtype=np.uint16)
+    out = None
+    for L in layers:
+        out, _, _ = moe_layer(x, L.logits, k, L.w_gu, L.s_gu, L.w_d, L.s_d, group, fmt,
+                              residual_bits=x)
+        last_in = x
+        x = bf16_round_to_bits(out)
+    return last_in, out
+
+
+# ------------------------------------------------------------------------------------
+# dense packed GEMV
+# ------------------------------------------------------------------------------------
+def packed_gemv(x_bits, w_packed, s_bits, group: int, fmt: int = FMT_INT4,
+                cols: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[t, n] = sum_k x[t, k] * W[k, n] with W the dequantized packed matrix.
+    Returns the unrounded float64 ``[T, N]`` (or ``[T, len(cols)]``)."""
+    x = bf16_to_f64(x_bits)
+    W = dequant(w_packed, s_bits, group, fmt, cols)
+    return x @ W

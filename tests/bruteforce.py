@@ -1,0 +1,102 @@
+"""Exact-rational brute force for tiny MoE layers and GEMVs (test-side only).
+
+Independent of ``oracle/``: element values come from the hand-typed golden decode table,
+gate/up and GEMV sums are exact ``fractions.Fraction`` arithmetic, and only SiLU, the
+softmax and the final conversion use float64 (``math.exp``, ``math.fsum``).  Top-k is a
+full sort of all (logit, index) pairs.  Pure-Python loops: keep shapes tiny.
+"""
+from __future__ import annotations
+
+import math
+import os
+import struct
+from fractions import Fraction
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def golden_tables():
+    """{'int4': [Fraction]*16, 'fp4': [Fraction]*16, 'fp4_signbit': [bool]*16}"""
+    int4, fp4, neg = [], [], []
+    with open(os.path.join(_HERE, "golden", "decode_tables.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            n, a, b = line.split()
+            assert int(n) == len(int4)
+            int4.append(Fraction(a))
+            fp4.append(Fraction(b))
+            neg.append(b.startswith("-"))
+    return {"int4": int4, "fp4": fp4, "fp4_signbit": neg}
+
+
+_TABLES = golden_tables()
+
+
+def bf16_fraction(bits: int) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0])
+
+
+def dequant_exact(packed, scales, group: int, fmt: str):
+    """packed [K/2][N] bytes, scales [K/G][N] bf16 bits -> exact W [K][N] (Fractions)."""
+    tab = _TABLES[fmt]
+    Kp, N = len(packed), len(packed[0])
+    W = [[None] * N for _ in range(2 * Kp)]
+    for r in range(Kp):
+        for n in range(N):
+            b = int(packed[r][n])
+            for k, code in ((2 * r, b & 0xF), (2 * r + 1, b >> 4)):
+                W[k][n] = tab[code] * bf16_fraction(scales[k // group][n])
+    return W
+
+
+def topk_exact(row, k: int):
+    pairs = sorted(((Fraction(float(v)), e) for e, v in enumerate(row)),
+                   key=lambda p: (-p[0], p[1]))[:k]
+    ids = [e for _, e in pairs]
+    l0 = float(pairs[0][0])
+    ex = [math.exp(float(v) - l0) for v, _ in pairs]
+    s = math.fsum(ex)
+    return ids, [v / s for v in ex]
+
+
+def moe_exact(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: str,
+              residual_bits=None):
+    """Returns (out [T][H] float64, ids [T][k], weights [T][k])."""
+    T, H = len(x_bits), len(x_bits[0])
+    E = len(w_gu)
+    I = len(w_gu[0][0]) // 2
+    Wgu = [dequant_exact(w_gu[e], s_gu[e], group, fmt) for e in range(E)]
+    Wd = [dequant_exact(w_d[e], s_d[e], group, fmt) for e in range(E)]
+    out, all_ids, all_w = [], [], []
+    for t in range(T):
+        x = [bf16_fraction(v) for v in x_bits[t]]
+        ids, wts = topk_exact(logits[t], k)
+        ys = []
+        for e in ids:
+            g = [sum(x[c] * Wgu[e][c][n] for c in range(H)) for n in range(I)]
+            u = [sum(x[c] * Wgu[e][c][I + n] for c in range(H)) for n in range(I)]
+            h = [float(g[n]) / (1.0 + math.exp(-float(g[n]))) * float(u[n]) for n in range(I)]
+            hf = [Fraction(v) for v in h]
+            ys.append([float(sum(hf[n] * Wd[e][n][m] for n in range(I))) for m in range(H)])
+        row = []
+        for m in range(H):
+            terms = [wts[j] * ys[j][m] for j in range(len(ids))]
+            if residual_bits is not None:
+                terms.append(float(bf16_fraction(residual_bits[t][m])))
+            row.append(math.fsum(terms))
+        out.append(row)
+        all_ids.append(ids)
+        all_w.append(wts)
+    return out, all_ids, all_w
+
+
+def gemv_exact(x_bits, packed, scales, group: int, fmt: str = "int4"):
+    W = dequant_exact(packed, scales, group, fmt)
+    K, N = len(W), len(W[0])
+    out = []
+    for xr in x_bits:
+        x = [bf16_fraction(v) for v in xr]
+        out.append([float(sum(x[k] * W[k][n] for k in range(K))) for n in range(N)])
+    return out
