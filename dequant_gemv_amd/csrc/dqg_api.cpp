@@ -1,0 +1,284 @@
+// C-ABI layer: argument checks, workspace layout, launch geometry.  No device memory is
+// allocated or read here; every call only enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/dqg.h"
+#include "dqg_internal.hpp"
+
+namespace {
+
+using dqg::GemvArgs;
+using dqg::MoeArgs;
+
+constexpr int kMaxE = 4096;
+constexpr int kMaxK = 32;
+constexpr int kMaxTK = 65536;
+constexpr int kTargetWG = 512;   // workgroups per launch to aim for (2 per CU)
+constexpr int kMinBlocksPerWG = 8;
+constexpr int kMfmaMinTokens = INT_MAX;  // matrix-core tiles: not enabled in this build
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct MoePlan {
+  int T, H, I, E, k, TK, A;
+  int tiles_gu, tiles_dn, S_gu, S_dn, nt;
+  size_t o_err, o_nact, o_actexp, o_actoff, o_slots, o_nvalid, o_ids, o_wts, o_cnt, o_h, o_pgu,
+      o_pdn, total;
+  int n_cnt_gu, n_cnt_dn;
+};
+
+int pick_split(int units, int nblk) {
+  int S = (kTargetWG + units - 1) / units;
+  S = std::min(S, std::max(1, nblk / kMinBlocksPerWG));
+  return std::max(1, S);
+}
+
+bool moe_sizes_ok(int T, int H, int I, int E, int k) {
+  if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1) return false;
+  if (E > kMaxE || k > kMaxK || k > E) return false;
+  if ((long long)T * k > kMaxTK) return false;
+  if (H % 64 || I % 64) return false;
+  if ((long long)H * I > (1LL << 31)) return false;
+  return true;
+}
+
+MoePlan plan_moe(int T, int H, int I, int E, int k) {
+  MoePlan p{};
+  p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
+  p.TK = T * k;
+  p.A = std::min(E, p.TK);
+  p.tiles_gu = I / 64;
+  p.tiles_dn = H / 64;
+  p.S_gu = pick_split(p.A * p.tiles_gu, H / 32);
+  p.S_dn = pick_split(p.A * p.tiles_dn, I / 32);
+  p.nt = (T == 1) ? 1 : (T == 2 ? 2 : 4);
+  p.n_cnt_gu = p.A * p.tiles_gu;
+  p.n_cnt_dn = T * p.tiles_dn;
+  size_t o = 0;
+  p.o_err = o;     o += 256;
+  p.o_nact = o;    o += 256;
+  p.o_actexp = o;  o = up256(o + sizeof(int) * p.A);
+  p.o_actoff = o;  o = up256(o + sizeof(int) * (p.A + 1));
+  p.o_slots = o;   o = up256(o + sizeof(int) * p.TK);
+  p.o_nvalid = o;  o = up256(o + sizeof(int) * T);
+  p.o_ids = o;     o = up256(o + sizeof(int) * p.TK);
+  p.o_wts = o;     o = up256(o + sizeof(float) * p.TK);
+  p.o_cnt = o;     o = up256(o + sizeof(unsigned) * (p.n_cnt_gu + p.n_cnt_dn));
+  p.o_h = o;       o = up256(o + sizeof(float) * (size_t)p.TK * I);
+  p.o_pgu = o;     o = up256(o + (p.S_gu > 1 ? sizeof(float) * (size_t)p.S_gu * p.TK * 2 * I : 0));
+  p.o_pdn = o;     o = up256(o + sizeof(float) * (size_t)p.S_dn * p.TK * H);
+  p.total = o;
+  return p;
+}
+
+int check_moe_common(const uint16_t* x, int T, int H, int I, int E, int k, const uint8_t* wgu,
+                     const uint16_t* sgu, const uint8_t* wd, const uint16_t* sd, int group,
+                     int format, const uint16_t* res, uint16_t* out, void* ws,
+                     size_t ws_bytes) {
+  if (!x || !wgu || !sgu || !wd || !sd || !out) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return DQG_ERR_INVALID_ARG;
+  const int fmt = format & 0xFF;
+  const int flags = format & ~0xFF;
+  if (fmt != DQG_FMT_INT4 && fmt != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;
+  if (flags & ~(DQG_PATH_FORCE_GEMV | DQG_PATH_FORCE_MFMA | DQG_PATH_NO_FUSED))
+    return DQG_ERR_UNSUPPORTED;
+  if ((flags & DQG_PATH_FORCE_GEMV) && (flags & DQG_PATH_FORCE_MFMA)) return DQG_ERR_INVALID_ARG;
+  if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
+  if (!moe_sizes_ok(T, H, I, E, k)) return DQG_ERR_UNSUPPORTED;
+  if (H % group || I % group) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(wgu) || !aligned16(sgu) || !aligned16(wd) || !aligned16(sd) ||
+      !aligned16(out) || (res && !aligned16(res)))
+    return DQG_ERR_MISALIGNED;
+  if (!ws) return DQG_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DQG_ERR_MISALIGNED;
+  if (ws_bytes < plan_moe(T, H, I, E, k).total) return DQG_ERR_WORKSPACE;
+  return DQG_OK;
+}
+
+MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
+                      const uint16_t* sgu, const uint8_t* wd, const uint16_t* sd, int group,
+                      int format, const uint16_t* res, uint16_t* out, void* ws) {
+  char* b = static_cast<char*>(ws);
+  MoeArgs a{};
+  a.x = x; a.T = p.T; a.H = p.H; a.I = p.I; a.E = p.E; a.k = p.k; a.group = group;
+  a.fmt = format & 0xFF;
+  a.wgu = wgu; a.sgu = sgu; a.wd = wd; a.sd = sd; a.res = res; a.out = out;
+  a.ws.err = reinterpret_cast<int*>(b + p.o_err);
+  a.ws.n_active = reinterpret_cast<int*>(b + p.o_nact);
+  a.ws.act_expert = reinterpret_cast<int*>(b + p.o_actexp);
+  a.ws.act_off = reinterpret_cast<int*>(b + p.o_actoff);
+  a.ws.slot_list = reinterpret_cast<int*>(b + p.o_slots);
+  a.ws.nvalid = reinterpret_cast<int*>(b + p.o_nvalid);
+  a.ws.ids = reinterpret_cast<int32_t*>(b + p.o_ids);
+  a.ws.wts = reinterpret_cast<float*>(b + p.o_wts);
+  a.ws.cnt = reinterpret_cast<unsigned*>(b + p.o_cnt);
+  a.ws.n_cnt = p.n_cnt_gu + p.n_cnt_dn;
+  a.ws.cnt_gu = a.ws.cnt;
+  a.ws.cnt_dn = a.ws.cnt + p.n_cnt_gu;
+  a.ws.cnt_fx = nullptr;
+  a.ws.h = reinterpret_cast<float*>(b + p.o_h);
+  a.ws.part_gu = reinterpret_cast<float*>(b + p.o_pgu);
+  a.ws.part_dn = reinterpret_cast<float*>(b + p.o_pdn);
+  a.S_gu = p.S_gu;
+  a.S_dn = p.S_dn;
+  const int flags = format & ~0xFF;
+  a.mfma_min = (flags & DQG_PATH_FORCE_GEMV) ? INT_MAX
+               : (flags & DQG_PATH_FORCE_MFMA) ? 1
+                                               : kMfmaMinTokens;
+  return a;
+}
+
+int run_moe(MoeArgs& a, const MoePlan& p, const float* logits, hipStream_t st) {
+  hipError_t e = dqg::launch_schedule(a, logits, st);
+  if (e != hipSuccess) return DQG_ERR_HIP;
+  e = dqg::launch_moe_valu(a, p.A, p.nt, st);
+  if (e != hipSuccess) return DQG_ERR_HIP;
+  return DQG_OK;
+}
+
+struct GemvPlan {
+  int tiles, S, nt;
+  size_t o_cnt, o_part, total;
+};
+
+GemvPlan plan_gemv(int T, int K, int N) {
+  GemvPlan g{};
+  g.tiles = N / 64;
+  g.S = pick_split(g.tiles, K / 32);
+  g.nt = (T == 1) ? 1 : (T == 2 ? 2 : 4);
+  if (g.S == 1) return g;
+  size_t o = 0;
+  g.o_cnt = o;  o = up256(o + sizeof(unsigned) * g.tiles);
+  g.o_part = o; o = up256(o + sizeof(float) * (size_t)g.S * T * N);
+  g.total = o;
+  return g;
+}
+
+bool gemv_sizes_ok(int T, int K, int N, int group) {
+  if (T < 1 || K < 2 || N < 1) return false;
+  if (group != 32 && group != 128) return false;
+  if (K % group || N % 64) return false;
+  if (T > 4096 || (long long)K * N > (1LL << 40)) return false;
+  if (K > 65536) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dqg_abi_version(void) { return DQG_ABI_VERSION; }
+
+const char* dqg_status_string(int status) {
+  switch (status) {
+    case DQG_OK: return "DQG_OK";
+    case DQG_ERR_INVALID_ARG: return "DQG_ERR_INVALID_ARG";
+    case DQG_ERR_UNSUPPORTED: return "DQG_ERR_UNSUPPORTED";
+    case DQG_ERR_MISALIGNED: return "DQG_ERR_MISALIGNED";
+    case DQG_ERR_WORKSPACE: return "DQG_ERR_WORKSPACE";
+    case DQG_ERR_HIP: return "DQG_ERR_HIP";
+    default: return "DQG_ERR_UNKNOWN";
+  }
+}
+
+int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
+               hipStream_t stream) {
+  if (!logits || !ids || !weights) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || E < 1 || k < 1 || k > E) return DQG_ERR_INVALID_ARG;
+  if (E > kMaxE || k > kMaxK) return DQG_ERR_UNSUPPORTED;
+  if (((uintptr_t)logits & 3u) || ((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u))
+    return DQG_ERR_MISALIGNED;
+  return dqg::launch_topk(logits, T, E, k, ids, weights, stream) == hipSuccess ? DQG_OK
+                                                                                : DQG_ERR_HIP;
+}
+
+size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (!moe_sizes_ok(T, H, I, E, k)) return 0;
+  return plan_moe(T, H, I, E, k).total;
+}
+
+int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int32_t* ids,
+                const float* weights, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                const uint8_t* w_down, const uint16_t* s_down, int group, int format,
+                const uint16_t* residual, uint16_t* out, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (!ids || !weights) return DQG_ERR_INVALID_ARG;
+  int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
+                            format, residual, out, workspace, workspace_bytes);
+  if (rc != DQG_OK) return rc;
+  if (((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u)) return DQG_ERR_MISALIGNED;
+  const MoePlan p = plan_moe(T, H, I, E, k);
+  MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
+                            out, workspace);
+  a.ids = ids;
+  a.wts = weights;
+  return run_moe(a, p, nullptr, stream);
+}
+
+int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
+                  const uint8_t* w_gate_up, const uint16_t* s_gate_up, const uint8_t* w_down,
+                  const uint16_t* s_down, int group, int format, const uint16_t* residual,
+                  uint16_t* out, int32_t* ids_out, float* weights_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (!logits) return DQG_ERR_INVALID_ARG;
+  int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
+                            format, residual, out, workspace, workspace_bytes);
+  if (rc != DQG_OK) return rc;
+  if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
+    return DQG_ERR_MISALIGNED;
+  const MoePlan p = plan_moe(T, H, I, E, k);
+  MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
+                            out, workspace);
+  a.ids_w = ids_out ? ids_out : a.ws.ids;
+  a.wts_w = weights_out ? weights_out : a.ws.wts;
+  a.ids = a.ids_w;
+  a.wts = a.wts_w;
+  return run_moe(a, p, logits, stream);
+}
+
+size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group) {
+  if (!gemv_sizes_ok(T, K, N, group)) return 0;
+  return plan_gemv(T, K, N).total;
+}
+
+int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
+                     const uint16_t* s, int group, uint16_t* y, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !w || !s || !y) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (!gemv_sizes_ok(T, K, N, group)) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return DQG_ERR_MISALIGNED;
+  GemvPlan gp = plan_gemv(T, K, N);
+  if (gp.S > 1 && (!workspace || workspace_bytes < gp.total)) {
+    if (workspace) return DQG_ERR_WORKSPACE;
+    gp.S = 1;  // no workspace: one workgroup per column tile
+  }
+  if (workspace && !aligned16(workspace)) return DQG_ERR_MISALIGNED;
+  GemvArgs g{};
+  g.x = x; g.T = T; g.K = K; g.N = N; g.group = group; g.w = w; g.s = s; g.y = y; g.S = gp.S;
+  if (gp.S > 1) {
+    char* b = static_cast<char*>(workspace);
+    g.cnt = reinterpret_cast<unsigned*>(b + gp.o_cnt);
+    g.part = reinterpret_cast<float*>(b + gp.o_part);
+  }
+  return dqg::launch_gemv(g, gp.nt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+}
+
+int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                       int format, float* out, hipStream_t stream) {
+  if (!w || !s || !out) return DQG_ERR_INVALID_ARG;
+  if (K < 2 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (format != DQG_FMT_INT4 && format != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;
+  if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
+  if (K % group || N % 16) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(w) || !aligned16(s) || !aligned16(out)) return DQG_ERR_MISALIGNED;
+  return dqg::launch_dequant(w, s, K, N, group, format, out, stream) == hipSuccess ? DQG_OK
+                                                                                     : DQG_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal host/device structures shared by the kernels and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dqg {
+
+// Device-side views into the caller's MoE workspace (laid out by plan_moe).
+struct MoeWs {
+  int* err;             // [1]  sticky error word (1: an expert id outside [0, E) was seen)
+  int* n_active;        // [1]  number of distinct valid experts this call
+  int* act_expert;      // [A]  expert id of active index a (ascending ids)
+  int* act_off;         // [A+1] start of expert a's slots in slot_list
+  int* slot_list;       // [T*k] slots (t*k + j) grouped by expert, ascending within an expert
+  int* nvalid;          // [T]  number of valid slots of token t
+  int32_t* ids;         // [T*k] routing written by the layer call when the caller passes none
+  float* wts;           // [T*k]
+  unsigned* cnt;        // all counters (n_cnt of them), zeroed by the schedule kernel
+  int n_cnt;
+  unsigned* cnt_gu;     // [A * I/64]   gate_up split completion counters
+  unsigned* cnt_dn;     // [T * H/64]   down/combine completion counters
+  unsigned* cnt_fx;     // [fused-layer counters]
+  float* h;             // [T*k, I]     SiLU(gate) * up
+  float* part_gu;       // [S_gu, T*k, 2I] gate/up split partials
+  float* part_dn;       // [S_dn, T*k, H]  down partials per slot
+};
+
+struct MoeArgs {
+  const uint16_t* x;
+  int T, H, I, E, k, group, fmt;
+  const int32_t* ids;   // routing read by the expert kernels
+  const float* wts;
+  int32_t* ids_w;       // routing written by the schedule kernel (layer call)
+  float* wts_w;
+  const uint8_t* wgu;
+  const uint16_t* sgu;
+  const uint8_t* wd;
+  const uint16_t* sd;
+  const uint16_t* res;
+  uint16_t* out;
+  MoeWs ws;
+  int S_gu, S_dn;
+  int mfma_min;         // experts with at least this many tokens use the MFMA tiles
+};
+
+struct GemvArgs {
+  const uint16_t* x;
+  int T, K, N, group;
+  const uint8_t* w;
+  const uint16_t* s;
+  uint16_t* y;
+  float* part;          // [S, T, N] split partials (S > 1)
+  unsigned* cnt;        // [N/64] split completion counters (S > 1)
+  int S;
+};
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
+                       hipStream_t st);
+hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st);
+hipError_t launch_moe_valu(const MoeArgs& a, int A, int nt, hipStream_t st);
+hipError_t launch_gemv(const GemvArgs& g, int nt, hipStream_t st);
+hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
+                          float* out, hipStream_t st);
+
+}  // namespace dqg

@@ -1,0 +1,631 @@
+// HIP kernels for gfx950: top-k routing, the device-built expert schedule, the packed
+// 4-bit MoE expert FFN (fused gate_up + SiLU*up, down + top-k combine) and the dense
+// packed INT4 GEMV.  Host launchers at the bottom; the C ABI lives in dqg_api.cpp.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dqg_device.hpp"
+#include "dqg_internal.hpp"
+
+namespace dqg {
+
+// =====================================================================================
+// top-k routing: one wavefront per token
+// =====================================================================================
+// a ranks before b: larger logit first, equal logits -> lower expert index first
+// (-0.0 == +0.0 compares equal, so the index decides).
+__device__ __forceinline__ bool ranks_before(float av, int ae, float bv, int be) {
+  return av > bv || (av == bv && ae < be);
+}
+
+// Selects the k best (logit, index) pairs of `row` in rank order; lane j < k returns
+// pair j in (*v, *e).  Each round takes the best pair that ranks after the previous
+// round's pair, so no selection mask is needed.
+template <int CACHE>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
+                                          float* my_v, int* my_e, float* top_v) {
+  float cache[CACHE > 0 ? CACHE : 1];
+  if (CACHE > 0) {
+#pragma unroll
+    for (int i = 0; i < CACHE; ++i) {
+      const int e = lane + 64 * i;
+      cache[i] = (e < E) ? row[e] : 0.0f;
+    }
+  }
+  float pv = __builtin_inff();
+  int pe = -1;
+  *my_v = 0.0f;
+  *my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = -__builtin_inff();
+    int be = 0x7FFFFFFF;
+    if (CACHE > 0) {
+#pragma unroll
+      for (int i = 0; i < CACHE; ++i) {
+        const int e = lane + 64 * i;
+        const float v = cache[i];
+        if (e < E && ranks_before(pv, pe, v, e) && ranks_before(v, e, bv, be)) {
+          bv = v;
+          be = e;
+        }
+      }
+    } else {
+      for (int e = lane; e < E; e += 64) {
+        const float v = row[e];
+        if (ranks_before(pv, pe, v, e) && ranks_before(v, e, bv, be)) {
+          bv = v;
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ranks_before(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (j == 0) *top_v = bv;
+    if (lane == j) {
+      *my_v = bv;
+      *my_e = be;
+    }
+    pv = bv;
+    pe = be;
+  }
+}
+
+// Softmax over the k selected logits (top logit subtracted), lanes j < k hold theirs.
+__device__ __forceinline__ float wave_softmax_k(float my_v, float top_v, int k, int lane) {
+  const float ex = (lane < k) ? expf(my_v - top_v) : 0.0f;
+  float s = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  return ex / s;
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int lane, int32_t* ids, float* wts) {
+  const float* row = logits + (size_t)t * E;
+  float my_v, top_v;
+  int my_e;
+  if (E <= 512)
+    wave_topk<8>(row, E, k, lane, &my_v, &my_e, &top_v);
+  else
+    wave_topk<0>(row, E, k, lane, &my_v, &my_e, &top_v);
+  const float w = wave_softmax_k(my_v, top_v, k, lane);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_e;
+    wts[(size_t)t * k + lane] = w;
+  }
+}
+
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token(logits, t, E, k, lane, ids, wts);
+}
+
+// =====================================================================================
+// schedule: (optional routing) + per-expert slot lists, one workgroup
+// =====================================================================================
+constexpr int SCHED_THREADS = 1024;
+
+// exclusive scan of n (<= 4 * SCHED_THREADS) ints in LDS, in place; returns the total
+__device__ int block_exclusive_scan(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + SCHED_THREADS - 1) / SCHED_THREADS;
+  const int b = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) local += a[b + i];
+  tmp[tid] = local;
+  __syncthreads();
+  // Hillis-Steele over SCHED_THREADS partials
+  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+    const int v = (tid >= off) ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  int run = (tid > 0) ? tmp[tid - 1] : 0;
+  const int total = tmp[SCHED_THREADS - 1];
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      const int v = a[b + i];
+      a[b + i] = run;
+      run += v;
+    }
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, const float* logits) {
+  extern __shared__ int sm[];
+  const int E = a.E, T = a.T, k = a.k, TK = T * k;
+  int* cnt = sm;                         // [E] slots per expert
+  int* aidx = cnt + E;                   // [E] active index of each expert
+  int* base = aidx + E;                  // [E] first slot position of each expert
+  int* tmp = base + E;                   // [SCHED_THREADS]
+  int* chunk_ids = tmp + SCHED_THREADS;  // [SCHED_THREADS]
+  int* s_flag = chunk_ids + SCHED_THREADS;
+  const int tid = threadIdx.x;
+
+  if (logits) {  // routing from logits, one wave per token
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int t = wv; t < T; t += SCHED_THREADS / 64)
+      route_token(logits, t, E, k, lane, a.ids_w, a.wts_w);
+    __threadfence_block();
+    __syncthreads();
+  }
+  const int32_t* ids = a.ids;
+  // reset the cross-workgroup counters used by the expert kernels of this call
+  for (int i = tid; i < a.ws.n_cnt; i += SCHED_THREADS) a.ws.cnt[i] = 0u;
+  for (int i = tid; i < E; i += SCHED_THREADS) cnt[i] = 0;
+  if (tid == 0) *s_flag = 0;
+  __syncthreads();
+  for (int i = tid; i < TK; i += SCHED_THREADS) {
+    const int e = ids[i];
+    if (e >= 0 && e < E)
+      atomicAdd(&cnt[e], 1);
+    else
+      *s_flag = 1;
+  }
+  for (int t = tid; t < T; t += SCHED_THREADS) {
+    int nv = 0;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      nv += (e >= 0 && e < E);
+    }
+    a.ws.nvalid[t] = nv;
+  }
+  __syncthreads();
+  if (tid == 0 && *s_flag) atomicOr(a.ws.err, 1);
+  // active experts in ascending id order; slot offsets per expert
+  for (int i = tid; i < E; i += SCHED_THREADS) {
+    aidx[i] = cnt[i] > 0 ? 1 : 0;
+    base[i] = cnt[i];
+  }
+  __syncthreads();
+  const int n_active = block_exclusive_scan(aidx, E, tmp);
+  const int total = block_exclusive_scan(base, E, tmp);
+  for (int i = tid; i < E; i += SCHED_THREADS)
+    if (cnt[i] > 0) {
+      a.ws.act_expert[aidx[i]] = i;
+      a.ws.act_off[aidx[i]] = base[i];
+    }
+  if (tid == 0) {
+    *a.ws.n_active = n_active;
+    a.ws.act_off[n_active] = total;
+  }
+  __syncthreads();
+  // stable placement: slots of one expert keep ascending slot order
+  for (int c0 = 0; c0 < TK; c0 += SCHED_THREADS) {
+    const int i = c0 + tid;
+    const int e = (i < TK) ? ids[i] : -1;
+    chunk_ids[tid] = e;
+    __syncthreads();
+    if (e >= 0 && e < E) {
+      int rank = 0;
+      for (int q = 0; q < tid; ++q) rank += (chunk_ids[q] == e);
+      a.ws.slot_list[base[e] + rank] = i;
+    }
+    __syncthreads();
+    if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+    __syncthreads();
+  }
+  // tokens with no valid slot: out = residual (or zero)
+  for (int t = 0; t < T; ++t) {
+    if (a.ws.nvalid[t] != 0) continue;
+    for (int m = tid; m < a.H; m += SCHED_THREADS)
+      a.out[(size_t)t * a.H + m] = a.res ? a.res[(size_t)t * a.H + m] : (uint16_t)0;
+  }
+}
+
+// =====================================================================================
+// reductions over the row-lanes of a workgroup
+// =====================================================================================
+// Lanes that share (lane % CPR) own the same columns; sum them inside the wave.
+template <int CPR>
+__device__ __forceinline__ float wave_sum_rowlanes(float v) {
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// acc[NT][16] of every lane -> red[wave][t][ch*16 + j] (wave-reduced), then the caller
+// sums over waves.
+template <int CPR, int NT>
+__device__ __forceinline__ void reduce_to_lds(float (&acc)[NT][16], float* red, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, ch = lane % CPR;
+  constexpr int COLS = CPR * 16;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float v = wave_sum_rowlanes<CPR>(acc[t][j]);
+      if (lane < CPR) red[(wv * NT + t) * COLS + ch * 16 + j] = v;
+    }
+}
+
+// =====================================================================================
+// gate_up + SwiGLU (vector-ALU tiles)
+// =====================================================================================
+// Grid: x = 64-wide h tile, y = K split, z = active-expert index.  A workgroup owns h
+// columns [n0, n0+64): 64 gate columns and the matching 64 up columns (lanes 0-3 and 4-7
+// of each row), 32 row-lanes walk the K blocks of its split.  Every token routed to the
+// expert is processed (NT at a time), so each weight byte is read once per call.
+constexpr int GU_THREADS = 256, GU_CPR = 8, GU_RL = GU_THREADS / GU_CPR, GU_WAVES = 4;
+
+template <int FMT, int NT>
+__global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
+  constexpr int XM = (FMT == FMT_FP4) ? X_BF16 : X_F16;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int act = blockIdx.z;
+  if (act >= *a.ws.n_active) return;
+  const int beg = a.ws.act_off[act];
+  const int cnt = a.ws.act_off[act + 1] - beg;
+  if (cnt >= a.mfma_min) return;  // matrix-core tiles own this expert
+  const int e = a.ws.act_expert[act];
+  const int H = a.H, I = a.I, k = a.k, TK = a.T * k;
+  const int Kp = H / 2, nblk = H / 32;
+  const int tid = threadIdx.x, rl = tid / GU_CPR, ch = tid % GU_CPR;
+  const int n0 = blockIdx.x * 64;
+  const int col0 = (ch < 4) ? (n0 + 16 * ch) : (I + n0 + 16 * (ch - 4));
+  const int S = gridDim.y, s = blockIdx.y;
+  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
+  const size_t ld = 2 * (size_t)I;
+  const uint8_t* w = a.wgu + (size_t)e * Kp * ld;
+  const uint16_t* sc = a.sgu + (size_t)e * (H / a.group) * ld;
+
+  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);                   // [NT][Kp]
+  float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
+  float* red = corr + NT * nblk;                                      // [4][NT][128]
+  __shared__ int s_flag;
+
+  for (int c0 = 0; c0 < cnt; c0 += NT) {
+    const uint16_t* src[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      src[t] = (c0 + t < cnt) ? a.x + (size_t)(a.ws.slot_list[beg + c0 + t] / k) * H : nullptr;
+    __syncthreads();
+    stage_bf16_rows<XM, FMT, NT>(src, Kp, xl, corr, GU_THREADS, tid);
+    __syncthreads();
+    float acc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
+    tile_rows<FMT, XM, NT>(w, sc, (int)ld, a.group, col0, b0 + rl, b1, GU_RL, xl, Kp, corr, nblk,
+                           acc);
+    reduce_to_lds<GU_CPR, NT>(acc, red, tid);
+    __syncthreads();
+    // thread (t, n): gate column n and up column n of the tile
+    for (int i = tid; i < NT * 64; i += GU_THREADS) {
+      const int t = i / 64, n = i % 64;
+      if (c0 + t >= cnt) continue;
+      float g = 0.0f, u = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < GU_WAVES; ++wv) {
+        g += red[(wv * NT + t) * 128 + n];
+        u += red[(wv * NT + t) * 128 + 64 + n];
+      }
+      const int slot = a.ws.slot_list[beg + c0 + t];
+      if (S == 1) {
+        a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
+      } else {
+        float* p = a.ws.part_gu + ((size_t)s * TK + slot) * ld;
+        p[n0 + n] = g;
+        p[I + n0 + n] = u;
+      }
+    }
+  }
+  if (S == 1) return;
+  unsigned* counter = a.ws.cnt_gu + (size_t)act * gridDim.x + blockIdx.x;
+  if (!last_arriver(counter, (unsigned)S, &s_flag)) return;
+  for (int i = tid; i < cnt * 64; i += GU_THREADS) {
+    const int t = i / 64, n = i % 64;
+    const int slot = a.ws.slot_list[beg + t];
+    float g = 0.0f, u = 0.0f;
+    for (int q = 0; q < S; ++q) {
+      const float* p = a.ws.part_gu + ((size_t)q * TK + slot) * ld;
+      g += p[n0 + n];
+      u += p[I + n0 + n];
+    }
+    a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
+  }
+  if (tid == 0) *counter = 0u;
+}
+
+// =====================================================================================
+// down projection + top-k combine (vector-ALU tiles)
+// =====================================================================================
+// Grid: x = 64-wide output tile of H, y = K split over I, z = active-expert index.
+// 4 lanes per byte row (64 columns), 64 row-lanes.  Partial y of every (split, slot) goes
+// to the workspace; the workgroup that completes a (token, tile) sums the k slots in
+// ascending j order (and the splits in ascending order), adds the residual and writes out.
+constexpr int DN_THREADS = 256, DN_CPR = 4, DN_RL = DN_THREADS / DN_CPR, DN_WAVES = 4;
+
+__device__ void combine_tile(const MoeArgs& a, int t, int tile, int tid, int S) {
+  const int H = a.H, k = a.k, TK = a.T * a.k;
+  for (int i = tid; i < 64; i += blockDim.x) {
+    const int m = tile * 64 + i;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int slot = t * k + j;
+      const int e = a.ids[slot];
+      if (e < 0 || e >= a.E) continue;
+      float y = 0.0f;
+      for (int q = 0; q < S; ++q) y += a.ws.part_dn[((size_t)q * TK + slot) * H + m];
+      acc = fmaf(a.wts[slot], y, acc);
+    }
+    if (a.res) acc += bf16_to_f32(a.res[(size_t)t * H + m]);
+    a.out[(size_t)t * H + m] = f32_to_bf16(acc);
+  }
+}
+
+template <int FMT, int NT>
+__global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int act = blockIdx.z;
+  if (act >= *a.ws.n_active) return;
+  const int beg = a.ws.act_off[act];
+  const int cnt = a.ws.act_off[act + 1] - beg;
+  if (cnt >= a.mfma_min) return;
+  const int e = a.ws.act_expert[act];
+  const int H = a.H, I = a.I, k = a.k, TK = a.T * k;
+  const int Kp = I / 2, nblk = I / 32;
+  const int tid = threadIdx.x, rl = tid / DN_CPR, ch = tid % DN_CPR;
+  const int tile = blockIdx.x;
+  const int col0 = tile * 64 + 16 * ch;
+  const int S = gridDim.y, s = blockIdx.y;
+  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
+  const uint8_t* w = a.wd + (size_t)e * Kp * H;
+  const uint16_t* sc = a.sd + (size_t)e * (I / a.group) * H;
+
+  float2* xl = reinterpret_cast<float2*>(smem);                       // [NT][Kp]
+  float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
+  float* red = corr + NT * nblk;                                      // [4][NT][64]
+  __shared__ int s_last[NT];
+
+  for (int c0 = 0; c0 < cnt; c0 += NT) {
+    const float* src[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      src[t] = (c0 + t < cnt) ? a.ws.h + (size_t)a.ws.slot_list[beg + c0 + t] * I : nullptr;
+    __syncthreads();
+    stage_f32_rows<FMT, NT>(src, Kp, xl, corr, DN_THREADS, tid);
+    __syncthreads();
+    float acc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
+    tile_rows<FMT, X_F32, NT>(w, sc, H, a.group, col0, b0 + rl, b1, DN_RL, xl, Kp, corr, nblk,
+                              acc);
+    reduce_to_lds<DN_CPR, NT>(acc, red, tid);
+    __syncthreads();
+    for (int i = tid; i < NT * 64; i += DN_THREADS) {
+      const int t = i / 64, c = i % 64;
+      if (c0 + t >= cnt) continue;
+      float v = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < DN_WAVES; ++wv) v += red[(wv * NT + t) * 64 + c];
+      const int slot = a.ws.slot_list[beg + c0 + t];
+      a.ws.part_dn[((size_t)s * TK + slot) * H + tile * 64 + c] = v;
+    }
+    // count this (token, tile) contribution; the completing workgroup combines
+    __threadfence();
+    __syncthreads();
+    if (tid < NT) {
+      int last = 0;
+      if (c0 + tid < cnt) {
+        const int slot = a.ws.slot_list[beg + c0 + tid];
+        const int t = slot / k;
+        unsigned* counter = a.ws.cnt_dn + (size_t)t * gridDim.x + tile;
+        const unsigned expected = (unsigned)(a.ws.nvalid[t] * S);
+        last = (atomicAdd(counter, 1u) + 1u == expected) ? 1 : 0;
+      }
+      s_last[tid] = last;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (!s_last[t]) continue;
+      __threadfence();
+      const int slot = a.ws.slot_list[beg + c0 + t];
+      const int tok = slot / k;
+      combine_tile(a, tok, tile, tid, S);
+      if (tid == 0) a.ws.cnt_dn[(size_t)tok * gridDim.x + tile] = 0u;
+    }
+  }
+}
+
+// =====================================================================================
+// dense packed INT4 GEMV
+// =====================================================================================
+constexpr int GV_THREADS = 256, GV_CPR = 4, GV_RL = GV_THREADS / GV_CPR, GV_WAVES = 4;
+
+template <int NT>
+__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int K = g.K, N = g.N, T = g.T;
+  const int Kp = K / 2, nblk = K / 32;
+  const int tid = threadIdx.x, rl = tid / GV_CPR, ch = tid % GV_CPR;
+  const int tile = blockIdx.x;
+  const int col0 = tile * 64 + 16 * ch;
+  const int S = gridDim.y, s = blockIdx.y;
+  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
+  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
+  float* corr = reinterpret_cast<float*>(xl + NT * Kp);
+  float* red = corr + NT * nblk;
+  __shared__ int s_flag;
+
+  for (int c0 = 0; c0 < T; c0 += NT) {
+    const uint16_t* src[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) src[t] = (c0 + t < T) ? g.x + (size_t)(c0 + t) * K : nullptr;
+    __syncthreads();
+    stage_bf16_rows<X_F16, FMT_INT4, NT>(src, Kp, xl, corr, GV_THREADS, tid);
+    __syncthreads();
+    float acc[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
+    tile_rows<FMT_INT4, X_F16, NT>(g.w, g.s, N, g.group, col0, b0 + rl, b1, GV_RL, xl, Kp, corr,
+                                   nblk, acc);
+    reduce_to_lds<GV_CPR, NT>(acc, red, tid);
+    __syncthreads();
+    for (int i = tid; i < NT * 64; i += GV_THREADS) {
+      const int t = i / 64, c = i % 64;
+      if (c0 + t >= T) continue;
+      float v = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < GV_WAVES; ++wv) v += red[(wv * NT + t) * 64 + c];
+      const int n = tile * 64 + c;
+      if (S == 1)
+        g.y[(size_t)(c0 + t) * N + n] = f32_to_bf16(v);
+      else
+        g.part[((size_t)s * T + c0 + t) * N + n] = v;
+    }
+  }
+  if (S == 1) return;
+  unsigned* counter = g.cnt + tile;
+  if (!last_arriver(counter, (unsigned)S, &s_flag)) return;
+  for (int i = tid; i < T * 64; i += GV_THREADS) {
+    const int t = i / 64, n = tile * 64 + i % 64;
+    float v = 0.0f;
+    for (int q = 0; q < S; ++q) v += g.part[((size_t)q * T + t) * N + n];
+    g.y[(size_t)t * N + n] = f32_to_bf16(v);
+  }
+  if (tid == 0) *counter = 0u;
+}
+
+// =====================================================================================
+// test aid: dequantize with the compute kernels' decode
+// =====================================================================================
+template <int FMT>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ w,
+                                                      const uint16_t* __restrict__ s, int K, int N,
+                                                      int group, float* __restrict__ out) {
+  // one thread per 4 bytes of one byte row
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nq = (size_t)(K / 2) * (N / 4);
+  if (idx >= nq) return;
+  const int r = (int)(idx / (N / 4));
+  const int n = (int)(idx % (N / 4)) * 4;
+  const uint32_t d = *reinterpret_cast<const uint32_t*>(w + (size_t)r * N + n);
+  float lo[4], hi[4];
+  if constexpr (FMT == FMT_FP4) {
+    const bf16x2_t p[4] = {fp4_pair_bf16<0>(d), fp4_pair_bf16<1>(d), fp4_pair_bf16<2>(d),
+                           fp4_pair_bf16<3>(d)};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t u = __builtin_bit_cast(uint32_t, p[b]);
+      lo[b] = bf16_lo(u);
+      hi[b] = bf16_hi(u);
+    }
+  } else {
+    const f16x2_t p[4] = {int4_pair_f16_biased<0>(d), int4_pair_f16_biased<1>(d),
+                          int4_pair_f16_biased<2>(d), int4_pair_f16_biased<3>(d)};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      lo[b] = (float)p[b].x - (INT4_F16_BIAS_LO - 8.0f) - 8.0f;
+      hi[b] = (float)p[b].y - (INT4_F16_BIAS_HI - 8.0f) - 8.0f;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float sc_lo = bf16_to_f32(s[(size_t)((2 * r) / group) * N + n + b]);
+    const float sc_hi = bf16_to_f32(s[(size_t)((2 * r + 1) / group) * N + n + b]);
+    out[(size_t)(2 * r) * N + n + b] = lo[b] * sc_lo;
+    out[(size_t)(2 * r + 1) * N + n + b] = hi[b] * sc_hi;
+  }
+}
+
+// =====================================================================================
+// host launchers
+// =====================================================================================
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
+                       hipStream_t st) {
+  const int grid = (T + 3) / 4;
+  hipLaunchKernelGGL(topk_kernel, dim3(grid), dim3(256), 0, st, logits, T, E, k, ids, wts);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st) {
+  const size_t sm = (size_t)(3 * a.E + 2 * SCHED_THREADS + 4) * sizeof(int);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), sm, st, a, logits);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT>
+static hipError_t launch_gateup_t(const MoeArgs& a, int A, hipStream_t st) {
+  const int Kp = a.H / 2, nblk = a.H / 32;
+  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GU_WAVES * NT * 128 * 4;
+  hipLaunchKernelGGL((gateup_kernel<FMT, NT>), dim3(a.I / 64, a.S_gu, A), dim3(GU_THREADS), sm, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT>
+static hipError_t launch_down_t(const MoeArgs& a, int A, hipStream_t st) {
+  const int Kp = a.I / 2, nblk = a.I / 32;
+  const size_t sm = (size_t)NT * Kp * 8 + (size_t)NT * nblk * 4 + (size_t)DN_WAVES * NT * 64 * 4;
+  hipLaunchKernelGGL((down_kernel<FMT, NT>), dim3(a.H / 64, a.S_dn, A), dim3(DN_THREADS), sm, st,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_valu(const MoeArgs& a, int A, int nt, hipStream_t st) {
+  hipError_t e;
+#define DQG_MOE_CASE(F, N)                         \
+  if (a.fmt == F && nt == N) {                     \
+    e = launch_gateup_t<F, N>(a, A, st);           \
+    if (e != hipSuccess) return e;                 \
+    return launch_down_t<F, N>(a, A, st);          \
+  }
+  DQG_MOE_CASE(FMT_FP4, 1)
+  DQG_MOE_CASE(FMT_FP4, 2)
+  DQG_MOE_CASE(FMT_FP4, 4)
+  DQG_MOE_CASE(FMT_INT4, 1)
+  DQG_MOE_CASE(FMT_INT4, 2)
+  DQG_MOE_CASE(FMT_INT4, 4)
+#undef DQG_MOE_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int NT>
+static hipError_t launch_gemv_t(const GemvArgs& g, hipStream_t st) {
+  const int Kp = g.K / 2, nblk = g.K / 32;
+  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GV_WAVES * NT * 64 * 4;
+  hipLaunchKernelGGL(gemv_kernel<NT>, dim3(g.N / 64, g.S), dim3(GV_THREADS), sm, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemvArgs& g, int nt, hipStream_t st) {
+  if (nt == 1) return launch_gemv_t<1>(g, st);
+  if (nt == 2) return launch_gemv_t<2>(g, st);
+  return launch_gemv_t<4>(g, st);
+}
+
+hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
+                          float* out, hipStream_t st) {
+  const size_t nq = (size_t)(K / 2) * (N / 4);
+  const int grid = (int)((nq + 255) / 256);
+  if (fmt == FMT_FP4)
+    hipLaunchKernelGGL(dequant_kernel<FMT_FP4>, dim3(grid), dim3(256), 0, st, w, s, K, N, group,
+                       out);
+  else
+    hipLaunchKernelGGL(dequant_kernel<FMT_INT4>, dim3(grid), dim3(256), 0, st, w, s, K, N, group,
+                       out);
+  return hipGetLastError();
+}
+
+}  // namespace dqg

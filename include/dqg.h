@@ -1,0 +1,175 @@
+/*
+ * dqg.h -- packed 4-bit dequant-in-register MoE FFN and dense GEMV for decode on
+ * AMD Instinct MI355X (gfx950).  C linkage, plain pointers and sizes.
+ *
+ * Every pointer argument is a caller-owned DEVICE pointer unless stated otherwise.
+ * bf16 values travel as uint16_t bit patterns.  All compute calls are asynchronous on
+ * `stream`: they never synchronize, never allocate and never read device memory from
+ * the host, so they can be captured into a hipGraph.  The caller keeps every buffer
+ * alive until the stream work has completed.  The library owns no device memory and
+ * keeps no state between calls (reentrant), except that concurrent calls must not
+ * share one workspace.
+ *
+ * Argument checks happen on the host before any launch; a failed check returns a
+ * negative status and launches nothing.  A launch failure is reported as DQG_ERR_HIP
+ * (read with hipGetLastError, no synchronization).
+ *
+ * Storage formats (FireEcho page, section "The Goliath Kernel: Why It's Fast": all
+ * experts of a layer in one contiguous [E, K//2, N] buffer whose bytes are split into
+ * a low nibble, taken first, and a high nibble, each dequantized with a scale inside
+ * the matmul loop):
+ *   packed weights  uint8 [E, K/2, N]: byte [e, r, n] holds K index 2r in bits 0-3 and
+ *                   K index 2r+1 in bits 4-7; N is the contiguous axis.
+ *   group scales    bf16  [E, K/G, N]: one scale per G consecutive K and per column.
+ *   element value   DQG_FMT_INT4:     nibble - 8            (symmetric INT4)
+ *                   DQG_FMT_FP4_E2M1: OCP MX E2M1 (sign bit, 2-bit exponent with bias 1,
+ *                                     1-bit mantissa: magnitudes 0 .5 1 1.5 2 3 4 6)
+ *   weight          W[k, n] = value(nibble) * scale[k / G, n]   (exact in fp32)
+ * Shapes: K even, K % G == 0, N % 16 == 0, G in {32, 128}; base pointers of packed
+ * weights, scales, x, residual and out 16-byte aligned.  Anything else returns
+ * DQG_ERR_UNSUPPORTED or DQG_ERR_MISALIGNED so that the caller can keep another path.
+ */
+#ifndef DQG_H
+#define DQG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DQG_ABI_VERSION 1
+
+typedef enum dqg_status {
+  DQG_OK = 0,
+  DQG_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, k > E, ...        */
+  DQG_ERR_UNSUPPORTED = -2, /* shape/format outside what the kernels implement     */
+  DQG_ERR_MISALIGNED = -3,  /* a base pointer is not 16-byte aligned               */
+  DQG_ERR_WORKSPACE = -4,   /* workspace null or smaller than the query returns    */
+  DQG_ERR_HIP = -5          /* a kernel launch failed                              */
+} dqg_status;
+
+typedef enum dqg_format {
+  DQG_FMT_INT4 = 0,     /* value = nibble - 8            */
+  DQG_FMT_FP4_E2M1 = 1  /* value = E2M1(nibble)          */
+} dqg_format;
+
+/* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
+ * default, 0, picks the path from the shapes).  FORCE_GEMV runs every expert on the
+ * vector-ALU tiles, FORCE_MFMA runs every expert with at least one token on the bf16
+ * matrix-core tiles, NO_FUSED disables the single-launch T=1 layer. */
+#define DQG_PATH_FORCE_GEMV 0x100
+#define DQG_PATH_FORCE_MFMA 0x200
+#define DQG_PATH_NO_FUSED 0x400
+
+/* Version of this ABI (DQG_ABI_VERSION).  Host only. */
+int dqg_abi_version(void);
+
+/* Human-readable name of a status code.  Host only; never fails. */
+const char* dqg_status_string(int status);
+
+/*
+ * topk_route -- expert selection for T tokens (FireEcho page, "The Goliath Kernel":
+ * expert IDs live in a GPU tensor and are read by the expert kernel with no host
+ * synchronization).
+ *   logits  fp32 [T, E], finite values (NaN/inf give unspecified ids)
+ *   ids     int32 [T, k] out: the k largest logits of each row in rank order; equal
+ *           logits (including -0.0 vs +0.0) rank the lower expert index first
+ *   weights fp32 [T, k] out: softmax over the k selected logits (the top logit is
+ *           subtracted before exponentiation), in the same order as ids
+ * Requires 1 <= k <= E, 1 <= E <= 4096, k <= 32, T >= 1.
+ */
+int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* weights,
+               hipStream_t stream);
+
+/*
+ * Bytes of device workspace that moe_fp4_ffn / moe_fp4_layer need for these sizes.
+ * Host only.  Returns 0 for invalid sizes.  The workspace holds a sticky int32 error
+ * word at byte 0 (set to 1 when an expert id outside [0, E) was seen; the slot then
+ * contributes zero), the device-built expert schedule, per-tile counters and fp32
+ * partial sums.  It needs no initialization; its contents are undefined after a call,
+ * except the error word, which only the caller clears.
+ */
+size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
+
+/*
+ * moe_fp4_ffn -- packed-MoE expert FFN with the top-k weighted combine, for a given
+ * routing (FireEcho page: "The Goliath Kernel" -- dequant of both nibbles times the
+ * scale in registers inside the tile loop; "Speed Optimization History" -- fused
+ * gate_up projection, one multi-expert kernel over a contiguous packed buffer;
+ * FastInfer page, "Confirmed elementwise SwiGLU scheduling" -- SiLU(gate) * up).
+ *
+ *   x          bf16 [T, H] tokens
+ *   ids        int32 [T, k] expert of each slot (device, read by the kernels)
+ *   weights    fp32 [T, k] combine weight of each slot
+ *   w_gate_up  uint8 [E, H/2, 2I], s_gate_up bf16 [E, H/G, 2I]; columns [0, I) are the
+ *              gate projection, [I, 2I) the up projection
+ *   w_down     uint8 [E, I/2, H],  s_down    bf16 [E, I/G, H]
+ *   group      G (32 or 128), format DQG_FMT_* optionally OR-ed with DQG_PATH_* flags
+ *   residual   bf16 [T, H] or NULL
+ *   out        bf16 [T, H]:
+ *     out[t] = bf16_rne( residual[t] + sum_{j<k} weights[t,j] * y_{t,j} ), j ascending,
+ *     y_{t,j} = (SiLU(g) * u) W_down[e],  [g | u] = x[t] W_gate_up[e],  e = ids[t,j],
+ *   accumulated in fp32.
+ * Each expert's weights are read once per call whatever its token count; experts with
+ * >= 16 tokens run on bf16 MFMA tiles, the others on vector-ALU tiles.
+ * Results are deterministic (fixed reduction order, no floating-point atomics).
+ * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
+ * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
+ * activations must satisfy |x| < 65504 (INT4 tiles multiply in fp16, accumulate in fp32).
+ */
+int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int32_t* ids,
+                const float* weights, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                const uint8_t* w_down, const uint16_t* s_down, int group, int format,
+                const uint16_t* residual, uint16_t* out, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_fp4_layer -- topk_route followed by moe_fp4_ffn in one call (routing computed on
+ * the device from `logits` fp32 [T, E]; same rules as topk_route).  For T == 1 the
+ * whole layer runs as a single kernel launch.  ids_out (int32 [T, k]) and weights_out
+ * (fp32 [T, k]) are optional outputs of the routing (NULL to skip).
+ */
+int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
+                  const uint8_t* w_gate_up, const uint16_t* s_gate_up, const uint8_t* w_down,
+                  const uint16_t* s_down, int group, int format, const uint16_t* residual,
+                  uint16_t* out, int32_t* ids_out, float* weights_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace packed_gemv_int4 needs (0 is a valid answer: no
+ * workspace).  Host only.  Returns 0 also for invalid sizes.
+ */
+size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
+
+/*
+ * packed_gemv_int4 -- dense packed INT4 GEMV (FastInfer page, "Specialized
+ * matrix-vector result": a token vector times a stored weight, FP32 products and
+ * reductions; eole page, "Packed Marlin projections": gate and up packed into one
+ * projection for 1-token and 4-token decode).
+ *   x  bf16 [T, K];  w uint8 [K/2, N];  s bf16 [K/G, N];  y bf16 [T, N] out
+ *   y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation.
+ * x must satisfy |x| < 65504 (the INT4 tiles multiply in fp16 with fp32 accumulation;
+ * every bf16 in that range converts exactly).  When the query returns a non-zero size
+ * the call splits K across workgroups: pass a workspace of at least that many bytes,
+ * zero-filled before its first use (every call leaves it zero-filled again).  With a NULL
+ * workspace the call runs without the K split (correct, fewer workgroups).  Deterministic.
+ */
+int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
+                     const uint16_t* s, int group, uint16_t* y, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * packed_dequant_f32 -- TEST AID: dequantize one packed matrix with the same in-register
+ * decode the compute kernels use.  w uint8 [K/2, N], s bf16 [K/G, N] -> out fp32 [K, N],
+ * out[k, n] = value(nibble) * s[k/G, n], exact.
+ */
+int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                       int format, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DQG_H */

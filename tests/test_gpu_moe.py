@@ -1,0 +1,191 @@
+"""GPU parity: packed-MoE expert FFN (route, gate_up, SiLU*up, down, top-k combine)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bits16, check_bf16, dev, upload_layer
+from oracle import moe_oracle as O
+from workloads import synth as S
+
+pytestmark = pytest.mark.gpu
+
+
+def _b():
+    from dequant_gemv_amd import binding
+    return binding
+
+
+def _layer(cfg, seed=0, layer=0):
+    """Generator layer + device buffers (only routed experts for wide E)."""
+    if cfg.E > 128:
+        lg = S.moe_layer_logits(cfg, seed, layer)
+        ids, _ = O.topk_route(lg, cfg.k)
+        L = S.make_moe_layer(cfg, seed, layer, experts=np.unique(ids))
+        return L, upload_layer(L, np.unique(ids))
+    L = S.make_moe_layer(cfg, seed, layer)
+    return L, upload_layer(L)
+
+
+def _run_layer(cfg, L, D, flags=0, residual=None):
+    B = _b()
+    x = dev(L.x)
+    lg = dev(L.logits)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    out = B.moe_fp4_layer(x, lg, cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"], cfg.group,
+                          cfg.fmt, residual=residual, ids_out=ids, weights_out=w, flags=flags)
+    torch.cuda.synchronize()
+    return bits16(out), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def _oracle_layer(cfg, L, residual_bits=None):
+    return O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group, cfg.fmt,
+                       residual_bits=residual_bits)
+
+
+CASES = [
+    ("tiny", S.TINY, 0), ("tiny", S.TINY, 1), ("tiny", S.TINY, 2),
+    ("q30", S.Q30, 0), ("q30", S.Q30, 1), ("q30", S.Q30, 2),
+    ("q30_t4", S.Q30_BATCH.with_T(4), 0), ("q30_t16", S.Q30_BATCH.with_T(16), 0),
+    ("q30_t64", S.Q30_BATCH.with_T(64), 0),
+    ("w512_t1", S.replace(S.W512, layers=1), 0), ("w512_t8", S.replace(S.W512, layers=1, T=8), 0),
+]
+
+
+@pytest.mark.parametrize("name,cfg,seed", CASES, ids=[f"{c[0]}-s{c[2]}" for c in CASES])
+def test_moe_layer_parity(name, cfg, seed):
+    L, D = _layer(cfg, seed)
+    out, ids, w = _run_layer(cfg, L, D)
+    want, oids, ow = _oracle_layer(cfg, L)
+    assert np.array_equal(ids, oids), "expert selection must match bit-exactly"
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    check_bf16(out, want, what=name)
+
+
+@pytest.mark.parametrize("cfg,T", [(S.TINY, 3), (S.Q30, 4), (S.Q30, 1)])
+def test_moe_ffn_given_routing_with_residual(cfg, T):
+    cfg = cfg.with_T(T)
+    L, D = _layer(cfg, seed=5)
+    rng = np.random.default_rng(6)
+    ids, wts = S.make_routing(rng, T, cfg.E, cfg.k)
+    res = S.f32_to_bf16_bits(rng.standard_normal((T, cfg.H)))
+    B = _b()
+    out = B.moe_fp4_ffn(dev(L.x), dev(ids), dev(wts), D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                        cfg.group, cfg.fmt, residual=dev(res))
+    torch.cuda.synchronize()
+    want = O.moe_ffn(L.x, ids, wts.astype(np.float64), L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                     cfg.fmt, residual_bits=res)
+    check_bf16(bits16(out), want, what="ffn+residual")
+
+
+def test_moe_deterministic_and_layer_equals_ffn():
+    cfg = S.Q30_BATCH.with_T(16)
+    L, D = _layer(cfg, seed=0)
+    o1, ids, w = _run_layer(cfg, L, D)
+    o2, _, _ = _run_layer(cfg, L, D)
+    assert np.array_equal(o1, o2), "two runs must match bitwise"
+    B = _b()
+    o3 = B.moe_fp4_ffn(dev(L.x), dev(ids), dev(w), D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                       cfg.group, cfg.fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(o3), o1)
+
+
+def test_moe_invalid_ids_contribute_zero_and_set_error_word():
+    cfg = S.TINY.with_T(3)
+    L, D = _layer(cfg, seed=7)
+    ids = np.array([[1, -1], [8, 3], [-5, 99]], np.int32)   # token 2 has no valid slot
+    wts = np.full((3, 2), 0.5, np.float32)
+    res = S.f32_to_bf16_bits(np.random.default_rng(8).standard_normal((3, cfg.H)))
+    B = _b()
+    ws = B.moe_workspace(3, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    out = B.moe_fp4_ffn(dev(L.x), dev(ids), dev(wts), D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                        cfg.group, cfg.fmt, residual=dev(res), workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 1
+    keep = np.array([[1, 0], [0, 1], [0, 0]], np.float64)
+    want = O.moe_ffn(L.x, np.where(keep > 0, ids, 0), wts.astype(np.float64) * keep, L.w_gu,
+                     L.s_gu, L.w_d, L.s_d, cfg.group, cfg.fmt, residual_bits=res)
+    check_bf16(bits16(out), want, what="invalid ids")
+    assert np.array_equal(bits16(out)[2], res[2])
+
+
+def test_moe_workspace_reused_across_shapes():
+    B = _b()
+    big = S.Q30_BATCH.with_T(16)
+    ws = B.moe_workspace(16, big.H, big.I, big.E, big.k, "cuda")
+    for cfg in (S.Q30, big, S.Q30.with_T(4)):
+        L, D = _layer(cfg, seed=11)
+        out = B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                              D["s_d"], cfg.group, cfg.fmt, workspace=ws)
+        torch.cuda.synchronize()
+        check_bf16(bits16(out), _oracle_layer(cfg, L)[0], what=f"reuse T={cfg.T}")
+
+
+def test_graph_replay_with_changing_inputs():
+    """Capture one layer call, replay it with new x and logits copied into the captured
+    inputs; every replay must equal an eager call on the same inputs."""
+    B = _b()
+    cfg = S.Q30
+    L, D = _layer(cfg, seed=0)
+    x = dev(L.x).clone()
+    lg = dev(L.logits).clone()
+    ws = B.moe_workspace(1, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    out = torch.empty((1, cfg.H), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.moe_fp4_layer(x, lg, cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"], cfg.group,
+                        cfg.fmt, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.moe_fp4_layer(x, lg, cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"], cfg.group,
+                        cfg.fmt, out=out, workspace=ws)
+    ws2 = B.moe_workspace(1, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    rng = np.random.default_rng(12)
+    for rep in range(4):
+        xn = S.f32_to_bf16_bits(rng.standard_normal((1, cfg.H)))
+        ln = rng.standard_normal((1, cfg.E)).astype(np.float32)
+        x.copy_(dev(xn))
+        lg.copy_(dev(ln))
+        g.replay()
+        torch.cuda.synchronize()
+        got = bits16(out).copy()
+        eager = B.moe_fp4_layer(dev(xn), dev(ln), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                                D["s_d"], cfg.group, cfg.fmt, workspace=ws2)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, bits16(eager)), f"replay {rep}"
+        L2 = S.MoELayer(cfg, 0, xn, ln, L.w_gu, L.s_gu, L.w_d, L.s_d)
+        check_bf16(got, _oracle_layer(cfg, L2)[0], what=f"replay {rep}")
+
+
+def _stack(T, n_layers):
+    cfg = S.replace(S.W512, T=T)
+    layers, devs = [], []
+    for l in range(n_layers):
+        lg = S.moe_layer_logits(cfg, 0, l)
+        ids, _ = O.topk_route(lg, cfg.k)
+        L = S.make_moe_layer(cfg, 0, l, with_x=(l == 0), experts=np.unique(ids))
+        layers.append(L)
+        devs.append(upload_layer(L, np.unique(ids)))
+    return cfg, layers, devs
+
+
+@pytest.mark.parametrize("T,n_layers", [(1, 48), (8, 12)])
+def test_w512_stack_chained_residual(T, n_layers):
+    """48 independently seeded E=512 layers chained as x_{l+1} = bf16(x_l + MoE_l(x_l))."""
+    B = _b()
+    cfg, layers, devs = _stack(T, n_layers)
+    ws = B.moe_workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    bufs = [dev(layers[0].x).view(torch.bfloat16),
+            torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")]
+    for l, (L, D) in enumerate(zip(layers, devs)):
+        xin, xout = bufs[l % 2], bufs[(l + 1) % 2]
+        B.moe_fp4_layer(xin, dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                        cfg.group, cfg.fmt, residual=xin, out=xout, workspace=ws)
+    torch.cuda.synchronize()
+    got = bits16(bufs[n_layers % 2])
+    _, want = O.moe_stack(layers[0].x, layers, cfg.k, cfg.group, cfg.fmt)
+    check_bf16(got, want, what=f"stack T={T}")

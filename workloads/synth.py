@@ -227,3 +227,20 @@ def random_packed(rng: np.random.Generator, K: int, N: int, group: int, lo=0.002
     """Uniform random packed codes ``[K/2, N]`` and bf16 scales ``[K/G, N]``."""
     return (rng.integers(0, 256, size=(K // 2, N), dtype=np.uint8),
             _scales(rng, (K // group, N), lo, hi))
+
+
+def make_routing(rng: np.random.Generator, T: int, E: int, k: int):
+    """A routing given as input (for calls that take ids and weights): per token k
+    distinct experts drawn uniformly, weights from a flat Dirichlet (positive, summing to
+    about 1), as int32 [T, k] and float32 [T, k]."""
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    return ids, w
+
+
+def moe_layer_logits(cfg: MoEConfig, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """The logits make_moe_layer(cfg, seed, layer) draws, without drawing the experts."""
+    s = seed if cfg.layers == 1 else 1000 * seed + layer
+    rng = np.random.default_rng(s)
+    rng.standard_normal((cfg.T, cfg.H))
+    return make_logits(cfg, rng, cfg.T)
