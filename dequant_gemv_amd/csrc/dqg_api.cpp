@@ -27,8 +27,8 @@ inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct MoePlan {
   int T, H, I, E, k, TK, A;
   int tiles_gu, tiles_dn, S_gu, S_dn, nt;
-  size_t o_err, o_nact, o_actexp, o_actoff, o_slots, o_nvalid, o_ids, o_wts, o_cnt, o_h, o_pgu,
-      o_pdn, total;
+  size_t o_err, o_fx, o_nact, o_actexp, o_actoff, o_slots, o_nvalid, o_ids, o_wts, o_cnt, o_h,
+      o_pgu, o_pdn, total;
   int n_cnt_gu, n_cnt_dn;
 };
 
@@ -61,6 +61,9 @@ MoePlan plan_moe(int T, int H, int I, int E, int k) {
   p.n_cnt_dn = T * p.tiles_dn;
   size_t o = 0;
   p.o_err = o;     o += 256;
+  // the single-launch T=1 region sits at the same offset for every T, so a workspace
+  // keeps its self-resetting counters valid when calls with other T values reuse it
+  p.o_fx = o;      o = up256(o + dqg::fused_ws_bytes(H, I, k));
   p.o_nact = o;    o += 256;
   p.o_actexp = o;  o = up256(o + sizeof(int) * p.A);
   p.o_actoff = o;  o = up256(o + sizeof(int) * (p.A + 1));
@@ -131,6 +134,25 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
                : (flags & DQG_PATH_FORCE_MFMA) ? 1
                                                : kMfmaMinTokens;
   return a;
+}
+
+bool use_fused(int T, int E, int k, int format) {
+  return T == 1 && E <= 512 && k <= 32 && !(format & DQG_PATH_NO_FUSED);
+}
+
+int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint8_t* wgu,
+              const uint16_t* sgu, const uint8_t* wd, const uint16_t* sd, int group, int format,
+              const uint16_t* res, uint16_t* out, int32_t* ids_out, float* w_out, void* ws,
+              hipStream_t st) {
+  dqg::FusedArgs f{};
+  f.x = x; f.logits = logits; f.H = p.H; f.I = p.I; f.E = p.E; f.k = p.k; f.group = group;
+  f.fmt = format & 0xFF;
+  f.wgu = wgu; f.sgu = sgu; f.wd = wd; f.sd = sd; f.res = res; f.out = out;
+  f.ids_out = ids_out; f.w_out = w_out;
+  char* b = static_cast<char*>(ws);
+  f.err = reinterpret_cast<int*>(b + p.o_err);
+  dqg::fused_layout(f, b + p.o_fx, p.H, p.I, p.k);
+  return dqg::launch_fused_t1(f, st) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }
 
 int run_moe(MoeArgs& a, const MoePlan& p, const float* logits, hipStream_t st) {
@@ -232,6 +254,9 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k);
+  if (use_fused(T, E, k, format))
+    return run_fused(p, x, logits, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
+                     out, ids_out, weights_out, workspace, stream);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
                             out, workspace);
   a.ids_w = ids_out ? ids_out : a.ws.ids;

@@ -31,6 +31,7 @@ namespace dqg {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 enum { FMT_INT4 = 0, FMT_FP4 = 1 };
 enum { X_BF16 = 0, X_F16 = 1, X_F32 = 2 };
@@ -276,21 +277,182 @@ __device__ __forceinline__ void stage_f32_rows(const float* const (&src)[NT], in
   }
 }
 
-// ---- cross-workgroup "last arriver" -----------------------------------------------------
-// Every thread has stored its partial results; returns true (in all threads) for exactly
-// one workgroup -- the one whose increment completes `expected`.  That workgroup then
-// reads the others' partials (after the acquire fence) and resets the counter.
+// ---- top-k routing: one wavefront per token ---------------------------------------------
+// Order-preserving integer key of a logit: larger float -> larger int; -0.0 and +0.0 get the
+// same key (so they tie and the lower expert index ranks first).  The map is an involution
+// on the bits, so key_to_float undoes it (returning +0.0 for either zero).
+__device__ __forceinline__ int logit_key(float v) {
+  const int b = __float_as_int(v + 0.0f);  // -0.0 + 0.0 = +0.0
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_to_float(int k) {
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+// Maximum over the wavefront, uniform result: DPP within each row of 16 lanes (xor 1, xor 2,
+// rotate 4, rotate 8), then the four row maxima through readlane.
+__device__ __forceinline__ int wave_max_key(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, 0xB1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, 0x4E, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp((int)0x80000000, v, 0x128, 0xF, 0xF, false));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+
+// Top-k of one row of E logits (E <= 64 * MAXV) by one wavefront; lane j < k returns the
+// j-th selection (rank order) in *sel_e / *sel_w, with w = softmax over the k selected
+// logits (top logit subtracted).  Each round takes the wave maximum of the not-yet-taken
+// keys, then the lowest expert index holding that key (ballot over expert = lane + 64 i,
+// i ascending), so ties go to the lower index.  Logits must not be NaN.
+template <int MAXV>
+__device__ __forceinline__ void wave_route(const float* __restrict__ row, int E, int k, int lane,
+                                           int* sel_e, float* sel_w) {
+  int key[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? logit_key(row[e]) : (int)0x80000000;
+  }
+  unsigned long long taken = 0;
+  int my_key = 0, my_e = -1, top = 0;
+  for (int j = 0; j < k; ++j) {
+    int m = (int)0x80000000;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (!((taken >> i) & 1ull) && lane + 64 * i < E) m = max(m, key[i]);
+    m = wave_max_key(m);
+    int win = -1;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const unsigned long long bal =
+          __ballot(!((taken >> i) & 1ull) && lane + 64 * i < E && key[i] == m);
+      if (bal) {
+        const int l = __ffsll((long long)bal) - 1;
+        win = l + 64 * i;
+        if (lane == l) taken |= 1ull << i;
+        break;
+      }
+    }
+    if (j == 0) top = m;
+    if (lane == j) {
+      my_key = m;
+      my_e = win;
+    }
+  }
+  const float ex = (lane < k) ? expf(key_to_float(my_key) - key_to_float(top)) : 0.0f;
+  const float s = wave_sum_f32(ex);
+  *sel_e = my_e;
+  *sel_w = ex / s;
+}
+
+// Same selection for E > 512: keys are re-read from memory (L1/L2) every round instead of
+// being held in registers; `taken` covers up to 64 entries per lane (E <= 4096).
+__device__ __forceinline__ void wave_route_mem(const float* __restrict__ row, int E, int k,
+                                               int lane, int* sel_e, float* sel_w) {
+  unsigned long long taken = 0;
+  int my_key = 0, my_e = -1, top = 0;
+  const int nv = (E + 63) / 64;
+  for (int j = 0; j < k; ++j) {
+    int m = (int)0x80000000;
+    for (int i = 0; i < nv; ++i)
+      if (!((taken >> i) & 1ull) && lane + 64 * i < E) m = max(m, logit_key(row[lane + 64 * i]));
+    m = wave_max_key(m);
+    int win = -1;
+    for (int i = 0; i < nv; ++i) {
+      const bool mine = !((taken >> i) & 1ull) && lane + 64 * i < E &&
+                        logit_key(row[lane + 64 * i]) == m;
+      const unsigned long long bal = __ballot(mine);
+      if (bal) {
+        const int l = __ffsll((long long)bal) - 1;
+        win = l + 64 * i;
+        if (lane == l) taken |= 1ull << i;
+        break;
+      }
+    }
+    if (j == 0) top = m;
+    if (lane == j) {
+      my_key = m;
+      my_e = win;
+    }
+  }
+  const float ex = (lane < k) ? expf(key_to_float(my_key) - key_to_float(top)) : 0.0f;
+  const float s = wave_sum_f32(ex);
+  *sel_e = my_e;
+  *sel_w = ex / s;
+}
+
+// MAXE: the largest E the caller supports (E <= 512 keeps the keys in registers).
+template <int MAXE = 4096>
+__device__ __forceinline__ void route_row(const float* __restrict__ row, int E, int k, int lane,
+                                          int* sel_e, float* sel_w) {
+  if (E <= 128)
+    wave_route<2>(row, E, k, lane, sel_e, sel_w);
+  else if (MAXE <= 512 || E <= 512)
+    wave_route<8>(row, E, k, lane, sel_e, sel_w);
+  else
+    wave_route_mem(row, E, k, lane, sel_e, sel_w);
+}
+
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int lane, int32_t* ids, float* wts) {
+  int e;
+  float w;
+  route_row<4096>(logits + (size_t)t * E, E, k, lane, &e, &w);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = e;
+    wts[(size_t)t * k + lane] = w;
+  }
+}
+
+// ---- cross-workgroup exchange ----------------------------------------------------------
+// Data that another workgroup reads within the same launch moves with agent-coherent
+// (sc1) loads and stores: relaxed agent-scope atomic accesses, which need no cache
+// writeback or invalidate.  (An agent-scope fence writes back and invalidates the L2 and
+// costs tens of microseconds when hundreds of workgroups issue it.)  Ordering: each thread
+// waits until its own stores are acknowledged, the workgroup meets at a barrier, then one
+// thread increments the counter.
+__device__ __forceinline__ void st_sc1(float* base, size_t idx, float v) {
+  __hip_atomic_store(base + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_sc1(const float* base, size_t idx) {
+  return __hip_atomic_load(base + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ld_cnt(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned add_cnt(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_cnt(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait for this thread's outstanding memory operations (stores acknowledged)
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Every thread has stored its partial results with st_sc1; returns true (in all threads)
+// for exactly one workgroup -- the one whose increment completes `expected`.  That
+// workgroup reads the others' partials with ld_sc1 and resets the counter.
 __device__ __forceinline__ bool last_arriver(unsigned* counter, unsigned expected, int* s_flag) {
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
+    const unsigned prev = add_cnt(counter, 1u);
     *s_flag = (prev + 1u == expected) ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *s_flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *s_flag != 0;
 }
 
 }  // namespace dqg

@@ -55,6 +55,29 @@ struct GemvArgs {
   int S;
 };
 
+// Single-launch T = 1 layer (routing + expert FFN + combine); see dqg_fused.hip.
+struct FusedArgs {
+  const uint16_t* x;
+  const float* logits;
+  int H, I, E, k, group, fmt;
+  const uint8_t* wgu;
+  const uint16_t* sgu;
+  const uint8_t* wd;
+  const uint16_t* sd;
+  const uint16_t* res;
+  uint16_t* out;
+  int32_t* ids_out;     // optional routing outputs (may be null)
+  float* w_out;
+  float* h;             // [2][k, I]         SiLU(gate)*up, two copies
+  float* ypart;         // [2][n_chunks, H]  partial output rows, two copies
+  unsigned long long* calls;  // completed column tiles over all calls (parity source)
+  int* err;
+  int n_a, n_b, n_chunks;
+};
+size_t fused_ws_bytes(int H, int I, int k);
+void fused_layout(FusedArgs& f, void* ws, int H, int I, int k);
+hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st);
+
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
                        hipStream_t st);
 hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st);

@@ -12,96 +12,6 @@ namespace dqg {
 // =====================================================================================
 // top-k routing: one wavefront per token
 // =====================================================================================
-// a ranks before b: larger logit first, equal logits -> lower expert index first
-// (-0.0 == +0.0 compares equal, so the index decides).
-__device__ __forceinline__ bool ranks_before(float av, int ae, float bv, int be) {
-  return av > bv || (av == bv && ae < be);
-}
-
-// Selects the k best (logit, index) pairs of `row` in rank order; lane j < k returns
-// pair j in (*v, *e).  Each round takes the best pair that ranks after the previous
-// round's pair, so no selection mask is needed.
-template <int CACHE>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
-                                          float* my_v, int* my_e, float* top_v) {
-  float cache[CACHE > 0 ? CACHE : 1];
-  if (CACHE > 0) {
-#pragma unroll
-    for (int i = 0; i < CACHE; ++i) {
-      const int e = lane + 64 * i;
-      cache[i] = (e < E) ? row[e] : 0.0f;
-    }
-  }
-  float pv = __builtin_inff();
-  int pe = -1;
-  *my_v = 0.0f;
-  *my_e = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = -__builtin_inff();
-    int be = 0x7FFFFFFF;
-    if (CACHE > 0) {
-#pragma unroll
-      for (int i = 0; i < CACHE; ++i) {
-        const int e = lane + 64 * i;
-        const float v = cache[i];
-        if (e < E && ranks_before(pv, pe, v, e) && ranks_before(v, e, bv, be)) {
-          bv = v;
-          be = e;
-        }
-      }
-    } else {
-      for (int e = lane; e < E; e += 64) {
-        const float v = row[e];
-        if (ranks_before(pv, pe, v, e) && ranks_before(v, e, bv, be)) {
-          bv = v;
-          be = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (ranks_before(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (j == 0) *top_v = bv;
-    if (lane == j) {
-      *my_v = bv;
-      *my_e = be;
-    }
-    pv = bv;
-    pe = be;
-  }
-}
-
-// Softmax over the k selected logits (top logit subtracted), lanes j < k hold theirs.
-__device__ __forceinline__ float wave_softmax_k(float my_v, float top_v, int k, int lane) {
-  const float ex = (lane < k) ? expf(my_v - top_v) : 0.0f;
-  float s = ex;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  return ex / s;
-}
-
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int lane, int32_t* ids, float* wts) {
-  const float* row = logits + (size_t)t * E;
-  float my_v, top_v;
-  int my_e;
-  if (E <= 512)
-    wave_topk<8>(row, E, k, lane, &my_v, &my_e, &top_v);
-  else
-    wave_topk<0>(row, E, k, lane, &my_v, &my_e, &top_v);
-  const float w = wave_softmax_k(my_v, top_v, k, lane);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    wts[(size_t)t * k + lane] = w;
-  }
-}
-
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts) {
@@ -320,8 +230,8 @@ __global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
         a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
       } else {
         float* p = a.ws.part_gu + ((size_t)s * TK + slot) * ld;
-        p[n0 + n] = g;
-        p[I + n0 + n] = u;
+        st_sc1(p, n0 + n, g);
+        st_sc1(p, I + n0 + n, u);
       }
     }
   }
@@ -334,12 +244,12 @@ __global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
     float g = 0.0f, u = 0.0f;
     for (int q = 0; q < S; ++q) {
       const float* p = a.ws.part_gu + ((size_t)q * TK + slot) * ld;
-      g += p[n0 + n];
-      u += p[I + n0 + n];
+      g += ld_sc1(p, n0 + n);
+      u += ld_sc1(p, I + n0 + n);
     }
     a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
   }
-  if (tid == 0) *counter = 0u;
+  if (tid == 0) st_cnt(counter, 0u);
 }
 
 // =====================================================================================
@@ -361,7 +271,7 @@ __device__ void combine_tile(const MoeArgs& a, int t, int tile, int tid, int S) 
       const int e = a.ids[slot];
       if (e < 0 || e >= a.E) continue;
       float y = 0.0f;
-      for (int q = 0; q < S; ++q) y += a.ws.part_dn[((size_t)q * TK + slot) * H + m];
+      for (int q = 0; q < S; ++q) y += ld_sc1(a.ws.part_dn, ((size_t)q * TK + slot) * H + m);
       acc = fmaf(a.wts[slot], y, acc);
     }
     if (a.res) acc += bf16_to_f32(a.res[(size_t)t * H + m]);
@@ -417,10 +327,10 @@ __global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
 #pragma unroll
       for (int wv = 0; wv < DN_WAVES; ++wv) v += red[(wv * NT + t) * 64 + c];
       const int slot = a.ws.slot_list[beg + c0 + t];
-      a.ws.part_dn[((size_t)s * TK + slot) * H + tile * 64 + c] = v;
+      st_sc1(a.ws.part_dn, ((size_t)s * TK + slot) * H + tile * 64 + c, v);
     }
     // count this (token, tile) contribution; the completing workgroup combines
-    __threadfence();
+    wait_mem();
     __syncthreads();
     if (tid < NT) {
       int last = 0;
@@ -429,7 +339,7 @@ __global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
         const int t = slot / k;
         unsigned* counter = a.ws.cnt_dn + (size_t)t * gridDim.x + tile;
         const unsigned expected = (unsigned)(a.ws.nvalid[t] * S);
-        last = (atomicAdd(counter, 1u) + 1u == expected) ? 1 : 0;
+        last = (add_cnt(counter, 1u) + 1u == expected) ? 1 : 0;
       }
       s_last[tid] = last;
     }
@@ -437,11 +347,10 @@ __global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (!s_last[t]) continue;
-      __threadfence();
       const int slot = a.ws.slot_list[beg + c0 + t];
       const int tok = slot / k;
       combine_tile(a, tok, tile, tid, S);
-      if (tid == 0) a.ws.cnt_dn[(size_t)tok * gridDim.x + tile] = 0u;
+      if (tid == 0) st_cnt(a.ws.cnt_dn + (size_t)tok * gridDim.x + tile, 0u);
     }
   }
 }
@@ -492,7 +401,7 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
       if (S == 1)
         g.y[(size_t)(c0 + t) * N + n] = f32_to_bf16(v);
       else
-        g.part[((size_t)s * T + c0 + t) * N + n] = v;
+        st_sc1(g.part, ((size_t)s * T + c0 + t) * N + n, v);
     }
   }
   if (S == 1) return;
@@ -501,10 +410,10 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
   for (int i = tid; i < T * 64; i += GV_THREADS) {
     const int t = i / 64, n = tile * 64 + i % 64;
     float v = 0.0f;
-    for (int q = 0; q < S; ++q) v += g.part[((size_t)q * T + t) * N + n];
+    for (int q = 0; q < S; ++q) v += ld_sc1(g.part, ((size_t)q * T + t) * N + n);
     g.y[(size_t)t * N + n] = f32_to_bf16(v);
   }
-  if (tid == 0) *counter = 0u;
+  if (tid == 0) st_cnt(counter, 0u);
 }
 
 // =====================================================================================

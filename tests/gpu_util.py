@@ -63,3 +63,26 @@ def upload_layer(L, experts=None):
             t[e].copy_(dev(a[e]))
         out[k] = t
     return out
+
+
+def check_chain(gpu_bits: np.ndarray, oracle: np.ndarray, n_layers: int, rel: float = 1e-2,
+                what: str = ""):
+    """Tolerance for an L-layer residual chain x_{l+1} = bf16(x_l + MoE_l(x_l)) run
+    independently on both sides.  Each side rounds every layer's output to bf16, and one
+    rounding decision that falls differently (values within fp32 noise of a bf16
+    midpoint) shifts later layers' inputs, so the per-layer bound does not compose.
+    Checked instead: the method's relative tolerance in norm,
+    rms(gpu - oracle) <= rel * rms(oracle), and per element at most one bf16 ulp per
+    layer on top of the per-layer bound."""
+    g = bf16_f64(gpu_bits)
+    o = np.asarray(oracle, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(np.square(o))))
+    err = np.abs(g - o)
+    rms_err = float(np.sqrt(np.mean(np.square(err))))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    assert rms_err <= rel * rms, f"{what}: rms error {rms_err!r} > {rel} * rms {rms!r}"
+    bound = rel * rms + n_layers * ulp_bf16(np.maximum(np.abs(o), np.abs(g)))
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond {n_layers} ulps + "
+                           f"{rel} * rms; worst {err.max()!r}")
+    return rms_err / rms
