@@ -63,7 +63,7 @@ MoePlan plan_moe(int T, int H, int I, int E, int k) {
   p.o_err = o;     o += 256;
   // the single-launch T=1 region sits at the same offset for every T, so a workspace
   // keeps its self-resetting counters valid when calls with other T values reuse it
-  p.o_fx = o;      o = up256(o + dqg::fused_ws_bytes(H, I, k));
+  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, k) : 0));
   p.o_nact = o;    o += 256;
   p.o_actexp = o;  o = up256(o + sizeof(int) * p.A);
   p.o_actoff = o;  o = up256(o + sizeof(int) * (p.A + 1));
@@ -136,8 +136,8 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
   return a;
 }
 
-bool use_fused(int T, int E, int k, int format) {
-  return T == 1 && E <= 512 && k <= 32 && !(format & DQG_PATH_NO_FUSED);
+bool use_fused(int T, int H, int I, int E, int k, int format) {
+  return T == 1 && E <= 512 && dqg::fused_supported(H, I, k) && !(format & DQG_PATH_NO_FUSED);
 }
 
 int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint8_t* wgu,
@@ -254,7 +254,7 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k);
-  if (use_fused(T, E, k, format))
+  if (use_fused(T, H, I, E, k, format))
     return run_fused(p, x, logits, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
                      out, ids_out, weights_out, workspace, stream);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,

@@ -416,6 +416,33 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   }
 }
 
+// ---- workgroup column sums ----------------------------------------------------------------
+// Lane tid owns columns chunk*16 .. chunk*16+15 of row-lane tid / CPR (chunk = tid % CPR).
+// Sum the 16 partials over all row-lanes: one LDS transpose (4 x b128 writes per lane, a
+// barrier, then thread c < CPR*16 reads its column from every row-lane with all reads in
+// flight).  Summation order is fixed (row-lane ascending).  `red` holds THREADS*16 floats;
+// the caller must not overwrite it before a following barrier.
+template <int CPR, int THREADS>
+__device__ __forceinline__ float wg_colsum(const float (&acc)[16], float* red, int tid) {
+  constexpr int RL = THREADS / CPR, COLS = CPR * 16;
+  const int rl = tid / CPR, ch = tid % CPR;
+  float4* dst = reinterpret_cast<float4*>(red + rl * COLS + ch * 16);
+  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  dst[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+  dst[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+  __syncthreads();
+  float s = 0.0f;
+  if (tid < COLS) {
+    float v[RL];
+#pragma unroll
+    for (int r = 0; r < RL; ++r) v[r] = red[r * COLS + tid];
+#pragma unroll
+    for (int r = 0; r < RL; ++r) s += v[r];
+  }
+  return s;
+}
+
 // ---- cross-workgroup exchange ----------------------------------------------------------
 // Data that another workgroup reads within the same launch moves with agent-coherent
 // (sc1) loads and stores: relaxed agent-scope atomic accesses, which need no cache

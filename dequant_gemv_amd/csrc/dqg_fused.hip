@@ -3,30 +3,32 @@
 //
 // FireEcho page, "The Goliath Kernel: Why It's Fast": one launch reads the expert ids from
 // device memory and indexes the contiguous packed buffer, with the dequant in registers
-// inside the tile loop.  On MI355X a launch costs about 1.6 us even inside a graph, a whole
-// T=1 layer moves only ~21 MB, and every dependent memory round trip costs about 1 us, so
-// the layer is one launch and its workgroups exchange data with as few round trips as
-// possible: consumers poll the data itself instead of a separate counter.
+// inside the tile loop.  Measured on MI355X: a launch costs about 1.6 us even inside a
+// graph, every dependent memory round trip about 1 us, and a workgroup that reads a matrix
+// in 128-byte row segments streams about 2.5x faster than one reading 32-byte segments.
+// A whole T=1 layer moves only ~21 MB, so it is one launch whose workgroups read full
+// 128-byte lines and exchange data with as few round trips as possible.
 //
-// Workgroups (256 threads, 4 waves) play one of two roles, decided by blockIdx.x:
-//   gate_up (the first n_a = k * I/32 workgroups): slot j, h columns [32t, 32t+32).  64
-//     row-lanes x 4 lanes (2 x 16 B of gate, 2 x 16 B of up per byte row) walk all H/32
-//     K blocks; the K reduction stays in registers, wave shuffles and LDS.  SiLU(g)*u is
-//     stored to the h buffer with agent-coherent (sc1) stores.
-//   down + combine (the rest): output columns [64m, 64m+64) for one chunk of 64 K blocks
-//     of the concatenated (slot, K block) list.  The weights are loaded first; then each
-//     lane polls the 32 h values of its block until they are all published, scales its
-//     block sum by its slot weight, and the workgroup reduces in LDS.  The last chunk of a
-//     column tile polls the other chunks' partial rows, sums all chunks in ascending order,
-//     adds the residual and writes bf16 out (deterministic).
-// Publication protocol: the h and partial buffers hold the bit pattern 0 when empty, and a
-// producer never stores 0 (+0.0 is stored as -0.0, which computes identically).  Each
-// buffer exists twice; a call uses copy p = (completed calls) & 1, read from a 64-bit call
-// counter that the last chunk of every column tile increments without waiting, and its
-// producers clear their slots of copy 1-p, which the previous call used and which the next
-// call will use.  Polls are bounded and report a timeout in the error word (bit 1) instead
-// of hanging.  Down workgroups only wait on workgroups with lower block ids (gate_up, and
-// the earlier chunks of their tile), so in-order dispatch cannot deadlock.
+// Workgroups (256 threads, 4 waves), every lane owning 16 columns x 8 byte rows:
+//   gate_up units (j, nt, ks): slot j, h columns [128 nt, 128 nt + 128) -- 128 bytes of
+//     gate and 128 bytes of up per byte row (16 lanes) -- over byte rows
+//     [128 ks, 128 ks + 128) (16 row-lanes x 8 rows).  Each publishes its partial gate/up
+//     row and exits; gate_up units never wait.
+//   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
+//     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
+//     rows).  Weights are loaded first; then 128 threads gather the KS partial gate/up rows
+//     of the unit's 512 h values (ascending ks), form h = SiLU(g)*u into LDS, and every
+//     lane scales its sum by its slot weight.  Units c < NC-1 publish a partial output
+//     row; unit c = NC-1 gathers them in ascending c, adds its own, the residual, and
+//     writes bf16 out.
+// Publication protocol: exchange buffers hold the bit pattern 0 when empty and producers
+// never store 0 (+0.0 is stored as -0.0, which computes identically); consumers poll the
+// data itself with agent-coherent (sc1) loads, all of a gather's loads in flight at once.
+// Each buffer exists twice: a call uses copy p = (completed calls) & 1, read from a 64-bit
+// counter that every gathering down unit increments without waiting, and producers clear
+// their slots of copy 1-p, which the previous call used and the next call will use.  A
+// unit only waits on units with lower block ids, so in-order dispatch cannot deadlock;
+// waits are bounded and set bit 1 of the error word on timeout instead of hanging.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,23 +51,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// sum over the 16 row-lanes of a wave that share (lane % 4)
-__device__ __forceinline__ float wave_sum_rl4(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
+constexpr int FX_ROWS = 8;        // byte rows per lane
+constexpr int FX_KROWS = 128;     // gate_up byte rows per unit (16 row-lanes x 8)
+constexpr int FX_DROWS = 256;     // down byte rows per unit (32 row-lanes x 8)
+constexpr int FX_MAX_KS = 8;      // gate_up K splits (H <= 2048 on this path)
 
-// One K block (16 byte rows) of a lane's 16 columns against activations held in
-// registers: xr[r] is the pair for byte row r (bf16 for FP4, fp16 for INT4 in the gate_up
-// role); for the fp32 role xf[2r], xf[2r+1].
 template <int FMT>
-__device__ __forceinline__ void block_dot_x16(const uint4 (&wv)[BLK_ROWS],
-                                              const uint32_t (&xr)[BLK_ROWS], float (&acc)[16]) {
+__device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[FX_ROWS],
+                                           const uint32_t (&xr)[FX_ROWS], float (&acc)[16]) {
 #pragma unroll
-  for (int r = 0; r < BLK_ROWS; ++r) {
+  for (int r = 0; r < FX_ROWS; ++r) {
     const uint32_t d[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
     if constexpr (FMT == FMT_FP4) {
       const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xr[r]);
@@ -90,12 +85,12 @@ __device__ __forceinline__ void block_dot_x16(const uint4 (&wv)[BLK_ROWS],
 }
 
 template <int FMT>
-__device__ __forceinline__ void block_dot_f32(const uint4 (&wv)[BLK_ROWS],
-                                              const float (&xf)[2 * BLK_ROWS], float (&acc)[16]) {
+__device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[FX_ROWS],
+                                             const float (&hf)[2 * FX_ROWS], float (&acc)[16]) {
 #pragma unroll
-  for (int r = 0; r < BLK_ROWS; ++r) {
+  for (int r = 0; r < FX_ROWS; ++r) {
     const uint32_t d[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
-    const float x0 = xf[2 * r], x1 = xf[2 * r + 1];
+    const float x0 = hf[2 * r], x1 = hf[2 * r + 1];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (FMT == FMT_FP4) {
@@ -121,9 +116,9 @@ __device__ __forceinline__ void block_dot_f32(const uint4 (&wv)[BLK_ROWS],
   }
 }
 
-__device__ __forceinline__ void load_block(const uint8_t* wp, size_t ld, uint4 (&wv)[BLK_ROWS]) {
+__device__ __forceinline__ void load_rows(const uint8_t* wp, size_t ld, uint4 (&wv)[FX_ROWS]) {
 #pragma unroll
-  for (int r = 0; r < BLK_ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
+  for (int r = 0; r < FX_ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
 }
 
 __device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16]) {
@@ -137,22 +132,17 @@ __device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16]) {
   }
 }
 
-// block b of the gate_up role: x pairs for byte rows 16b..16b+15 (+ INT4 bias correction)
+// x pairs of byte rows r0 .. r0+7 (+ the INT4 bias correction of those rows)
 template <int FMT>
-__device__ __forceinline__ float load_x_block(const uint16_t* x, int b, uint32_t (&xr)[BLK_ROWS]) {
-  const uint4* xp = reinterpret_cast<const uint4*>(x) + b * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = xp[i];
-    xr[4 * i + 0] = v.x;
-    xr[4 * i + 1] = v.y;
-    xr[4 * i + 2] = v.z;
-    xr[4 * i + 3] = v.w;
-  }
+__device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t (&xr)[FX_ROWS]) {
+  const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(x) + r0);
+  const uint4 v0 = xp[0], v1 = xp[1];
+  xr[0] = v0.x; xr[1] = v0.y; xr[2] = v0.z; xr[3] = v0.w;
+  xr[4] = v1.x; xr[5] = v1.y; xr[6] = v1.z; xr[7] = v1.w;
   float corr = 0.0f;
   if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-    for (int r = 0; r < BLK_ROWS; ++r) {
+    for (int r = 0; r < FX_ROWS; ++r) {
       const f16x2_t h = {(_Float16)bf16_lo(xr[r]), (_Float16)bf16_hi(xr[r])};
       xr[r] = __builtin_bit_cast(uint32_t, h);
       corr = fmaf(-INT4_F16_BIAS_LO, (float)h.x, corr);
@@ -162,16 +152,31 @@ __device__ __forceinline__ float load_x_block(const uint16_t* x, int b, uint32_t
   return corr;
 }
 
+// Poll n (<= 16) published floats p[i * stride] until none is the empty pattern; all loads
+// of one round are in flight together.  Returns false on timeout.
+__device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n, float* v) {
+  for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
+    bool ready = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < n) v[i] = ld_sc1(p, (size_t)i * stride);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < n) ready = ready && (__float_as_uint(v[i]) != 0u);
+    if (ready) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
-  __shared__ float s_red[4][64];
+  __shared__ __align__(16) float s_red[FX_THREADS * 16];
   __shared__ int s_par;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
-  const int rl = tid >> 2, ch = tid & 3;
-  const int n_mt = H / 64;
 
   // ---- routing (wave 0 of every workgroup) and the buffer parity (wave 1) ----
   if (wv == 0) {
@@ -189,159 +194,161 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   } else if (tid == 64) {
     const unsigned long long calls =
         __hip_atomic_load(a.calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_par = (int)((calls / (unsigned long long)n_mt) & 1ull);
+    s_par = (int)((calls / (unsigned long long)a.n_mt) & 1ull);
   }
   __syncthreads();
   const int par = s_par;
-  float* hbuf = a.h + (size_t)par * k * I;
-  float* hold = a.h + (size_t)(1 - par) * k * I;
-  float* pbuf = a.ypart + (size_t)par * a.n_chunks * H;
-  float* pold = a.ypart + (size_t)(1 - par) * a.n_chunks * H;
+  const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
+  const size_t gsz = (size_t)k * NT * KS * 256;     // one copy of the gate/up partial rows
+  const size_t psz = (size_t)a.n_mt * NC * 128;
+  float* gpart = a.gpart + par * gsz;
+  float* gold = a.gpart + (1 - par) * gsz;
+  float* pbuf = a.ypart + par * psz;
+  float* pold = a.ypart + (1 - par) * psz;
 
   const int bid = blockIdx.x;
-  const int tiles_a = I / 32;
   if (bid < a.n_a) {
-    // ================= gate_up role =================
-    int u = bid;
-    if ((a.n_a & 31) == 0) {  // keep the 4 tiles that share 128-byte lines on one XCD
-      const int xcd = bid & 7, slot = bid >> 3;
-      u = (slot >> 2) * 32 + xcd * 4 + (slot & 3);
-    }
-    const int j = u / tiles_a, t = u - j * tiles_a;
+    // ================= gate_up unit (j, nt, ks) =================
+    const int ks = bid % KS, grp = bid / KS;
+    const int j = grp / NT, nt = grp - j * NT;
     const int e = s_ids[j];
+    const int rl = tid >> 4, ch = tid & 15;
     const size_t ld = 2 * (size_t)I;
+    const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
+    const int r0 = ks * FX_KROWS + FX_ROWS * rl;
     const uint8_t* w = a.wgu + (size_t)e * (H / 2) * ld;
-    const uint16_t* sc = a.sgu + (size_t)e * (H / a.group) * ld;
-    const int col0 = (ch < 2) ? (32 * t + 16 * ch) : (I + 32 * t + 16 * (ch - 2));
-    float acc[16];
+    uint4 wvv[FX_ROWS];
+    load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
+    float sf[16];
+    scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((2 * r0) / a.group) * ld + col0, sf);
+    uint32_t xr[FX_ROWS];
+    const float corr = load_x_rows<FMT>(a.x, r0, xr);
+    float accb[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
-    const int nblk = H / 32;
-    for (int b = rl; b < nblk; b += FX_RL) {
-      uint4 wvv[BLK_ROWS];
-      load_block(w + (size_t)b * BLK_ROWS * ld + col0, ld, wvv);
-      float sf[16];
-      scales16(sc + (size_t)((b * 32) / a.group) * ld + col0, sf);
-      uint32_t xr[BLK_ROWS];
-      const float corr = load_x_block<FMT>(a.x, b, xr);
-      float accb[16];
+    for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
+    rows_dot_x<FMT>(wvv, xr, accb);
+    // reduce the 16 row-lanes; thread i then owns partial column i (i < 128 gate, else up)
 #pragma unroll
-      for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
-      block_dot_x16<FMT>(wvv, xr, accb);
-#pragma unroll
-      for (int c = 0; c < 16; ++c) acc[c] = fmaf(sf[c], accb[c] + corr, acc[c]);
-    }
-    // reduce over row-lanes: 16 per wave, then 4 waves
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const float v = wave_sum_rl4(acc[c]);
-      if (lane < 4) s_red[wv][lane * 16 + c] = v;
-    }
-    __syncthreads();
-    if (tid < 32) {
-      // column n of the tile: gate sum in s_red[.][n], up sum in s_red[.][32 + n]
-      float g = 0.0f, uu = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        g += s_red[q][tid];
-        uu += s_red[q][32 + tid];
-      }
-      const int idx = j * I + 32 * t + tid;
-      st_sc1(hbuf, idx, pub(g / (1.0f + expf(-g)) * uu));
-      st_sc1(hold, idx, 0.0f);
-    }
+    for (int c = 0; c < 16; ++c) accb[c] = sf[c] * (accb[c] + corr);
+    const float mine = wg_colsum<16, FX_THREADS>(accb, s_red, tid);
+    const size_t slot = (size_t)grp * KS + ks;
+    st_sc1(gpart, slot * 256 + tid, pub(mine));
+    st_sc1(gold, slot * 256 + tid, 0.0f);
     return;
   }
 
-  // ================= down + combine role =================
-  const int nblkI = I / 32;
-  int ub = bid - a.n_a;
-  if ((a.n_b & 15) == 0) {  // adjacent 64-column tiles (one 128-byte line) on one XCD
-    const int xcd = ub & 7, slot = ub >> 3;
-    ub = (slot >> 1) * 16 + xcd * 2 + (slot & 1);
+  // ================= down unit (mt, c) =================
+  const int ub = bid - a.n_a;
+  const int mt = ub / NC, c = ub - mt * NC;
+  const int rl = tid >> 3, ch = tid & 7;
+  const int col0 = 128 * mt + 16 * ch;
+  const int R = c * FX_DROWS + FX_ROWS * rl;     // row in the concatenated slot list
+  const int rows_per_slot = I / 2;
+  const bool active = R < k * rows_per_slot;
+  const int j = active ? R / rows_per_slot : 0;
+  const int r0 = active ? R - j * rows_per_slot : 0;
+  uint4 wvv[FX_ROWS];
+  float sf[16];
+  if (active) {
+    const int e = s_ids[j];
+    load_rows(a.wd + (size_t)e * rows_per_slot * H + (size_t)r0 * H + col0, H, wvv);
+    scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((2 * r0) / a.group) * H + col0, sf);
   }
-  const int chunk = ub / n_mt, mt = ub - chunk * n_mt;
-  const int q = chunk * FX_RL + rl;  // this row-lane's (slot, K block)
-  const bool active = q < k * nblkI;
-  const int j = active ? q / nblkI : 0;
-  const int b = active ? q - j * nblkI : 0;
-  const int col0 = 64 * mt + 16 * ch;
+  // gather h for this unit's rows: flat h index f = 2 R covers [512 c, 512 c + 512); thread
+  // t owns f = 512 c + 2t, +1 (two columns of one slot); the KS partial gate and up pairs
+  // are polled together and summed in ascending ks
+  float* hl = s_red;  // 512 floats, reused as the reduction buffer afterwards
+  {
+    const int f = 512 * c + 2 * tid;
+    float2 h2 = make_float2(0.0f, 0.0f);
+    if (f < k * I) {
+      const int jj = f / I, n = f - jj * I, nt = n >> 7, nc = n & 127;
+      const __amdgpu_buffer_rsrc_t gr = rsrc(gpart);
+      const int base = (((jj * NT + nt) * KS) * 256 + nc) * 4;
+      f32x2_t g2 = {0.0f, 0.0f}, u2 = {0.0f, 0.0f};
+      bool ok = false;
+      for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
+        f32x2_t gv[FX_MAX_KS], uv[FX_MAX_KS];
+#pragma unroll
+        for (int q = 0; q < FX_MAX_KS; ++q) {
+          if (q < KS) {
+            gv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024, 0, CPOL_SC1);
+            uv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024 + 512, 0, CPOL_SC1);
+          }
+        }
+        bool ready = true;
+#pragma unroll
+        for (int q = 0; q < FX_MAX_KS; ++q)
+          if (q < KS)
+            ready = ready && __float_as_uint(gv[q].x) && __float_as_uint(gv[q].y) &&
+                    __float_as_uint(uv[q].x) && __float_as_uint(uv[q].y);
+        if (ready) {
+          g2 = gv[0];
+          u2 = uv[0];
+#pragma unroll
+          for (int q = 1; q < FX_MAX_KS; ++q)
+            if (q < KS) {
+              g2 += gv[q];
+              u2 += uv[q];
+            }
+          ok = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      if (!ok) atomicOr(a.err, 2);
+      h2 = make_float2(g2.x / (1.0f + expf(-g2.x)) * u2.x, g2.y / (1.0f + expf(-g2.y)) * u2.y);
+    }
+    reinterpret_cast<float2*>(hl)[tid] = h2;
+  }
+  __syncthreads();
   float acc[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) acc[c] = 0.0f;
+  for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
   if (active) {
-    uint4 wvv[BLK_ROWS];
-    float sf[16];
-    const int e = s_ids[j];
-    const uint8_t* w = a.wd + (size_t)e * (I / 2) * H;
-    const uint16_t* sc = a.sd + (size_t)e * (I / a.group) * H;
-    load_block(w + (size_t)b * BLK_ROWS * H + col0, H, wvv);
-    scales16(sc + (size_t)((b * 32) / a.group) * H + col0, sf);
-    // poll the 32 h values of this block until all are published
-    float hf[2 * BLK_ROWS];
-    const __amdgpu_buffer_rsrc_t hr = rsrc(hbuf);
-    const int hoff = (j * I + 32 * b) * 4;
-    unsigned spins = 0;
-    while (true) {
-      bool ready = true;
+    float hf[2 * FX_ROWS];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const f32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(hr, hoff + 16 * i, 0, CPOL_SC1);
-        hf[4 * i + 0] = v.x;
-        hf[4 * i + 1] = v.y;
-        hf[4 * i + 2] = v.z;
-        hf[4 * i + 3] = v.w;
-        ready = ready && __float_as_uint(v.x) && __float_as_uint(v.y) && __float_as_uint(v.z) &&
-                __float_as_uint(v.w);
-      }
-      if (ready) break;
-      if (++spins > FX_SPIN_LIMIT) {
-        atomicOr(a.err, 2);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(hl)[4 * rl + i];
+      hf[4 * i + 0] = v.x;
+      hf[4 * i + 1] = v.y;
+      hf[4 * i + 2] = v.z;
+      hf[4 * i + 3] = v.w;
     }
     float corr = 0.0f;
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-      for (int i = 0; i < 2 * BLK_ROWS; ++i) corr += hf[i];
+      for (int i = 0; i < 2 * FX_ROWS; ++i) corr += hf[i];
       corr *= -8.0f;
     }
     float accb[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
-    block_dot_f32<FMT>(wvv, hf, accb);
+    for (int q = 0; q < 16; ++q) accb[q] = 0.0f;
+    rows_dot_f32<FMT>(wvv, hf, accb);
     const float wj = s_w[j];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = wj * (sf[c] * (accb[c] + corr));
+    for (int q = 0; q < 16; ++q) acc[q] = wj * (sf[q] * (accb[q] + corr));
   }
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const float v = wave_sum_rl4(acc[c]);
-    if (lane < 4) s_red[wv][lane * 16 + c] = v;
-  }
-  __syncthreads();
-  if (tid >= 64) return;
-  const float mine = (s_red[0][tid] + s_red[1][tid]) + (s_red[2][tid] + s_red[3][tid]);
-  const int m = 64 * mt + tid;
-  if (chunk != a.n_chunks - 1) {
-    st_sc1(pbuf, (size_t)chunk * H + m, pub(mine));
-    st_sc1(pold, (size_t)chunk * H + m, 0.0f);
+  __syncthreads();  // hl is reused by the reduction below
+  // reduce the 32 row-lanes; thread i < 128 then owns output column 128 mt + i
+  const float mine = wg_colsum<8, FX_THREADS>(acc, s_red, tid);
+  if (tid >= 128) return;
+  const int m = 128 * mt + tid;
+  const size_t row0 = (size_t)mt * NC;
+  if (c != NC - 1) {
+    st_sc1(pbuf, (row0 + c) * 128 + tid, pub(mine));
+    st_sc1(pold, (row0 + c) * 128 + tid, 0.0f);
     return;
   }
-  // last chunk of the tile: gather the earlier chunks' partial rows in order
+  // last chunk of the tile: gather the earlier chunks' rows (all in flight), ascending c
   float y = 0.0f;
-  for (int c = 0; c < a.n_chunks - 1; ++c) {
-    float v;
-    unsigned spins = 0;
-    while (__float_as_uint(v = ld_sc1(pbuf, (size_t)c * H + m)) == 0u) {
-      if (++spins > FX_SPIN_LIMIT) {
-        atomicOr(a.err, 2);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    y += v;
+  for (int c0 = 0; c0 < NC - 1; c0 += 16) {
+    const int n = min(16, NC - 1 - c0);
+    float pv[16];
+    if (!gather_sc1(pbuf + (row0 + c0) * 128 + tid, 128, n, pv)) atomicOr(a.err, 2);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < n) y += pv[i];
   }
   y += mine;
   if (a.res) y += bf16_to_f32(a.res[m]);
@@ -349,25 +356,30 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   if (tid == 0) __hip_atomic_fetch_add(a.calls, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+bool fused_supported(int H, int I, int k) {
+  return H % 256 == 0 && I % 128 == 0 && H / 2 / FX_KROWS <= FX_MAX_KS && k <= 32;
+}
+
 size_t fused_ws_bytes(int H, int I, int k) {
-  const int n_chunks = (k * (I / 32) + FX_RL - 1) / FX_RL;
-  size_t o = 256;                               // call counter
-  o += 2 * (size_t)k * I * 4;                   // h, two copies
-  o = (o + 255) & ~(size_t)255;
-  o += 2 * (size_t)n_chunks * H * 4;            // partial rows, two copies
+  const int KS = H / 2 / FX_KROWS, NT = I / 128, n_mt = H / 128;
+  const int NC = (k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
+  size_t o = 256;                                         // call counter
+  o += 2 * (size_t)k * NT * KS * 256 * 4;                 // gate/up partial rows
+  o += 2 * (size_t)n_mt * NC * 128 * 4;                   // output partial rows
   return (o + 255) & ~(size_t)255;
 }
 
 void fused_layout(FusedArgs& f, void* ws, int H, int I, int k) {
   char* p = static_cast<char*>(ws);
-  f.n_chunks = (k * (I / 32) + FX_RL - 1) / FX_RL;
-  f.n_a = k * (I / 32);
-  f.n_b = f.n_chunks * (H / 64);
+  f.ks = H / 2 / FX_KROWS;
+  f.n_mt = H / 128;
+  f.n_chunks = (k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
+  f.n_a = k * (I / 128) * f.ks;
+  f.n_b = f.n_mt * f.n_chunks;
   f.calls = reinterpret_cast<unsigned long long*>(p);
   size_t o = 256;
-  f.h = reinterpret_cast<float*>(p + o);
-  o += 2 * (size_t)k * I * 4;
-  o = (o + 255) & ~(size_t)255;
+  f.gpart = reinterpret_cast<float*>(p + o);
+  o += 2 * (size_t)k * (I / 128) * f.ks * 256 * 4;
   f.ypart = reinterpret_cast<float*>(p + o);
 }
 

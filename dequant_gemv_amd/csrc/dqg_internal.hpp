@@ -68,12 +68,13 @@ struct FusedArgs {
   uint16_t* out;
   int32_t* ids_out;     // optional routing outputs (may be null)
   float* w_out;
-  float* h;             // [2][k, I]         SiLU(gate)*up, two copies
-  float* ypart;         // [2][n_chunks, H]  partial output rows, two copies
+  float* gpart;         // [2][k * I/128 * ks][256] gate/up partial rows, two copies
+  float* ypart;         // [2][H/128 * n_chunks][128] output partial rows, two copies
   unsigned long long* calls;  // completed column tiles over all calls (parity source)
   int* err;
-  int n_a, n_b, n_chunks;
+  int n_a, n_b, n_chunks, ks, n_mt;
 };
+bool fused_supported(int H, int I, int k);
 size_t fused_ws_bytes(int H, int I, int k);
 void fused_layout(FusedArgs& f, void* ws, int H, int I, int k);
 hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st);

@@ -137,30 +137,18 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
   }
 }
 
-// =====================================================================================
-// reductions over the row-lanes of a workgroup
-// =====================================================================================
-// Lanes that share (lane % CPR) own the same columns; sum them inside the wave.
-template <int CPR>
-__device__ __forceinline__ float wave_sum_rowlanes(float v) {
-#pragma unroll
-  for (int off = CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-// acc[NT][16] of every lane -> red[wave][t][ch*16 + j] (wave-reduced), then the caller
-// sums over waves.
-template <int CPR, int NT>
-__device__ __forceinline__ void reduce_to_lds(float (&acc)[NT][16], float* red, int tid) {
-  const int lane = tid & 63, wv = tid >> 6, ch = lane % CPR;
+// Column totals of acc[NT][16] over the workgroup's row-lanes, token by token, through one
+// LDS transpose each (wg_colsum); tot[t * COLS + c] receives token t's total of column c.
+template <int CPR, int THREADS, int NT>
+__device__ __forceinline__ void colsum_tokens(const float (&acc)[NT][16], float* red, float* tot,
+                                              int tid) {
   constexpr int COLS = CPR * 16;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float v = wave_sum_rowlanes<CPR>(acc[t][j]);
-      if (lane < CPR) red[(wv * NT + t) * COLS + ch * 16 + j] = v;
-    }
+  for (int t = 0; t < NT; ++t) {
+    const float v = wg_colsum<CPR, THREADS>(acc[t], red, tid);
+    if (tid < COLS) tot[t * COLS + tid] = v;
+    __syncthreads();
+  }
 }
 
 // =====================================================================================
@@ -195,7 +183,8 @@ __global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
 
   uint32_t* xl = reinterpret_cast<uint32_t*>(smem);                   // [NT][Kp]
   float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
-  float* red = corr + NT * nblk;                                      // [4][NT][128]
+  float* red = corr + NT * nblk;                                      // [GU_THREADS * 16]
+  float* tot = red + GU_THREADS * 16;                                 // [NT][128]
   __shared__ int s_flag;
 
   for (int c0 = 0; c0 < cnt; c0 += NT) {
@@ -213,18 +202,12 @@ __global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
       for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
     tile_rows<FMT, XM, NT>(w, sc, (int)ld, a.group, col0, b0 + rl, b1, GU_RL, xl, Kp, corr, nblk,
                            acc);
-    reduce_to_lds<GU_CPR, NT>(acc, red, tid);
-    __syncthreads();
+    colsum_tokens<GU_CPR, GU_THREADS, NT>(acc, red, tot, tid);
     // thread (t, n): gate column n and up column n of the tile
     for (int i = tid; i < NT * 64; i += GU_THREADS) {
       const int t = i / 64, n = i % 64;
       if (c0 + t >= cnt) continue;
-      float g = 0.0f, u = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < GU_WAVES; ++wv) {
-        g += red[(wv * NT + t) * 128 + n];
-        u += red[(wv * NT + t) * 128 + 64 + n];
-      }
+      const float g = tot[t * 128 + n], u = tot[t * 128 + 64 + n];
       const int slot = a.ws.slot_list[beg + c0 + t];
       if (S == 1) {
         a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
@@ -300,7 +283,8 @@ __global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
 
   float2* xl = reinterpret_cast<float2*>(smem);                       // [NT][Kp]
   float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
-  float* red = corr + NT * nblk;                                      // [4][NT][64]
+  float* red = corr + NT * nblk;                                      // [DN_THREADS * 16]
+  float* tot = red + DN_THREADS * 16;                                 // [NT][64]
   __shared__ int s_last[NT];
 
   for (int c0 = 0; c0 < cnt; c0 += NT) {
@@ -318,14 +302,11 @@ __global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
       for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
     tile_rows<FMT, X_F32, NT>(w, sc, H, a.group, col0, b0 + rl, b1, DN_RL, xl, Kp, corr, nblk,
                               acc);
-    reduce_to_lds<DN_CPR, NT>(acc, red, tid);
-    __syncthreads();
+    colsum_tokens<DN_CPR, DN_THREADS, NT>(acc, red, tot, tid);
     for (int i = tid; i < NT * 64; i += DN_THREADS) {
       const int t = i / 64, c = i % 64;
       if (c0 + t >= cnt) continue;
-      float v = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < DN_WAVES; ++wv) v += red[(wv * NT + t) * 64 + c];
+      const float v = tot[t * 64 + c];
       const int slot = a.ws.slot_list[beg + c0 + t];
       st_sc1(a.ws.part_dn, ((size_t)s * TK + slot) * H + tile * 64 + c, v);
     }
@@ -372,7 +353,8 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
   const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
   uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
   float* corr = reinterpret_cast<float*>(xl + NT * Kp);
-  float* red = corr + NT * nblk;
+  float* red = corr + NT * nblk;                                      // [GV_THREADS * 16]
+  float* tot = red + GV_THREADS * 16;                                 // [NT][64]
   __shared__ int s_flag;
 
   for (int c0 = 0; c0 < T; c0 += NT) {
@@ -389,14 +371,11 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
       for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
     tile_rows<FMT_INT4, X_F16, NT>(g.w, g.s, N, g.group, col0, b0 + rl, b1, GV_RL, xl, Kp, corr,
                                    nblk, acc);
-    reduce_to_lds<GV_CPR, NT>(acc, red, tid);
-    __syncthreads();
+    colsum_tokens<GV_CPR, GV_THREADS, NT>(acc, red, tot, tid);
     for (int i = tid; i < NT * 64; i += GV_THREADS) {
       const int t = i / 64, c = i % 64;
       if (c0 + t >= T) continue;
-      float v = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < GV_WAVES; ++wv) v += red[(wv * NT + t) * 64 + c];
+      const float v = tot[t * 64 + c];
       const int n = tile * 64 + c;
       if (S == 1)
         g.y[(size_t)(c0 + t) * N + n] = f32_to_bf16(v);
@@ -477,7 +456,8 @@ hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st
 template <int FMT, int NT>
 static hipError_t launch_gateup_t(const MoeArgs& a, int A, hipStream_t st) {
   const int Kp = a.H / 2, nblk = a.H / 32;
-  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GU_WAVES * NT * 128 * 4;
+  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GU_THREADS * 16 * 4 +
+                    (size_t)NT * 128 * 4;
   hipLaunchKernelGGL((gateup_kernel<FMT, NT>), dim3(a.I / 64, a.S_gu, A), dim3(GU_THREADS), sm, st,
                      a);
   return hipGetLastError();
@@ -486,7 +466,8 @@ static hipError_t launch_gateup_t(const MoeArgs& a, int A, hipStream_t st) {
 template <int FMT, int NT>
 static hipError_t launch_down_t(const MoeArgs& a, int A, hipStream_t st) {
   const int Kp = a.I / 2, nblk = a.I / 32;
-  const size_t sm = (size_t)NT * Kp * 8 + (size_t)NT * nblk * 4 + (size_t)DN_WAVES * NT * 64 * 4;
+  const size_t sm = (size_t)NT * Kp * 8 + (size_t)NT * nblk * 4 + (size_t)DN_THREADS * 16 * 4 +
+                    (size_t)NT * 64 * 4;
   hipLaunchKernelGGL((down_kernel<FMT, NT>), dim3(a.H / 64, a.S_dn, A), dim3(DN_THREADS), sm, st,
                      a);
   return hipGetLastError();
@@ -513,7 +494,8 @@ hipError_t launch_moe_valu(const MoeArgs& a, int A, int nt, hipStream_t st) {
 template <int NT>
 static hipError_t launch_gemv_t(const GemvArgs& g, hipStream_t st) {
   const int Kp = g.K / 2, nblk = g.K / 32;
-  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GV_WAVES * NT * 64 * 4;
+  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GV_THREADS * 16 * 4 +
+                    (size_t)NT * 64 * 4;
   hipLaunchKernelGGL(gemv_kernel<NT>, dim3(g.N / 64, g.S), dim3(GV_THREADS), sm, st, g);
   return hipGetLastError();
 }
