@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["auto", "unfused"], default="auto")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (3 times); "
+                         "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
@@ -126,10 +129,21 @@ def main():
         sys.exit(2)
 
     import torch
-    from dequant_gemv_amd import binding as B
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    from dequant_gemv_amd import binding as B
     T, E, H, I, k, G = (SHAPE[s] for s in ("T", "E", "H", "I", "k", "group"))
     flags = B.PATH_NO_FUSED if args.path == "unfused" else 0
     x, layers = build_workload(args.layers, device=dev)
@@ -167,7 +181,8 @@ def main():
     ms_per_step = ms / args.steps
     us_per_layer = ms_per_step * 1000.0 / args.layers
 
-    # per-launch kernel time: events right before and after each layer call (eager)
+    # context only: events right before and after each eager layer call (includes the
+    # host launch overhead that the graph replay hides)
     per = []
     with torch.cuda.stream(stream):
         for rep in range(3):
@@ -180,14 +195,17 @@ def main():
                 a1.record(stream)
                 per.append((a0, a1))
     stream.synchronize()
-    launch_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)
-    kernel_us = launch_us[len(launch_us) // 2]
+    eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
 
     abytes, _ = active_bytes(H, I, G, k)
-    launches_per_layer = 1 if (args.path == "auto" and T == 1) else 3
+    fused = args.path == "auto" and T == 1
+    launches_per_layer = 1 if fused else 3
     gbps = abytes / (us_per_layer * 1e-6) / 1e9
-    kernel = "fused_t1_kernel" if launches_per_layer == 1 else "moe_layer_unfused"
-    kgbps = abytes / (kernel_us * 1e-6) / 1e9
+    # dominant kernel: on the single-launch path the whole layer is one kernel, so its
+    # average duration is the timed region (events on the replay stream) / launches
+    kernel = "fused_t1_kernel" if fused else "moe_layer_unfused"
+    avg_launch_us = us_per_layer / launches_per_layer if fused else us_per_layer
+    kgbps = abytes / (avg_launch_us * 1e-6) / 1e9
     roofline = {
         "bound": "hbm",
         "kernel": kernel,
@@ -197,11 +215,10 @@ def main():
         "frac": round(kgbps / HBM_PEAK_GBPS, 4),
         "traffic": read_traffic(kernel),
         "bytes_per_launch": abytes,
-        "avg_launch_us": round(kernel_us, 3),
-        "timing": "median over 3 x layers eager calls of the time between events recorded "
-                  "right before and after each layer call on its stream (one kernel launch "
-                  "per layer on the single-launch path; the whole call otherwise)",
-        "graph_us_per_layer": round(us_per_layer, 3),
+        "avg_launch_us": round(avg_launch_us, 3),
+        "timing": "events on the replay stream around the K timed graph replays, divided "
+                  "by the kernel launches they contain (steps x layers)",
+        "eager_call_us_median": round(eager_us, 3),
     }
     rec = {
         "metric": METRIC,
