@@ -2,15 +2,18 @@
 (E=128, H=2048, I=768, top-8, FP4 E2M1, group 32), with achieved HBM GB/s over the bytes
 of the active experts' packed weights and scales, against the 8 TB/s MI355X peak.
 
-One step = one token through a stack of `--layers` distinct layer weight sets (48 by
-default, about 1 GB of active expert bytes per step, four times the 256 MB last-level
-cache), each layer = routing from fp32 logits + gate_up + SiLU*up + down + top-k combine
-in one `moe_fp4_layer` call.  The layers are captured once into a graph; the timed region
+One step = one token through a stack of 48 distinct layer weight sets (about 1 GB of
+active expert bytes per step, four times the 256 MB last-level cache), each layer =
+routing from fp32 logits + gate_up + SiLU*up + down + top-k combine in one
+`moe_fp4_layer` call.  The layers are captured once into a graph; the timed region
 replays it K times between events on the capturing stream.  Inputs (weights, scales,
 activations, logits) are synthetic and already resident in device memory.
 
-Prints one JSON line (see the repository docs for the fields).  `--gpus` above 1 exits:
-this benchmark is single-GPU.
+`--workload` selects the other sizes (Q30 at T = 4, 16, 64; the 48-layer chained
+512-expert stack at T = 1, 8; a tiny INT4 layer; the dense INT4 GEMV with N = 256, 8192,
+34816 at T = 1, 4), each timed the same way.
+
+Prints one JSON line.  `--gpus` above 1 exits: this benchmark is single-GPU.
 """
 from __future__ import annotations
 
@@ -28,47 +31,125 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per MoE layer at T=1 and achieved HBM GB/s vs peak (Qwen3-30B-A3B shape)"
 HBM_PEAK_GBPS = 8000.0
-SHAPE = dict(T=1, E=128, H=2048, I=768, k=8, group=32)
+FP4, INT4 = 1, 0
+
+# Synthetic workloads (sizes of the 30B-A3B and 512-expert MoE layers, a tiny INT4 layer and
+# the dense INT4 GEMV).  `layers` distinct weight sets are rotated so that one timed pass
+# reads well past the 256 MB last-level cache; `chain` feeds each layer's output to the
+# next as both input and residual.
+WORKLOADS = {
+    "q30_moe_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                             scales=(0.002, 0.01), logits="normal", layers=48),
+    "q30_moe_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                             scales=(0.002, 0.01), logits="normal+bias", layers=48),
+    "q30_moe_layer_t16": dict(kind="moe", T=16, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                              scales=(0.002, 0.01), logits="normal+bias", layers=24),
+    "q30_moe_layer_t64": dict(kind="moe", T=64, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                              scales=(0.002, 0.01), logits="normal+bias", layers=12),
+    "w512_stack_t1": dict(kind="moe", T=1, E=512, H=2048, I=512, k=10, group=32, fmt=FP4,
+                          scales=(0.002, 0.01), logits="zipf", layers=48, chain=True),
+    "w512_stack_t8": dict(kind="moe", T=8, E=512, H=2048, I=512, k=10, group=32, fmt=FP4,
+                          scales=(0.002, 0.01), logits="zipf", layers=48, chain=True),
+    "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
+                              scales=(0.005, 0.02), logits="normal", layers=48),
+    "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),
+    "gemv_int4_n8192_t1": dict(kind="gemv", T=1, K=5120, N=8192, group=128, copies=48),
+    "gemv_int4_n8192_t4": dict(kind="gemv", T=4, K=5120, N=8192, group=128, copies=48),
+    "gemv_int4_n34816_t1": dict(kind="gemv", T=1, K=5120, N=34816, group=128, copies=8),
+    "gemv_int4_n34816_t4": dict(kind="gemv", T=4, K=5120, N=34816, group=128, copies=8),
+}
+DEFAULT_WORKLOAD = "q30_moe_layer_t1"
+KERNEL_SOURCES = {
+    "fused_t1_kernel": ("dqg_fused.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+    "gemv_kernel": ("dqg_kernels.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+}
+
+
+def expert_bytes(H, I, G):
+    """Packed bytes + bf16 scales of one expert (gate_up and down)."""
+    return (H // 2) * (2 * I) + (H // G) * (2 * I) * 2 + (I // 2) * H + (I // G) * H * 2
 
 
 def active_bytes(H, I, G, k):
-    per_expert = (H // 2) * (2 * I) + (H // G) * (2 * I) * 2 + (I // 2) * H + (I // G) * H * 2
+    per_expert = expert_bytes(H, I, G)
     return k * per_expert, per_expert
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel=None) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dequant_gemv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = KERNEL_SOURCES.get(kernel) if kernel else None
+    for f in sorted(files or os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def build_workload(layers: int, seed: int = 0, device="cuda"):
-    """Layer weight sets drawn on the device: packed bytes uniform over 0..255 (every
-    nibble uniform), scales U(0.002, 0.01) rounded to bf16, x ~ N(0,1) in bf16, logits
-    ~ N(0,1) fp32, one set per layer."""
+def _bf16_scales(shape, lo, hi, g, device):
     import torch
-    T, E, H, I, G = SHAPE["T"], SHAPE["E"], SHAPE["H"], SHAPE["I"], SHAPE["group"]
+    return (torch.rand(shape, device=device, generator=g) * (hi - lo) + lo).to(torch.bfloat16)
+
+
+def _logits(w, g, device):
+    """Router logits of one layer: N(0,1), plus a per-expert N(0, 0.5) bias
+    ("normal+bias"), or -1.1 ln(1 + perm(e)) + N(0,1) over a per-layer permutation
+    ("zipf")."""
+    import torch
+    T, E = w["T"], w["E"]
+    lg = torch.randn((T, E), device=device, generator=g, dtype=torch.float32)
+    if w["logits"] == "normal+bias":
+        lg += 0.5 * torch.randn((E,), device=device, generator=g)[None, :]
+    elif w["logits"] == "zipf":
+        perm = torch.randperm(E, device=device, generator=g).to(torch.float32)
+        lg += -1.1 * torch.log1p(perm)[None, :]
+    return lg
+
+
+def build_moe_workload(w, seed: int = 0, device="cuda"):
+    """Layer weight sets drawn on the device: packed bytes uniform over 0..255 (every
+    nibble uniform), scales uniform in the workload's range rounded to bf16, x ~ N(0,1)
+    in bf16, logits as in _logits, one set per layer."""
+    import torch
+    T, E, H, I, G = w["T"], w["E"], w["H"], w["I"], w["group"]
+    lo, hi = w["scales"]
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     out = []
-    for _ in range(layers):
-        L = dict(
+    for _ in range(w["layers"]):
+        out.append(dict(
             w_gu=torch.randint(0, 256, (E, H // 2, 2 * I), dtype=torch.uint8, device=device,
                                generator=g),
-            s_gu=(torch.rand((E, H // G, 2 * I), device=device, generator=g) * 0.008 + 0.002
-                  ).to(torch.bfloat16),
+            s_gu=_bf16_scales((E, H // G, 2 * I), lo, hi, g, device),
             w_d=torch.randint(0, 256, (E, I // 2, H), dtype=torch.uint8, device=device,
                               generator=g),
-            s_d=(torch.rand((E, I // G, H), device=device, generator=g) * 0.008 + 0.002
-                 ).to(torch.bfloat16),
-            logits=torch.randn((T, E), device=device, generator=g, dtype=torch.float32),
-        )
-        out.append(L)
+            s_d=_bf16_scales((E, I // G, H), lo, hi, g, device),
+            logits=_logits(w, g, device),
+        ))
     x = torch.randn((T, H), device=device, generator=g).to(torch.bfloat16)
     return x, out
+
+
+def build_gemv_workload(w, seed: int = 0, device="cuda"):
+    """`copies` weight sets W ~ N(0, 0.02) [K, N], symmetric INT4 per group of 128 along K
+    (s = bf16(absmax / 7), q = clamp(rint(w / s), -8, 7), nibble q + 8, low nibble = even
+    K), and x ~ N(0,1) bf16 [T, K]."""
+    import torch
+    T, K, N, G = w["T"], w["K"], w["N"], w["group"]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    sets = []
+    for _ in range(w["copies"]):
+        wf = torch.randn((K, N), device=device, generator=g) * 0.02
+        wg = wf.view(K // G, G, N)
+        s = (wg.abs().amax(dim=1) / 7.0).to(torch.bfloat16)
+        s = torch.where(s == 0, torch.ones_like(s), s)
+        q = torch.clamp(torch.round(wg / s.float()[:, None, :]), -8, 7).to(torch.int16) + 8
+        q = q.view(K, N).to(torch.uint8)
+        packed = (q[0::2] | (q[1::2] << 4)).contiguous()
+        sets.append(dict(w=packed, s=s.contiguous()))
+        del wf, wg, q
+    x = torch.randn((T, K), device=device, generator=g).to(torch.bfloat16)
+    return x, sets
 
 
 def cpu_baseline(budget_s: float = 12.0):
@@ -95,9 +176,9 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"one BLAS thread, {t_total:.1f} s total"}
 
 
-def read_traffic(kernel: str):
+def read_traffic(kernel: str, workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, or None when
-    the kernel sources changed since the counters were taken."""
+    the kernel's sources changed since the counters were taken."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
@@ -105,10 +186,169 @@ def read_traffic(kernel: str):
         d = json.load(open(p))
     except Exception:
         return None
-    e = d.get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    e = d.get(f"{kernel}/{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def time_graph(fn, stream, steps, warmup):
+    """Capture fn() once into a graph on `stream`, replay `warmup` times, then time `steps`
+    replays with events recorded on `stream`.  Returns ms per replay."""
+    import torch
+    # every input was written on the default stream: finish that work first, or the
+    # caching allocator's reuse of freed temporaries can overlap buffers used here
+    torch.cuda.synchronize()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fn()  # eager warm-up on the capture stream
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fn()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+    stream.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def calibration(dev, stream):
+    """Context recorded with every run: a 1 GiB device copy (read + write GB/s) and the
+    per-launch floor of a graph of 256 one-element kernels."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ms = time_graph(lambda: dst.copy_(src), stream, 10, 3)
+    t = torch.zeros(1, device=dev)
+
+    def tiny():
+        for _ in range(256):
+            t.add_(1.0)
+    ms_tiny = time_graph(tiny, stream, 10, 3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
+            "graph_launch_floor_us": round(ms_tiny * 1000.0 / 256, 3)}
+
+
+def distinct_experts(logits, k):
+    """Distinct experts the router selects for a [T, E] logits tensor (accounting only)."""
+    import torch
+    return int(torch.unique(torch.topk(logits, k, dim=1).indices).numel())
+
+
+def bench_moe(w, args, dev, stream, B):
+    import torch
+    T, E, H, I, k, G = (w[s] for s in ("T", "E", "H", "I", "k", "group"))
+    fmt = B.FMT_FP4_E2M1 if w["fmt"] == FP4 else B.FMT_INT4
+    flags = {"auto": 0, "unfused": B.PATH_NO_FUSED, "gemv": B.PATH_FORCE_GEMV | B.PATH_NO_FUSED,
+             "mfma": B.PATH_FORCE_MFMA | B.PATH_NO_FUSED}[args.path]
+    x, layers = build_moe_workload(w, device=dev)
+    ws = B.moe_workspace(T, H, I, E, k, dev)
+    chain = w.get("chain", False)
+    xs = [x] + [torch.empty_like(x) for _ in layers]
+    torch.cuda.synchronize()
+
+    def call(l, L):
+        xin = xs[l] if chain else x
+        B.moe_fp4_layer(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
+                        residual=xin if chain else None, out=xs[l + 1], workspace=ws,
+                        flags=flags)
+
+    def one_pass():
+        for l, L in enumerate(layers):
+            call(l, L)
+
+    ms_per_step = time_graph(one_pass, stream, args.steps, args.warmup)
+    n_layers = len(layers)
+    us_per_layer = ms_per_step * 1000.0 / n_layers
+
+    # context only: events right before and after each eager layer call (includes the
+    # host launch overhead that the graph replay hides)
+    per = []
+    with torch.cuda.stream(stream):
+        for rep in range(3):
+            for l, L in enumerate(layers):
+                a0 = torch.cuda.Event(enable_timing=True)
+                a1 = torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+                call(l, L)
+                a1.record(stream)
+                per.append((a0, a1))
+    stream.synchronize()
+    eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
+
+    per_expert = expert_bytes(H, I, G)
+    n_active = [distinct_experts(L["logits"], k) for L in layers]
+    abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
+    fused = args.path == "auto" and T == 1 and E <= 512
+    gbps = abytes / (us_per_layer * 1e-6) / 1e9
+    # the single-launch path runs the whole layer in one kernel, so its average duration
+    # is the timed region (events on the replay stream) / launches; the multi-launch path
+    # is reported per layer (schedule + gate_up + down)
+    kernel = "fused_t1_kernel" if fused else "moe_layer_multi_launch"
+    roofline = {
+        "bound": "hbm",
+        "kernel": kernel,
+        "achieved": round(gbps, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "traffic": read_traffic(kernel, args.workload),
+        "bytes_per_launch": round(abytes),
+        "avg_launch_us": round(us_per_layer, 3),
+        "timing": "events on the replay stream around the K timed graph replays, divided "
+                  "by the layer calls they contain (steps x layers)",
+        "eager_call_us_median": round(eager_us, 3),
+    }
+    config = {"workload": args.workload, "T": T, "E": E, "H": H, "I": I, "k": k,
+              "format": "fp4_e2m1" if w["fmt"] == FP4 else "int4", "group": G,
+              "layers_per_step": n_layers, "chained": chain, "path": args.path,
+              "active_experts_per_layer_mean": round(sum(n_active) / n_layers, 2),
+              "active_bytes_per_layer": round(abytes)}
+    return dict(value=round(us_per_layer, 3), unit="us/layer", ms_per_step=ms_per_step,
+                achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
+
+
+def bench_gemv(w, args, dev, stream, B):
+    import torch
+    T, K, N, G = w["T"], w["K"], w["N"], w["group"]
+    x, sets = build_gemv_workload(w, device=dev)
+    ws = B.gemv_workspace(T, K, N, G, dev)
+    ys = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in sets]
+    torch.cuda.synchronize()
+
+    def one_pass():
+        for S_, y in zip(sets, ys):
+            B.packed_gemv_int4(x, S_["w"], S_["s"], G, y=y, workspace=ws)
+
+    ms_per_step = time_graph(one_pass, stream, args.steps, args.warmup)
+    us = ms_per_step * 1000.0 / len(sets)
+    abytes = (K // 2) * N + (K // G) * N * 2
+    gbps = abytes / (us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "gemv_kernel", "achieved": round(gbps, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic("gemv_kernel", args.workload), "bytes_per_launch": abytes,
+                "avg_launch_us": round(us, 3),
+                "timing": "events around the K timed graph replays / GEMV calls (one "
+                          "launch per call)"}
+    config = {"workload": args.workload, "T": T, "K": K, "N": N, "group": G, "format": "int4",
+              "weight_copies": len(sets)}
+    return dict(value=round(us, 3), unit="us/call", ms_per_step=ms_per_step,
+                achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
 
 
 def main():
@@ -116,9 +356,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=48)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["auto", "unfused"], default="auto")
+    ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--path", choices=["auto", "unfused", "gemv", "mfma"], default="auto",
+                    help="MoE kernel path: auto, or force the multi-launch path with its "
+                         "automatic / vector-ALU-only / matrix-core-only expert tiles")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 times); "
                          "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -144,104 +387,33 @@ def main():
         return
 
     from dequant_gemv_amd import binding as B
-    T, E, H, I, k, G = (SHAPE[s] for s in ("T", "E", "H", "I", "k", "group"))
-    flags = B.PATH_NO_FUSED if args.path == "unfused" else 0
-    x, layers = build_workload(args.layers, device=dev)
-    ws = B.moe_workspace(T, H, I, E, k, dev)
-    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in layers]
-
-    def one_pass():
-        for L, o in zip(layers, outs):
-            B.moe_fp4_layer(x, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G,
-                            B.FMT_FP4_E2M1, out=o, workspace=ws, flags=flags)
-
+    w = WORKLOADS[args.workload]
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(stream):
-        one_pass()  # eager warm-up on the capture stream
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        one_pass()
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            graph.replay()
-    stream.synchronize()
-    torch.cuda.synchronize(dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        e1.record(stream)
-    e1.synchronize()
-    torch.cuda.synchronize(dev)
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / args.steps
-    us_per_layer = ms_per_step * 1000.0 / args.layers
-
-    # context only: events right before and after each eager layer call (includes the
-    # host launch overhead that the graph replay hides)
-    per = []
-    with torch.cuda.stream(stream):
-        for rep in range(3):
-            for L, o in zip(layers, outs):
-                a0 = torch.cuda.Event(enable_timing=True)
-                a1 = torch.cuda.Event(enable_timing=True)
-                a0.record(stream)
-                B.moe_fp4_layer(x, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G,
-                                B.FMT_FP4_E2M1, out=o, workspace=ws, flags=flags)
-                a1.record(stream)
-                per.append((a0, a1))
-    stream.synchronize()
-    eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
-
-    abytes, _ = active_bytes(H, I, G, k)
-    fused = args.path == "auto" and T == 1
-    launches_per_layer = 1 if fused else 3
-    gbps = abytes / (us_per_layer * 1e-6) / 1e9
-    # dominant kernel: on the single-launch path the whole layer is one kernel, so its
-    # average duration is the timed region (events on the replay stream) / launches
-    kernel = "fused_t1_kernel" if fused else "moe_layer_unfused"
-    avg_launch_us = us_per_layer / launches_per_layer if fused else us_per_layer
-    kgbps = abytes / (avg_launch_us * 1e-6) / 1e9
-    roofline = {
-        "bound": "hbm",
-        "kernel": kernel,
-        "achieved": round(kgbps, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(kgbps / HBM_PEAK_GBPS, 4),
-        "traffic": read_traffic(kernel),
-        "bytes_per_launch": abytes,
-        "avg_launch_us": round(avg_launch_us, 3),
-        "timing": "events on the replay stream around the K timed graph replays, divided "
-                  "by the kernel launches they contain (steps x layers)",
-        "eager_call_us_median": round(eager_us, 3),
-    }
+    cal = None if args.no_calibration else calibration(dev, stream)
+    r = (bench_moe if w["kind"] == "moe" else bench_gemv)(w, args, dev, stream, B)
     rec = {
-        "metric": METRIC,
-        "value": round(us_per_layer, 3),
-        "unit": "us/layer",
+        "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
+        f"{r['unit'].replace('us/', 'µs per ')} and achieved HBM GB/s vs peak ({args.workload})",
+        "value": r["value"],
+        "unit": r["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
-        "data": "synthetic",
-        "config": {"workload": "q30_moe_layer_t1", "T": T, "E": E, "H": H, "I": I, "k": k,
-                   "format": "fp4_e2m1", "group": G, "layers_per_step": args.layers,
-                   "active_bytes_per_layer": abytes, "path": args.path},
-        "achieved_GBps": round(gbps, 1),
-        "roofline": roofline,
+        "data": "synthetic (seeded device RNG; inputs resident in HBM)",
+        "config": r["config"],
+        "achieved_GBps": r["achieved_GBps"],
+        "roofline": r["roofline"],
+        "calibration": cal,
         "device": torch.cuda.get_device_name(dev),
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdqg.so")
-SOURCES = ["dqg_kernels.hip", "dqg_fused.hip", "dqg_api.cpp"]
+SOURCES = ["dqg_kernels.hip", "dqg_experts.hip", "dqg_fused.hip", "dqg_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/dqg.h"
 #include "dqg_internal.hpp"
@@ -19,17 +20,20 @@ constexpr int kMaxK = 32;
 constexpr int kMaxTK = 65536;
 constexpr int kTargetWG = 512;   // workgroups per launch to aim for (2 per CU)
 constexpr int kMinBlocksPerWG = 8;
-constexpr int kMfmaMinTokens = INT_MAX;  // matrix-core tiles: not enabled in this build
+constexpr int kMfmaMinTokens = 16;  // experts with this many tokens use the matrix cores
+constexpr int kMaxBlocksPerSplit = 512;  // staging limit of the expert kernels (blocks)
+constexpr int kMaxSplitDown = 16;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct MoePlan {
   int T, H, I, E, k, TK, A;
-  int tiles_gu, tiles_dn, S_gu, S_dn, nt;
+  int tiles_gu, tiles_dn, S_gu, S_dn;
   size_t o_err, o_fx, o_nact, o_actexp, o_actoff, o_slots, o_nvalid, o_ids, o_wts, o_cnt, o_h,
       o_pgu, o_pdn, total;
   int n_cnt_gu, n_cnt_dn;
+  bool ok;  // partial buffers addressable with 32-bit byte offsets
 };
 
 int pick_split(int units, int nblk) {
@@ -47,18 +51,40 @@ bool moe_sizes_ok(int T, int H, int I, int E, int k) {
   return true;
 }
 
+// Expected number of distinct experts when T tokens each pick k of E uniformly: sizes the
+// K splits so that the active tiles fill the GPU (only performance depends on it).
+int expected_active(int T, int E, int k) {
+  const double miss = std::pow(1.0 - (double)k / E, (double)T);
+  return std::max(1, std::min(std::min(E, T * k), (int)std::lround(E * (1.0 - miss))));
+}
+
+// K splits of an expert kernel: enough workgroups for `units` tiles, at least 4 blocks of
+// 16 byte rows per workgroup, at most kMaxBlocksPerSplit blocks per split.
+int pick_ex_split(int units, int nblk, int max_split) {
+  int S = (kTargetWG + units - 1) / units;
+  S = std::min(S, std::max(1, nblk / 4));
+  S = std::min(S, max_split);
+  S = std::max(S, (nblk + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit);
+  return std::max(1, S);
+}
+
 MoePlan plan_moe(int T, int H, int I, int E, int k) {
   MoePlan p{};
   p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
   p.TK = T * k;
   p.A = std::min(E, p.TK);
-  p.tiles_gu = I / 64;
-  p.tiles_dn = H / 64;
-  p.S_gu = pick_split(p.A * p.tiles_gu, H / 32);
-  p.S_dn = pick_split(p.A * p.tiles_dn, I / 32);
-  p.nt = (T == 1) ? 1 : (T == 2 ? 2 : 4);
+  p.tiles_gu = (I + 127) / 128;
+  p.tiles_dn = (H + 127) / 128;
+  const int a_est = expected_active(T, E, k);
+  p.S_gu = pick_ex_split(a_est * p.tiles_gu, H / 32, dqg::ex_max_split());
+  p.S_dn = pick_ex_split(a_est * p.tiles_dn, I / 32, kMaxSplitDown);
   p.n_cnt_gu = p.A * p.tiles_gu;
   p.n_cnt_dn = T * p.tiles_dn;
+  const size_t pgu = p.S_gu > 1 ? sizeof(float) * (size_t)p.S_gu * p.TK * 2 * I : 0;
+  const size_t pdn = sizeof(float) * (size_t)p.S_dn * p.TK * H;
+  p.ok = pgu < (1ull << 31) && pdn < (1ull << 31) &&
+         (H / 32 + p.S_gu - 1) / p.S_gu <= kMaxBlocksPerSplit &&
+         (I / 32 + p.S_dn - 1) / p.S_dn <= kMaxBlocksPerSplit;
   size_t o = 0;
   p.o_err = o;     o += 256;
   // the single-launch T=1 region sits at the same offset for every T, so a workspace
@@ -73,8 +99,8 @@ MoePlan plan_moe(int T, int H, int I, int E, int k) {
   p.o_wts = o;     o = up256(o + sizeof(float) * p.TK);
   p.o_cnt = o;     o = up256(o + sizeof(unsigned) * (p.n_cnt_gu + p.n_cnt_dn));
   p.o_h = o;       o = up256(o + sizeof(float) * (size_t)p.TK * I);
-  p.o_pgu = o;     o = up256(o + (p.S_gu > 1 ? sizeof(float) * (size_t)p.S_gu * p.TK * 2 * I : 0));
-  p.o_pdn = o;     o = up256(o + sizeof(float) * (size_t)p.S_dn * p.TK * H);
+  p.o_pgu = o;     o = up256(o + pgu);
+  p.o_pdn = o;     o = up256(o + pdn);
   p.total = o;
   return p;
 }
@@ -94,6 +120,7 @@ int check_moe_common(const uint16_t* x, int T, int H, int I, int E, int k, const
   if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
   if (!moe_sizes_ok(T, H, I, E, k)) return DQG_ERR_UNSUPPORTED;
   if (H % group || I % group) return DQG_ERR_UNSUPPORTED;
+  if (!plan_moe(T, H, I, E, k).ok) return DQG_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(wgu) || !aligned16(sgu) || !aligned16(wd) || !aligned16(sd) ||
       !aligned16(out) || (res && !aligned16(res)))
     return DQG_ERR_MISALIGNED;
@@ -136,6 +163,12 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
   return a;
 }
 
+// matrix-core tile height of the expert kernels: none when no expert can reach mfma_min
+int mfma_tiles(const MoeArgs& a) {
+  if (a.mfma_min > a.T) return 0;
+  return a.T <= 16 ? 1 : 2;
+}
+
 bool use_fused(int T, int H, int I, int E, int k, int format) {
   return T == 1 && E <= 512 && dqg::fused_supported(H, I, k) && !(format & DQG_PATH_NO_FUSED);
 }
@@ -158,7 +191,7 @@ int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const ui
 int run_moe(MoeArgs& a, const MoePlan& p, const float* logits, hipStream_t st) {
   hipError_t e = dqg::launch_schedule(a, logits, st);
   if (e != hipSuccess) return DQG_ERR_HIP;
-  e = dqg::launch_moe_valu(a, p.A, p.nt, st);
+  e = dqg::launch_moe_experts(a, p.A, mfma_tiles(a), st);
   if (e != hipSuccess) return DQG_ERR_HIP;
   return DQG_OK;
 }
@@ -221,7 +254,8 @@ int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* we
 
 size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k) {
   if (!moe_sizes_ok(T, H, I, E, k)) return 0;
-  return plan_moe(T, H, I, E, k).total;
+  const MoePlan p = plan_moe(T, H, I, E, k);
+  return p.ok ? p.total : 0;
 }
 
 int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int32_t* ids,

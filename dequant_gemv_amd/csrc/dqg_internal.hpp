@@ -18,8 +18,8 @@ struct MoeWs {
   float* wts;           // [T*k]
   unsigned* cnt;        // all counters (n_cnt of them), zeroed by the schedule kernel
   int n_cnt;
-  unsigned* cnt_gu;     // [A * I/64]   gate_up split completion counters
-  unsigned* cnt_dn;     // [T * H/64]   down/combine completion counters
+  unsigned* cnt_gu;     // [A * ceil(I/128)]   gate_up split completion counters
+  unsigned* cnt_dn;     // [T * ceil(H/128)]   down/combine completion counters
   unsigned* cnt_fx;     // [fused-layer counters]
   float* h;             // [T*k, I]     SiLU(gate) * up
   float* part_gu;       // [S_gu, T*k, 2I] gate/up split partials
@@ -82,7 +82,10 @@ hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
                        hipStream_t st);
 hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st);
-hipError_t launch_moe_valu(const MoeArgs& a, int A, int nt, hipStream_t st);
+// gate_up + down expert kernels; mt = 0: vector-ALU tiles only, 1 or 2: matrix-core tiles
+// of 16 mt tokens for experts with at least mfma_min tokens
+hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st);
+int ex_max_split();
 hipError_t launch_gemv(const GemvArgs& g, int nt, hipStream_t st);
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st);

@@ -1,6 +1,7 @@
-// HIP kernels for gfx950: top-k routing, the device-built expert schedule, the packed
-// 4-bit MoE expert FFN (fused gate_up + SiLU*up, down + top-k combine) and the dense
-// packed INT4 GEMV.  Host launchers at the bottom; the C ABI lives in dqg_api.cpp.
+// HIP kernels for gfx950: top-k routing, the device-built expert schedule and the dense
+// packed INT4 GEMV.  The expert kernels of the multi-launch MoE path are in
+// dqg_experts.hip, the single-launch T = 1 layer in dqg_fused.hip.  Host launchers at the
+// bottom; the C ABI lives in dqg_api.cpp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -152,191 +153,6 @@ __device__ __forceinline__ void colsum_tokens(const float (&acc)[NT][16], float*
 }
 
 // =====================================================================================
-// gate_up + SwiGLU (vector-ALU tiles)
-// =====================================================================================
-// Grid: x = 64-wide h tile, y = K split, z = active-expert index.  A workgroup owns h
-// columns [n0, n0+64): 64 gate columns and the matching 64 up columns (lanes 0-3 and 4-7
-// of each row), 32 row-lanes walk the K blocks of its split.  Every token routed to the
-// expert is processed (NT at a time), so each weight byte is read once per call.
-constexpr int GU_THREADS = 256, GU_CPR = 8, GU_RL = GU_THREADS / GU_CPR, GU_WAVES = 4;
-
-template <int FMT, int NT>
-__global__ void __launch_bounds__(GU_THREADS) gateup_kernel(MoeArgs a) {
-  constexpr int XM = (FMT == FMT_FP4) ? X_BF16 : X_F16;
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int act = blockIdx.z;
-  if (act >= *a.ws.n_active) return;
-  const int beg = a.ws.act_off[act];
-  const int cnt = a.ws.act_off[act + 1] - beg;
-  if (cnt >= a.mfma_min) return;  // matrix-core tiles own this expert
-  const int e = a.ws.act_expert[act];
-  const int H = a.H, I = a.I, k = a.k, TK = a.T * k;
-  const int Kp = H / 2, nblk = H / 32;
-  const int tid = threadIdx.x, rl = tid / GU_CPR, ch = tid % GU_CPR;
-  const int n0 = blockIdx.x * 64;
-  const int col0 = (ch < 4) ? (n0 + 16 * ch) : (I + n0 + 16 * (ch - 4));
-  const int S = gridDim.y, s = blockIdx.y;
-  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
-  const size_t ld = 2 * (size_t)I;
-  const uint8_t* w = a.wgu + (size_t)e * Kp * ld;
-  const uint16_t* sc = a.sgu + (size_t)e * (H / a.group) * ld;
-
-  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);                   // [NT][Kp]
-  float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
-  float* red = corr + NT * nblk;                                      // [GU_THREADS * 16]
-  float* tot = red + GU_THREADS * 16;                                 // [NT][128]
-  __shared__ int s_flag;
-
-  for (int c0 = 0; c0 < cnt; c0 += NT) {
-    const uint16_t* src[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      src[t] = (c0 + t < cnt) ? a.x + (size_t)(a.ws.slot_list[beg + c0 + t] / k) * H : nullptr;
-    __syncthreads();
-    stage_bf16_rows<XM, FMT, NT>(src, Kp, xl, corr, GU_THREADS, tid);
-    __syncthreads();
-    float acc[NT][16];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
-    tile_rows<FMT, XM, NT>(w, sc, (int)ld, a.group, col0, b0 + rl, b1, GU_RL, xl, Kp, corr, nblk,
-                           acc);
-    colsum_tokens<GU_CPR, GU_THREADS, NT>(acc, red, tot, tid);
-    // thread (t, n): gate column n and up column n of the tile
-    for (int i = tid; i < NT * 64; i += GU_THREADS) {
-      const int t = i / 64, n = i % 64;
-      if (c0 + t >= cnt) continue;
-      const float g = tot[t * 128 + n], u = tot[t * 128 + 64 + n];
-      const int slot = a.ws.slot_list[beg + c0 + t];
-      if (S == 1) {
-        a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
-      } else {
-        float* p = a.ws.part_gu + ((size_t)s * TK + slot) * ld;
-        st_sc1(p, n0 + n, g);
-        st_sc1(p, I + n0 + n, u);
-      }
-    }
-  }
-  if (S == 1) return;
-  unsigned* counter = a.ws.cnt_gu + (size_t)act * gridDim.x + blockIdx.x;
-  if (!last_arriver(counter, (unsigned)S, &s_flag)) return;
-  for (int i = tid; i < cnt * 64; i += GU_THREADS) {
-    const int t = i / 64, n = i % 64;
-    const int slot = a.ws.slot_list[beg + t];
-    float g = 0.0f, u = 0.0f;
-    for (int q = 0; q < S; ++q) {
-      const float* p = a.ws.part_gu + ((size_t)q * TK + slot) * ld;
-      g += ld_sc1(p, n0 + n);
-      u += ld_sc1(p, I + n0 + n);
-    }
-    a.ws.h[(size_t)slot * I + n0 + n] = g / (1.0f + expf(-g)) * u;
-  }
-  if (tid == 0) st_cnt(counter, 0u);
-}
-
-// =====================================================================================
-// down projection + top-k combine (vector-ALU tiles)
-// =====================================================================================
-// Grid: x = 64-wide output tile of H, y = K split over I, z = active-expert index.
-// 4 lanes per byte row (64 columns), 64 row-lanes.  Partial y of every (split, slot) goes
-// to the workspace; the workgroup that completes a (token, tile) sums the k slots in
-// ascending j order (and the splits in ascending order), adds the residual and writes out.
-constexpr int DN_THREADS = 256, DN_CPR = 4, DN_RL = DN_THREADS / DN_CPR, DN_WAVES = 4;
-
-__device__ void combine_tile(const MoeArgs& a, int t, int tile, int tid, int S) {
-  const int H = a.H, k = a.k, TK = a.T * a.k;
-  for (int i = tid; i < 64; i += blockDim.x) {
-    const int m = tile * 64 + i;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int slot = t * k + j;
-      const int e = a.ids[slot];
-      if (e < 0 || e >= a.E) continue;
-      float y = 0.0f;
-      for (int q = 0; q < S; ++q) y += ld_sc1(a.ws.part_dn, ((size_t)q * TK + slot) * H + m);
-      acc = fmaf(a.wts[slot], y, acc);
-    }
-    if (a.res) acc += bf16_to_f32(a.res[(size_t)t * H + m]);
-    a.out[(size_t)t * H + m] = f32_to_bf16(acc);
-  }
-}
-
-template <int FMT, int NT>
-__global__ void __launch_bounds__(DN_THREADS) down_kernel(MoeArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int act = blockIdx.z;
-  if (act >= *a.ws.n_active) return;
-  const int beg = a.ws.act_off[act];
-  const int cnt = a.ws.act_off[act + 1] - beg;
-  if (cnt >= a.mfma_min) return;
-  const int e = a.ws.act_expert[act];
-  const int H = a.H, I = a.I, k = a.k, TK = a.T * k;
-  const int Kp = I / 2, nblk = I / 32;
-  const int tid = threadIdx.x, rl = tid / DN_CPR, ch = tid % DN_CPR;
-  const int tile = blockIdx.x;
-  const int col0 = tile * 64 + 16 * ch;
-  const int S = gridDim.y, s = blockIdx.y;
-  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
-  const uint8_t* w = a.wd + (size_t)e * Kp * H;
-  const uint16_t* sc = a.sd + (size_t)e * (I / a.group) * H;
-
-  float2* xl = reinterpret_cast<float2*>(smem);                       // [NT][Kp]
-  float* corr = reinterpret_cast<float*>(xl + NT * Kp);               // [NT][nblk]
-  float* red = corr + NT * nblk;                                      // [DN_THREADS * 16]
-  float* tot = red + DN_THREADS * 16;                                 // [NT][64]
-  __shared__ int s_last[NT];
-
-  for (int c0 = 0; c0 < cnt; c0 += NT) {
-    const float* src[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      src[t] = (c0 + t < cnt) ? a.ws.h + (size_t)a.ws.slot_list[beg + c0 + t] * I : nullptr;
-    __syncthreads();
-    stage_f32_rows<FMT, NT>(src, Kp, xl, corr, DN_THREADS, tid);
-    __syncthreads();
-    float acc[NT][16];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
-    tile_rows<FMT, X_F32, NT>(w, sc, H, a.group, col0, b0 + rl, b1, DN_RL, xl, Kp, corr, nblk,
-                              acc);
-    colsum_tokens<DN_CPR, DN_THREADS, NT>(acc, red, tot, tid);
-    for (int i = tid; i < NT * 64; i += DN_THREADS) {
-      const int t = i / 64, c = i % 64;
-      if (c0 + t >= cnt) continue;
-      const float v = tot[t * 64 + c];
-      const int slot = a.ws.slot_list[beg + c0 + t];
-      st_sc1(a.ws.part_dn, ((size_t)s * TK + slot) * H + tile * 64 + c, v);
-    }
-    // count this (token, tile) contribution; the completing workgroup combines
-    wait_mem();
-    __syncthreads();
-    if (tid < NT) {
-      int last = 0;
-      if (c0 + tid < cnt) {
-        const int slot = a.ws.slot_list[beg + c0 + tid];
-        const int t = slot / k;
-        unsigned* counter = a.ws.cnt_dn + (size_t)t * gridDim.x + tile;
-        const unsigned expected = (unsigned)(a.ws.nvalid[t] * S);
-        last = (add_cnt(counter, 1u) + 1u == expected) ? 1 : 0;
-      }
-      s_last[tid] = last;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (!s_last[t]) continue;
-      const int slot = a.ws.slot_list[beg + c0 + t];
-      const int tok = slot / k;
-      combine_tile(a, tok, tile, tid, S);
-      if (tid == 0) st_cnt(a.ws.cnt_dn + (size_t)tok * gridDim.x + tile, 0u);
-    }
-  }
-}
-
-// =====================================================================================
 // dense packed INT4 GEMV
 // =====================================================================================
 constexpr int GV_THREADS = 256, GV_CPR = 4, GV_RL = GV_THREADS / GV_CPR, GV_WAVES = 4;
@@ -451,44 +267,6 @@ hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st
   const size_t sm = (size_t)(3 * a.E + 2 * SCHED_THREADS + 4) * sizeof(int);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), sm, st, a, logits);
   return hipGetLastError();
-}
-
-template <int FMT, int NT>
-static hipError_t launch_gateup_t(const MoeArgs& a, int A, hipStream_t st) {
-  const int Kp = a.H / 2, nblk = a.H / 32;
-  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GU_THREADS * 16 * 4 +
-                    (size_t)NT * 128 * 4;
-  hipLaunchKernelGGL((gateup_kernel<FMT, NT>), dim3(a.I / 64, a.S_gu, A), dim3(GU_THREADS), sm, st,
-                     a);
-  return hipGetLastError();
-}
-
-template <int FMT, int NT>
-static hipError_t launch_down_t(const MoeArgs& a, int A, hipStream_t st) {
-  const int Kp = a.I / 2, nblk = a.I / 32;
-  const size_t sm = (size_t)NT * Kp * 8 + (size_t)NT * nblk * 4 + (size_t)DN_THREADS * 16 * 4 +
-                    (size_t)NT * 64 * 4;
-  hipLaunchKernelGGL((down_kernel<FMT, NT>), dim3(a.H / 64, a.S_dn, A), dim3(DN_THREADS), sm, st,
-                     a);
-  return hipGetLastError();
-}
-
-hipError_t launch_moe_valu(const MoeArgs& a, int A, int nt, hipStream_t st) {
-  hipError_t e;
-#define DQG_MOE_CASE(F, N)                         \
-  if (a.fmt == F && nt == N) {                     \
-    e = launch_gateup_t<F, N>(a, A, st);           \
-    if (e != hipSuccess) return e;                 \
-    return launch_down_t<F, N>(a, A, st);          \
-  }
-  DQG_MOE_CASE(FMT_FP4, 1)
-  DQG_MOE_CASE(FMT_FP4, 2)
-  DQG_MOE_CASE(FMT_FP4, 4)
-  DQG_MOE_CASE(FMT_INT4, 1)
-  DQG_MOE_CASE(FMT_INT4, 2)
-  DQG_MOE_CASE(FMT_INT4, 4)
-#undef DQG_MOE_CASE
-  return hipErrorInvalidValue;
 }
 
 template <int NT>

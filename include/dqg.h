@@ -89,8 +89,13 @@ int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* we
  * Host only.  Returns 0 for invalid sizes.  The workspace holds a sticky int32 error
  * word at byte 0 (set to 1 when an expert id outside [0, E) was seen; the slot then
  * contributes zero), the device-built expert schedule, per-tile counters and fp32
- * partial sums.  It needs no initialization; its contents are undefined after a call,
- * except the error word, which only the caller clears.
+ * partial sums.  Zero-fill it once before its first use; every call leaves it ready for
+ * the next call with the same (H, I, E, k) and any T.  The single-launch T = 1 layer
+ * keeps a completed-tile counter and double-buffered exchange rows in it, so a workspace
+ * must not be shared by calls that may run at the same time, and one that was used for
+ * other sizes must be zero-filled again.  Bit 1 of the error word is set when a wait of
+ * the single-launch layer gave up (its output is then not valid).  Only the caller
+ * clears the error word.
  */
 size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
 

@@ -227,3 +227,86 @@ def test_w512_stack_chained_residual(T, n_layers):
     got = bits16(bufs[n_layers % 2])
     _, want = O.moe_stack(layers[0].x, layers, cfg.k, cfg.group, cfg.fmt)
     check_chain(got, want, n_layers, what=f"stack T={T}")
+
+
+# ---- multi-launch expert kernels: vector-ALU and matrix-core bodies -------------------------
+PATH_CASES = [
+    ("q30_t16", S.Q30_BATCH.with_T(16), 0),
+    ("q30_t64", S.Q30_BATCH.with_T(64), 0),
+    ("tiny_t20", S.TINY.with_T(20), 0),
+    ("w512_t8", S.replace(S.W512, layers=1, T=8), 1),
+]
+
+
+@pytest.mark.parametrize("name,cfg,seed", PATH_CASES, ids=[c[0] for c in PATH_CASES])
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_moe_forced_paths_match_oracle(name, cfg, seed, path):
+    """Every expert through the vector-ALU tiles, then every expert through the MFMA tiles
+    (whatever its token count): both meet the tolerance on the same inputs."""
+    B = _b()
+    L, D = _layer(cfg, seed)
+    want, oids, _ = _oracle_layer(cfg, L)
+    flags = B.PATH_FORCE_GEMV if path == "gemv" else B.PATH_FORCE_MFMA
+    out, ids, _ = _run_layer(cfg, L, D, flags=flags)
+    assert np.array_equal(ids, oids)
+    check_bf16(out, want, what=f"{name} {path}")
+
+
+def _hot_layer(cfg, seed, hot=5, boost=12.0):
+    """A layer whose logits favour expert `hot` for every token (it gets all T tokens)."""
+    L, D = _layer(cfg, seed)
+    L.logits = L.logits.copy()
+    L.logits[:, hot] += np.float32(boost)
+    return L, D
+
+
+@pytest.mark.parametrize("T", [16, 40, 64])
+def test_moe_hot_expert_uses_mfma_tiles(T):
+    """One expert with T >= 16 tokens takes the MFMA tiles by default (chunks of 32 tokens
+    at T = 40, 64); the other experts stay on the vector-ALU tiles."""
+    cfg = S.Q30_BATCH.with_T(T)
+    L, D = _hot_layer(cfg, seed=T)
+    want, oids, _ = _oracle_layer(cfg, L)
+    assert np.all(oids[:, 0] == 5)
+    for fl in (0, _b().PATH_FORCE_GEMV):
+        out, ids, _ = _run_layer(cfg, L, D, flags=fl)
+        assert np.array_equal(ids, oids)
+        check_bf16(out, want, what=f"hot T={T} flags={fl}")
+
+
+ODD = S.MoEConfig("odd", T=5, E=8, H=320, I=192, k=2, fmt=S.FMT_FP4, group=32,
+                  scale_lo=0.005, scale_hi=0.02)
+
+
+@pytest.mark.parametrize("fmt", [S.FMT_FP4, S.FMT_INT4])
+@pytest.mark.parametrize("path", ["auto", "gemv", "mfma"])
+def test_moe_tiles_with_64_column_tails(fmt, path):
+    """H = 320 and I = 192 are multiples of 64 but not of 128: the last column tile of
+    each projection is half full."""
+    B = _b()
+    cfg = S.replace(ODD, fmt=fmt)
+    L, D = _layer(cfg, seed=4)
+    want, _, _ = _oracle_layer(cfg, L)
+    flags = {"auto": 0, "gemv": B.PATH_FORCE_GEMV, "mfma": B.PATH_FORCE_MFMA}[path]
+    out, _, _ = _run_layer(cfg, L, D, flags=flags)
+    check_bf16(out, want, what=f"odd fmt={fmt} {path}")
+
+
+@pytest.mark.parametrize("path", ["gemv", "mfma"])
+def test_moe_group_128(path):
+    """Scale groups of 128 K indices (4 blocks share a scale row)."""
+    B = _b()
+    cfg = S.replace(S.Q30_BATCH.with_T(6), group=128)
+    L, D = _layer(cfg, seed=9)
+    want, _, _ = _oracle_layer(cfg, L)
+    flags = B.PATH_FORCE_GEMV if path == "gemv" else B.PATH_FORCE_MFMA
+    out, _, _ = _run_layer(cfg, L, D, flags=flags)
+    check_bf16(out, want, what=f"G=128 {path}")
+
+
+def test_moe_mfma_deterministic():
+    cfg = S.Q30_BATCH.with_T(64)
+    L, D = _hot_layer(cfg, seed=2)
+    o1, _, _ = _run_layer(cfg, L, D)
+    o2, _, _ = _run_layer(cfg, L, D)
+    assert np.array_equal(o1, o2)
