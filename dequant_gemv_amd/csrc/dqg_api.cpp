@@ -18,29 +18,23 @@ using dqg::MoeArgs;
 constexpr int kMaxE = 4096;
 constexpr int kMaxK = 32;
 constexpr int kMaxTK = 65536;
-constexpr int kTargetWG = 512;   // workgroups per launch to aim for (2 per CU)
-constexpr int kMinBlocksPerWG = 8;
 constexpr int kMfmaMinTokens = 16;  // experts with this many tokens use the matrix cores
-constexpr int kMaxBlocksPerSplit = 512;  // staging limit of the expert kernels (blocks)
 constexpr int kMaxSplitDown = 16;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Workspace of the multi-launch path.  Its layout depends only on (H, I, E, k) and the
+// workspace's capacity t_cap (the largest T whose layout fits the caller's bytes), so calls
+// with any T <= t_cap on one workspace find every region at the same place.  The split
+// partials are kept zero between calls (their readers clear them).
 struct MoePlan {
   int T, H, I, E, k, TK, A;
   int tiles_gu, tiles_dn, S_gu, S_dn;
-  size_t o_err, o_fx, o_nact, o_actexp, o_actoff, o_slots, o_nvalid, o_ids, o_wts, o_cnt, o_h,
-      o_pgu, o_pdn, total;
-  int n_cnt_gu, n_cnt_dn;
+  int t_cap, sgu_max, sdn_max;
+  size_t o_err, o_fx, o_nact, o_rec, o_slots, o_nvalid, o_ids, o_wts, o_h, o_pgu, o_pdn, total;
   bool ok;  // partial buffers addressable with 32-bit byte offsets
 };
-
-int pick_split(int units, int nblk) {
-  int S = (kTargetWG + units - 1) / units;
-  S = std::min(S, std::max(1, nblk / kMinBlocksPerWG));
-  return std::max(1, S);
-}
 
 bool moe_sizes_ok(int T, int H, int I, int E, int k) {
   if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1) return false;
@@ -58,50 +52,72 @@ int expected_active(int T, int E, int k) {
   return std::max(1, std::min(std::min(E, T * k), (int)std::lround(E * (1.0 - miss))));
 }
 
-// K splits of an expert kernel: enough workgroups for `units` tiles, at least 4 blocks of
-// 16 byte rows per workgroup, at most kMaxBlocksPerSplit blocks per split.
-int pick_ex_split(int units, int nblk, int max_split) {
-  int S = (kTargetWG + units - 1) / units;
-  S = std::min(S, std::max(1, nblk / 4));
-  S = std::min(S, max_split);
-  S = std::max(S, (nblk + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit);
-  return std::max(1, S);
+// K splits of a streaming kernel: one batch of `per_wg` blocks (16 byte rows each) per
+// workgroup when possible -- many small workgroups keep the most bytes in flight -- but
+// at most `max_split`, and few enough that the fp32 split partials (partial_bytes per
+// split) stay under 15% of the weight bytes the kernel streams.
+int pick_ex_split(int nblk, int per_wg, int max_split, double weight_bytes,
+                  double partial_bytes) {
+  int S = (nblk + per_wg - 1) / per_wg;
+  const double budget = 0.15 * weight_bytes / std::max(partial_bytes, 1.0);
+  S = std::min(S, std::max(1, (int)budget));
+  return std::max(1, std::min(S, max_split));
 }
 
-MoePlan plan_moe(int T, int H, int I, int E, int k) {
+// maximum K splits of the two expert kernels for a workspace of capacity t_cap (bounded
+// so that the partials stay addressable with 32-bit byte offsets)
+int moe_split_max(int nblk, int per_wg, int cap, long long tk_cap, long long row_bytes) {
+  const long long fit = ((1LL << 31) - 1) / std::max(1LL, tk_cap * row_bytes);
+  return (int)std::max(1LL, std::min<long long>(std::min((nblk + per_wg - 1) / per_wg, cap), fit));
+}
+
+void moe_layout(MoePlan& p, int t_cap) {
+  const int H = p.H, I = p.I, k = p.k;
+  const long long tkc = (long long)t_cap * k;
+  const int a_cap = (int)std::min<long long>(p.E, tkc);
+  p.t_cap = t_cap;
+  p.sgu_max = moe_split_max(H / 32, 4, dqg::ex_max_split(), tkc, 8LL * I);
+  p.sdn_max = moe_split_max(I / 32, 8, kMaxSplitDown, tkc, 4LL * H);
+  size_t o = 0;
+  p.o_err = o;     o += 256;
+  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, k) : 0));
+  p.o_nact = o;    o += 256;
+  p.o_rec = o;     o = up256(o + 16 * (size_t)a_cap);
+  p.o_slots = o;   o = up256(o + sizeof(int) * tkc);
+  p.o_nvalid = o;  o = up256(o + sizeof(int) * (size_t)t_cap);
+  p.o_ids = o;     o = up256(o + sizeof(int) * tkc);
+  p.o_wts = o;     o = up256(o + sizeof(float) * tkc);
+  p.o_h = o;       o = up256(o + sizeof(uint16_t) * (size_t)tkc * I);
+  p.o_pgu = o;     o = up256(o + sizeof(float) * (size_t)p.sgu_max * tkc * 2 * I);
+  p.o_pdn = o;     o = up256(o + sizeof(float) * (size_t)p.sdn_max * tkc * H);
+  p.total = o;
+}
+
+// Plan of a call with T tokens on a workspace of ws_bytes (0: the size query for T).
+MoePlan plan_moe(int T, int H, int I, int E, int k, size_t ws_bytes = 0) {
   MoePlan p{};
   p.T = T; p.H = H; p.I = I; p.E = E; p.k = k;
   p.TK = T * k;
   p.A = std::min(E, p.TK);
   p.tiles_gu = (I + 127) / 128;
   p.tiles_dn = (H + 127) / 128;
+  moe_layout(p, T);
+  p.ok = true;
+  if (ws_bytes > p.total) {  // the largest capacity that fits the caller's workspace
+    int lo = T, hi = kMaxTK / k;
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      MoePlan q = p;
+      moe_layout(q, mid);
+      if (q.total <= ws_bytes) lo = mid; else hi = mid - 1;
+    }
+    moe_layout(p, lo);
+  }
   const int a_est = expected_active(T, E, k);
-  p.S_gu = pick_ex_split(a_est * p.tiles_gu, H / 32, dqg::ex_max_split());
-  p.S_dn = pick_ex_split(a_est * p.tiles_dn, I / 32, kMaxSplitDown);
-  p.n_cnt_gu = p.A * p.tiles_gu;
-  p.n_cnt_dn = T * p.tiles_dn;
-  const size_t pgu = p.S_gu > 1 ? sizeof(float) * (size_t)p.S_gu * p.TK * 2 * I : 0;
-  const size_t pdn = sizeof(float) * (size_t)p.S_dn * p.TK * H;
-  p.ok = pgu < (1ull << 31) && pdn < (1ull << 31) &&
-         (H / 32 + p.S_gu - 1) / p.S_gu <= kMaxBlocksPerSplit &&
-         (I / 32 + p.S_dn - 1) / p.S_dn <= kMaxBlocksPerSplit;
-  size_t o = 0;
-  p.o_err = o;     o += 256;
-  // the single-launch T=1 region sits at the same offset for every T, so a workspace
-  // keeps its self-resetting counters valid when calls with other T values reuse it
-  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, k) : 0));
-  p.o_nact = o;    o += 256;
-  p.o_actexp = o;  o = up256(o + sizeof(int) * p.A);
-  p.o_actoff = o;  o = up256(o + sizeof(int) * (p.A + 1));
-  p.o_slots = o;   o = up256(o + sizeof(int) * p.TK);
-  p.o_nvalid = o;  o = up256(o + sizeof(int) * T);
-  p.o_ids = o;     o = up256(o + sizeof(int) * p.TK);
-  p.o_wts = o;     o = up256(o + sizeof(float) * p.TK);
-  p.o_cnt = o;     o = up256(o + sizeof(unsigned) * (p.n_cnt_gu + p.n_cnt_dn));
-  p.o_h = o;       o = up256(o + sizeof(float) * (size_t)p.TK * I);
-  p.o_pgu = o;     o = up256(o + pgu);
-  p.o_pdn = o;     o = up256(o + pdn);
-  p.total = o;
+  const double gu_bytes = (double)a_est * H * I * 1.125, dn_bytes = gu_bytes / 2;
+  p.S_gu = std::min(pick_ex_split(H / 32, 4, dqg::ex_max_split(), gu_bytes, 8.0 * p.TK * I),
+                    p.sgu_max);
+  p.S_dn = std::min(pick_ex_split(I / 32, 8, kMaxSplitDown, dn_bytes, 4.0 * p.TK * H), p.sdn_max);
   return p;
 }
 
@@ -120,7 +136,6 @@ int check_moe_common(const uint16_t* x, int T, int H, int I, int E, int k, const
   if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
   if (!moe_sizes_ok(T, H, I, E, k)) return DQG_ERR_UNSUPPORTED;
   if (H % group || I % group) return DQG_ERR_UNSUPPORTED;
-  if (!plan_moe(T, H, I, E, k).ok) return DQG_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(wgu) || !aligned16(sgu) || !aligned16(wd) || !aligned16(sd) ||
       !aligned16(out) || (res && !aligned16(res)))
     return DQG_ERR_MISALIGNED;
@@ -140,20 +155,15 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
   a.wgu = wgu; a.sgu = sgu; a.wd = wd; a.sd = sd; a.res = res; a.out = out;
   a.ws.err = reinterpret_cast<int*>(b + p.o_err);
   a.ws.n_active = reinterpret_cast<int*>(b + p.o_nact);
-  a.ws.act_expert = reinterpret_cast<int*>(b + p.o_actexp);
-  a.ws.act_off = reinterpret_cast<int*>(b + p.o_actoff);
+  a.ws.rec = reinterpret_cast<int4*>(b + p.o_rec);
   a.ws.slot_list = reinterpret_cast<int*>(b + p.o_slots);
   a.ws.nvalid = reinterpret_cast<int*>(b + p.o_nvalid);
   a.ws.ids = reinterpret_cast<int32_t*>(b + p.o_ids);
   a.ws.wts = reinterpret_cast<float*>(b + p.o_wts);
-  a.ws.cnt = reinterpret_cast<unsigned*>(b + p.o_cnt);
-  a.ws.n_cnt = p.n_cnt_gu + p.n_cnt_dn;
-  a.ws.cnt_gu = a.ws.cnt;
-  a.ws.cnt_dn = a.ws.cnt + p.n_cnt_gu;
-  a.ws.cnt_fx = nullptr;
-  a.ws.h = reinterpret_cast<float*>(b + p.o_h);
+  a.ws.hop = reinterpret_cast<uint16_t*>(b + p.o_h);
   a.ws.part_gu = reinterpret_cast<float*>(b + p.o_pgu);
   a.ws.part_dn = reinterpret_cast<float*>(b + p.o_pdn);
+  a.ws.tk_cap = p.t_cap * p.k;
   a.S_gu = p.S_gu;
   a.S_dn = p.S_dn;
   const int flags = format & ~0xFF;
@@ -196,21 +206,40 @@ int run_moe(MoeArgs& a, const MoePlan& p, const float* logits, hipStream_t st) {
   return DQG_OK;
 }
 
+// GEMV workspace: split partials [S_max][t_cap][N], zero between calls (the finishing
+// workgroups clear them); t_cap = the largest T whose layout fits the caller's bytes.
 struct GemvPlan {
-  int tiles, S, nt;
-  size_t o_cnt, o_part, total;
+  int tiles, S, mt, t_cap, s_max;
+  size_t total;
 };
 
-GemvPlan plan_gemv(int T, int K, int N) {
+void gemv_layout(GemvPlan& g, int K, int N, int t_cap) {
+  g.t_cap = t_cap;
+  const long long fit = ((1LL << 31) - 1) / std::max(1LL, 4LL * t_cap * N);
+  g.s_max = (int)std::max(1LL, std::min<long long>(
+                                   std::min((K / 32 + 7) / 8, dqg::ex_max_split_gemv()), fit));
+  // [error word, 256 bytes][partials]
+  g.total = g.s_max > 1 ? 256 + up256(sizeof(float) * (size_t)g.s_max * t_cap * N) : 0;
+}
+
+GemvPlan plan_gemv(int T, int K, int N, size_t ws_bytes = 0) {
   GemvPlan g{};
-  g.tiles = N / 64;
-  g.S = pick_split(g.tiles, K / 32);
-  g.nt = (T == 1) ? 1 : (T == 2 ? 2 : 4);
-  if (g.S == 1) return g;
-  size_t o = 0;
-  g.o_cnt = o;  o = up256(o + sizeof(unsigned) * g.tiles);
-  g.o_part = o; o = up256(o + sizeof(float) * (size_t)g.S * T * N);
-  g.total = o;
+  g.tiles = (N + 127) / 128;
+  g.mt = (T < kMfmaMinTokens) ? 0 : (T <= 16 ? 1 : 2);
+  gemv_layout(g, K, N, T);
+  if (ws_bytes > g.total && g.total > 0) {
+    int lo = T, hi = 4096;
+    while (lo < hi) {
+      const int mid = lo + (hi - lo + 1) / 2;
+      GemvPlan q = g;
+      gemv_layout(q, K, N, mid);
+      if (q.total <= ws_bytes) lo = mid; else hi = mid - 1;
+    }
+    gemv_layout(g, K, N, lo);
+  }
+  g.S = std::min(pick_ex_split(K / 32, 8, dqg::ex_max_split_gemv(), (double)K / 2 * N * 1.06,
+                               4.0 * T * N),
+                 g.s_max);
   return g;
 }
 
@@ -218,8 +247,10 @@ bool gemv_sizes_ok(int T, int K, int N, int group) {
   if (T < 1 || K < 2 || N < 1) return false;
   if (group != 32 && group != 128) return false;
   if (K % group || N % 64) return false;
-  if (T > 4096 || (long long)K * N > (1LL << 40)) return false;
-  if (K > 65536) return false;
+  if (T > 4096 || K > 65536) return false;
+  // buffer views: the packed matrix, its scales, x and the split partials must be
+  // addressable with 32-bit byte offsets
+  if ((long long)(K / 2) * N >= (1LL << 31) || (long long)T * K * 2 >= (1LL << 31)) return false;
   return true;
 }
 
@@ -268,7 +299,7 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
                             format, residual, out, workspace, workspace_bytes);
   if (rc != DQG_OK) return rc;
   if (((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u)) return DQG_ERR_MISALIGNED;
-  const MoePlan p = plan_moe(T, H, I, E, k);
+  const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
                             out, workspace);
   a.ids = ids;
@@ -287,7 +318,7 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   if (rc != DQG_OK) return rc;
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
-  const MoePlan p = plan_moe(T, H, I, E, k);
+  const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   if (use_fused(T, H, I, E, k, format))
     return run_fused(p, x, logits, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
                      out, ids_out, weights_out, workspace, stream);
@@ -312,20 +343,20 @@ int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
   if (T < 1 || K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
   if (!gemv_sizes_ok(T, K, N, group)) return DQG_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return DQG_ERR_MISALIGNED;
-  GemvPlan gp = plan_gemv(T, K, N);
+  GemvPlan gp = plan_gemv(T, K, N, workspace ? workspace_bytes : 0);
   if (gp.S > 1 && (!workspace || workspace_bytes < gp.total)) {
     if (workspace) return DQG_ERR_WORKSPACE;
-    gp.S = 1;  // no workspace: one workgroup per column tile
+    gp.S = 1;  // no workspace: no K split
   }
   if (workspace && !aligned16(workspace)) return DQG_ERR_MISALIGNED;
   GemvArgs g{};
   g.x = x; g.T = T; g.K = K; g.N = N; g.group = group; g.w = w; g.s = s; g.y = y; g.S = gp.S;
+  g.t_cap = gp.t_cap;
   if (gp.S > 1) {
-    char* b = static_cast<char*>(workspace);
-    g.cnt = reinterpret_cast<unsigned*>(b + gp.o_cnt);
-    g.part = reinterpret_cast<float*>(b + gp.o_part);
+    g.err = static_cast<int*>(workspace);
+    g.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
   }
-  return dqg::launch_gemv(g, gp.nt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+  return dqg::launch_gemv_ex(g, gp.mt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }
 
 int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,

@@ -10,20 +10,15 @@ namespace dqg {
 struct MoeWs {
   int* err;             // [1]  sticky error word (1: an expert id outside [0, E) was seen)
   int* n_active;        // [1]  number of distinct valid experts this call
-  int* act_expert;      // [A]  expert id of active index a (ascending ids)
-  int* act_off;         // [A+1] start of expert a's slots in slot_list
+  int4* rec;            // [A]  per active index: {expert, first slot position, slots, 0}
   int* slot_list;       // [T*k] slots (t*k + j) grouped by expert, ascending within an expert
   int* nvalid;          // [T]  number of valid slots of token t
   int32_t* ids;         // [T*k] routing written by the layer call when the caller passes none
   float* wts;           // [T*k]
-  unsigned* cnt;        // all counters (n_cnt of them), zeroed by the schedule kernel
-  int n_cnt;
-  unsigned* cnt_gu;     // [A * ceil(I/128)]   gate_up split completion counters
-  unsigned* cnt_dn;     // [T * ceil(H/128)]   down/combine completion counters
-  unsigned* cnt_fx;     // [fused-layer counters]
-  float* h;             // [T*k, I]     SiLU(gate) * up
-  float* part_gu;       // [S_gu, T*k, 2I] gate/up split partials
-  float* part_dn;       // [S_dn, T*k, H]  down partials per slot
+  uint16_t* hop;        // [T*k, I] SiLU(gate) * up as 16-bit operands (bf16 / fp16)
+  float* part_gu;       // [S_gu_max][tk_cap][2I] gate/up split partials (zero between calls)
+  float* part_dn;       // [S_dn_max][tk_cap][H]  down split partials per slot (zero between calls)
+  int tk_cap;           // slots of the workspace's capacity: the partials' split stride
 };
 
 struct MoeArgs {
@@ -42,6 +37,7 @@ struct MoeArgs {
   MoeWs ws;
   int S_gu, S_dn;
   int mfma_min;         // experts with at least this many tokens use the MFMA tiles
+  int combine;          // this down launch also runs the per-token combine (the last one)
 };
 
 struct GemvArgs {
@@ -50,9 +46,10 @@ struct GemvArgs {
   const uint8_t* w;
   const uint16_t* s;
   uint16_t* y;
-  float* part;          // [S, T, N] split partials (S > 1)
-  unsigned* cnt;        // [N/64] split completion counters (S > 1)
+  float* part;          // [S_max, t_cap, N] split partials (S > 1; zero between calls)
+  int t_cap;            // tokens of the workspace's capacity: the partials' split stride
   int S;
+  int* err;             // error word (bit 1: a wait gave up), may be null
 };
 
 // Single-launch T = 1 layer (routing + expert FFN + combine); see dqg_fused.hip.
@@ -86,7 +83,10 @@ hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st
 // of 16 mt tokens for experts with at least mfma_min tokens
 hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st);
 int ex_max_split();
-hipError_t launch_gemv(const GemvArgs& g, int nt, hipStream_t st);
+constexpr unsigned EX_SPIN_LIMIT = 1u << 16;  // polling rounds before a wait gives up
+// dense INT4 GEMV; mt = 0: vector-ALU tiles (T < 16), 1 or 2: matrix-core tiles
+hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st);
+int ex_max_split_gemv();
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st);
 

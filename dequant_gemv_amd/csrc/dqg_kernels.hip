@@ -1,6 +1,6 @@
-// HIP kernels for gfx950: top-k routing, the device-built expert schedule and the dense
-// packed INT4 GEMV.  The expert kernels of the multi-launch MoE path are in
-// dqg_experts.hip, the single-launch T = 1 layer in dqg_fused.hip.  Host launchers at the
+// HIP kernels for gfx950: top-k routing, the device-built expert schedule and the
+// dequantize test aid.  The expert kernels of the multi-launch MoE path and the dense GEMV
+// are in dqg_experts.hip, the single-launch T = 1 layer in dqg_fused.hip.  Host launchers at the
 // bottom; the C ABI lives in dqg_api.cpp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,67 +25,87 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 // =====================================================================================
 // schedule: (optional routing) + per-expert slot lists, one workgroup
 // =====================================================================================
+// Active experts in ascending id order get records {expert, first slot position, slot
+// count, 0} (records past the active count: all zero); the slot list holds, per active
+// expert, its slots t*k + j in ascending slot order.
 constexpr int SCHED_THREADS = 1024;
 
-// exclusive scan of n (<= 4 * SCHED_THREADS) ints in LDS, in place; returns the total
-__device__ int block_exclusive_scan(int* a, int n, int* tmp) {
-  const int tid = threadIdx.x;
-  const int per = (n + SCHED_THREADS - 1) / SCHED_THREADS;
-  const int b = tid * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) local += a[b + i];
-  tmp[tid] = local;
-  __syncthreads();
-  // Hillis-Steele over SCHED_THREADS partials
-  for (int off = 1; off < SCHED_THREADS; off <<= 1) {
-    const int v = (tid >= off) ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
-  }
-  int run = (tid > 0) ? tmp[tid - 1] : 0;
-  const int total = tmp[SCHED_THREADS - 1];
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) {
-      const int v = a[b + i];
-      a[b + i] = run;
-      run += v;
+constexpr int SCHED_LDS_IDS = 2048;  // slots whose ids are kept in LDS
+
+// exclusive prefix sums over experts of cnt (-> pos) by wave 0 (lane l takes experts
+// [l * per, l * per + per)); with `records`, active experts also get their records.
+// Returns the number of active experts in lane 63's s_nact.
+__device__ __forceinline__ void sched_scan(const MoeArgs& a, const int* cnt, int* pos, int E,
+                                           bool records, int* s_nact) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64, e0 = lane * per;
+  int c = 0, n = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      c += cnt[e];
+      n += cnt[e] > 0;
     }
-  __syncthreads();
-  return total;
+  }
+  int ci = c, ni = n;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int tc = __shfl_up(ci, off), tn = __shfl_up(ni, off);
+    if (lane >= off) {
+      ci += tc;
+      ni += tn;
+    }
+  }
+  int cx = ci - c, nx = ni - n;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      const int ce = cnt[e];
+      pos[e] = cx;
+      if (records && ce > 0) a.ws.rec[nx] = make_int4(e, cx, ce, 0);
+      cx += ce;
+      nx += ce > 0;
+    }
+  }
+  if (lane == 63) *s_nact = ni;
 }
 
 __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, const float* logits) {
   extern __shared__ int sm[];
   const int E = a.E, T = a.T, k = a.k, TK = T * k;
-  int* cnt = sm;                         // [E] slots per expert
-  int* aidx = cnt + E;                   // [E] active index of each expert
-  int* base = aidx + E;                  // [E] first slot position of each expert
-  int* tmp = base + E;                   // [SCHED_THREADS]
-  int* chunk_ids = tmp + SCHED_THREADS;  // [SCHED_THREADS]
-  int* s_flag = chunk_ids + SCHED_THREADS;
-  const int tid = threadIdx.x;
+  int* cnt = sm;                                   // [E] slots per expert
+  unsigned* mask = reinterpret_cast<unsigned*>(cnt + E);  // [E] token masks of a round
+  int* pos = cnt + 2 * E;                          // [E] next slot position
+  int* s_misc = pos + E;                           // invalid, n_active, duplicate, empty token
+  int* chunk_ids = s_misc + 4;                     // [SCHED_THREADS]
+  int* lids = chunk_ids + SCHED_THREADS;           // [SCHED_LDS_IDS] ids when TK fits
+  const bool in_lds = TK <= SCHED_LDS_IDS;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   if (logits) {  // routing from logits, one wave per token
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int t = wv; t < T; t += SCHED_THREADS / 64)
-      route_token(logits, t, E, k, lane, a.ids_w, a.wts_w);
-    __threadfence_block();
-    __syncthreads();
+    for (int t = wv; t < T; t += SCHED_THREADS / 64) {
+      int e;
+      float w;
+      route_row<4096>(logits + (size_t)t * E, E, k, lane, &e, &w);
+      if (lane < k) {
+        a.ids_w[(size_t)t * k + lane] = e;
+        a.wts_w[(size_t)t * k + lane] = w;
+        if (in_lds) lids[t * k + lane] = e;
+      }
+    }
+  } else if (in_lds) {
+    for (int i = tid; i < TK; i += SCHED_THREADS) lids[i] = a.ids[i];
   }
-  const int32_t* ids = a.ids;
-  // reset the cross-workgroup counters used by the expert kernels of this call
-  for (int i = tid; i < a.ws.n_cnt; i += SCHED_THREADS) a.ws.cnt[i] = 0u;
+  if (!in_lds) __threadfence_block();  // routing results are read back from memory
   for (int i = tid; i < E; i += SCHED_THREADS) cnt[i] = 0;
-  if (tid == 0) *s_flag = 0;
+  if (tid < 4) s_misc[tid] = 0;
   __syncthreads();
+  const int32_t* ids = in_lds ? lids : a.ids;
   for (int i = tid; i < TK; i += SCHED_THREADS) {
     const int e = ids[i];
     if (e >= 0 && e < E)
       atomicAdd(&cnt[e], 1);
     else
-      *s_flag = 1;
+      s_misc[0] = 1;
   }
   for (int t = tid; t < T; t += SCHED_THREADS) {
     int nv = 0;
@@ -94,47 +114,76 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
       nv += (e >= 0 && e < E);
     }
     a.ws.nvalid[t] = nv;
+    if (nv == 0) s_misc[3] = 1;
   }
   __syncthreads();
-  if (tid == 0 && *s_flag) atomicOr(a.ws.err, 1);
-  // active experts in ascending id order; slot offsets per expert
-  for (int i = tid; i < E; i += SCHED_THREADS) {
-    aidx[i] = cnt[i] > 0 ? 1 : 0;
-    base[i] = cnt[i];
-  }
+  if (tid == 0 && s_misc[0]) atomicOr(a.ws.err, 1);
+  if (wv == 0) sched_scan(a, cnt, pos, E, true, &s_misc[1]);
   __syncthreads();
-  const int n_active = block_exclusive_scan(aidx, E, tmp);
-  const int total = block_exclusive_scan(base, E, tmp);
-  for (int i = tid; i < E; i += SCHED_THREADS)
-    if (cnt[i] > 0) {
-      a.ws.act_expert[aidx[i]] = i;
-      a.ws.act_off[aidx[i]] = base[i];
-    }
-  if (tid == 0) {
-    *a.ws.n_active = n_active;
-    a.ws.act_off[n_active] = total;
-  }
-  __syncthreads();
-  // stable placement: slots of one expert keep ascending slot order
-  for (int c0 = 0; c0 < TK; c0 += SCHED_THREADS) {
-    const int i = c0 + tid;
-    const int e = (i < TK) ? ids[i] : -1;
-    chunk_ids[tid] = e;
+  const int n_active = s_misc[1];
+  const int A = min(E, TK);
+  if (tid == 0) *a.ws.n_active = n_active;
+  for (int i = n_active + tid; i < A; i += SCHED_THREADS) a.ws.rec[i] = make_int4(0, 0, 0, 0);
+  // stable placement, 32 tokens per round: a slot's rank within its expert is the number
+  // of the round's earlier tokens in the expert's token mask; pos[e] advances per round.
+  // A token that lists an expert twice shows up as a mask bit that is already set: then
+  // the placement is redone in chunks of SCHED_THREADS slots, rank = earlier equal ids.
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    for (int e = tid; e < E; e += SCHED_THREADS) mask[e] = 0u;
     __syncthreads();
-    if (e >= 0 && e < E) {
-      int rank = 0;
-      for (int q = 0; q < tid; ++q) rank += (chunk_ids[q] == e);
-      a.ws.slot_list[base[e] + rank] = i;
+    const int n_r = min(32, T - t0) * k;  // <= SCHED_THREADS
+    const int i = tid;
+    const int e = (i < n_r) ? ids[t0 * k + i] : -1;
+    const bool ok = e >= 0 && e < E;
+    if (ok && (atomicOr(&mask[e], 1u << (i / k)) & (1u << (i / k)))) s_misc[2] = 1;
+    __syncthreads();
+    if (ok) {
+      const int rank = __popc(mask[e] & ((1u << (i / k)) - 1u));
+      a.ws.slot_list[pos[e] + rank] = t0 * k + i;
     }
     __syncthreads();
-    if (e >= 0 && e < E) atomicAdd(&base[e], 1);
+    for (int x = tid; x < E; x += SCHED_THREADS) pos[x] += __popc(mask[x]);
     __syncthreads();
+    if (s_misc[2]) break;
+  }
+  if (s_misc[2]) {
+    if (wv == 0) sched_scan(a, cnt, pos, E, false, &s_misc[1]);
+    __syncthreads();
+    for (int c0 = 0; c0 < TK; c0 += SCHED_THREADS) {
+      const int i = c0 + tid;
+      const int e = (i < TK) ? ids[i] : -1;
+      chunk_ids[tid] = e;
+      __syncthreads();
+      if (e >= 0 && e < E) {
+        int rank = 0;
+        for (int q = 0; q < tid; ++q) rank += (chunk_ids[q] == e);
+        a.ws.slot_list[pos[e] + rank] = i;
+      }
+      __syncthreads();
+      if (e >= 0 && e < E) atomicAdd(&pos[e], 1);
+      __syncthreads();
+    }
+  }
+  // an invalid slot has no expert: its down partial rows are published as zeros, so that
+  // the combiners (which read every slot of a token) find them
+  if (s_misc[0]) {
+    const long long n = (long long)a.S_dn * TK * a.H;
+    for (long long idx = tid; idx < n; idx += SCHED_THREADS) {
+      const int m = (int)(idx % a.H);
+      const long long rest = idx / a.H;
+      const int slot = (int)(rest % TK), sp = (int)(rest / TK);
+      const int e = ids[slot];
+      if (e < 0 || e >= E)
+        a.ws.part_dn[((size_t)sp * a.ws.tk_cap + slot) * a.H + m] = __uint_as_float(0x80000000u);
+    }
   }
   // tokens with no valid slot: out = residual (or zero)
-  for (int t = 0; t < T; ++t) {
-    if (a.ws.nvalid[t] != 0) continue;
-    for (int m = tid; m < a.H; m += SCHED_THREADS)
-      a.out[(size_t)t * a.H + m] = a.res ? a.res[(size_t)t * a.H + m] : (uint16_t)0;
+  if (s_misc[3]) {
+    for (int t = 0; t < T; ++t) {
+      if (a.ws.nvalid[t] != 0) continue;
+      for (int m = tid; m < a.H; m += SCHED_THREADS)
+        a.out[(size_t)t * a.H + m] = a.res ? a.res[(size_t)t * a.H + m] : (uint16_t)0;
+    }
   }
 }
 
@@ -150,65 +199,6 @@ __device__ __forceinline__ void colsum_tokens(const float (&acc)[NT][16], float*
     if (tid < COLS) tot[t * COLS + tid] = v;
     __syncthreads();
   }
-}
-
-// =====================================================================================
-// dense packed INT4 GEMV
-// =====================================================================================
-constexpr int GV_THREADS = 256, GV_CPR = 4, GV_RL = GV_THREADS / GV_CPR, GV_WAVES = 4;
-
-template <int NT>
-__global__ void __launch_bounds__(GV_THREADS) gemv_kernel(GemvArgs g) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int K = g.K, N = g.N, T = g.T;
-  const int Kp = K / 2, nblk = K / 32;
-  const int tid = threadIdx.x, rl = tid / GV_CPR, ch = tid % GV_CPR;
-  const int tile = blockIdx.x;
-  const int col0 = tile * 64 + 16 * ch;
-  const int S = gridDim.y, s = blockIdx.y;
-  const int b0 = (s * nblk) / S, b1 = ((s + 1) * nblk) / S;
-  uint32_t* xl = reinterpret_cast<uint32_t*>(smem);
-  float* corr = reinterpret_cast<float*>(xl + NT * Kp);
-  float* red = corr + NT * nblk;                                      // [GV_THREADS * 16]
-  float* tot = red + GV_THREADS * 16;                                 // [NT][64]
-  __shared__ int s_flag;
-
-  for (int c0 = 0; c0 < T; c0 += NT) {
-    const uint16_t* src[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) src[t] = (c0 + t < T) ? g.x + (size_t)(c0 + t) * K : nullptr;
-    __syncthreads();
-    stage_bf16_rows<X_F16, FMT_INT4, NT>(src, Kp, xl, corr, GV_THREADS, tid);
-    __syncthreads();
-    float acc[NT][16];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[t][j] = 0.0f;
-    tile_rows<FMT_INT4, X_F16, NT>(g.w, g.s, N, g.group, col0, b0 + rl, b1, GV_RL, xl, Kp, corr,
-                                   nblk, acc);
-    colsum_tokens<GV_CPR, GV_THREADS, NT>(acc, red, tot, tid);
-    for (int i = tid; i < NT * 64; i += GV_THREADS) {
-      const int t = i / 64, c = i % 64;
-      if (c0 + t >= T) continue;
-      const float v = tot[t * 64 + c];
-      const int n = tile * 64 + c;
-      if (S == 1)
-        g.y[(size_t)(c0 + t) * N + n] = f32_to_bf16(v);
-      else
-        st_sc1(g.part, ((size_t)s * T + c0 + t) * N + n, v);
-    }
-  }
-  if (S == 1) return;
-  unsigned* counter = g.cnt + tile;
-  if (!last_arriver(counter, (unsigned)S, &s_flag)) return;
-  for (int i = tid; i < T * 64; i += GV_THREADS) {
-    const int t = i / 64, n = tile * 64 + i % 64;
-    float v = 0.0f;
-    for (int q = 0; q < S; ++q) v += ld_sc1(g.part, ((size_t)q * T + t) * N + n);
-    g.y[(size_t)t * N + n] = f32_to_bf16(v);
-  }
-  if (tid == 0) st_cnt(counter, 0u);
 }
 
 // =====================================================================================
@@ -264,24 +254,9 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 }
 
 hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st) {
-  const size_t sm = (size_t)(3 * a.E + 2 * SCHED_THREADS + 4) * sizeof(int);
+  const size_t sm = (size_t)(3 * a.E + 4 + SCHED_THREADS + SCHED_LDS_IDS) * sizeof(int);
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), sm, st, a, logits);
   return hipGetLastError();
-}
-
-template <int NT>
-static hipError_t launch_gemv_t(const GemvArgs& g, hipStream_t st) {
-  const int Kp = g.K / 2, nblk = g.K / 32;
-  const size_t sm = (size_t)NT * Kp * 4 + (size_t)NT * nblk * 4 + (size_t)GV_THREADS * 16 * 4 +
-                    (size_t)NT * 64 * 4;
-  hipLaunchKernelGGL(gemv_kernel<NT>, dim3(g.N / 64, g.S), dim3(GV_THREADS), sm, st, g);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv(const GemvArgs& g, int nt, hipStream_t st) {
-  if (nt == 1) return launch_gemv_t<1>(g, st);
-  if (nt == 2) return launch_gemv_t<2>(g, st);
-  return launch_gemv_t<4>(g, st);
 }
 
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,

@@ -49,7 +49,8 @@ def test_workspace_queries():
     assert B.moe_fp4_ffn_workspace_bytes(1, 2048, 768, 8, 9) == 0      # k > E
     assert B.moe_fp4_ffn_workspace_bytes(1, 2000, 768, 128, 8) == 0    # H % 64
     assert B.moe_fp4_ffn_workspace_bytes(0, 2048, 768, 128, 8) == 0
-    assert B.packed_gemv_int4_workspace_bytes(1, 5120, 34816, 128) == 0  # enough tiles
+    big = B.packed_gemv_int4_workspace_bytes(1, 5120, 34816, 128)        # K splits
+    assert big > 0 and big % 256 == 0
     assert B.packed_gemv_int4_workspace_bytes(1, 5120, 8192, 128) > 0    # K split
     assert B.packed_gemv_int4_workspace_bytes(1, 5120, 100, 128) == 0    # N % 64
 

@@ -45,6 +45,9 @@ def test_gemv_configs(N, T):
     (1, 5120, 8192, 128, False),   # no workspace: no K split
     (2, 256, 64, 128, True),       # one tile, short K
     (4, 5120, 64, 128, True),      # many K splits for one tile
+    (16, 5120, 320, 128, True),    # matrix-core tiles (T >= 16), half-full last tile
+    (40, 1024, 192, 32, True),     # matrix-core tiles, two token chunks of 32
+    (20, 2048, 256, 128, False),   # matrix-core tiles, no workspace
 ])
 def test_gemv_ragged(T, K, N, group, use_ws):
     g = S.make_gemv(S.GemvConfig("r", T=T, K=K, N=N, group=group), seed=3)
@@ -57,13 +60,17 @@ def test_gemv_seeds_1_2():
         check_bf16(_run(g), O.packed_gemv(g.x, g.w, g.s, 128), what=f"seed {seed}")
 
 
-def test_gemv_one_hot_rows_exact():
+@pytest.mark.parametrize("rows", [
+    [0, 1, 127, 128, 129, 2559, 2560, 5118, 5119],                       # vector-ALU tiles
+    [0, 1, 31, 32, 33, 127, 128, 129, 1000, 2559, 2560, 2561, 4095, 4096,
+     4097, 5000, 5117, 5118, 5119, 3],                                  # matrix-core tiles
+])
+def test_gemv_one_hot_rows_exact(rows):
     """x = e_k with power-of-two scales: y must equal row k of W exactly in bf16."""
     rng = np.random.default_rng(5)
     K, N, G = 5120, 256, 128
     w = rng.integers(0, 256, size=(K // 2, N), dtype=np.uint8)
     s = ((rng.integers(-8, 4, size=(K // G, N)) + 127).astype(np.uint32) << 7).astype(np.uint16)
-    rows = [0, 1, 127, 128, 129, 2559, 2560, 5118, 5119]
     x = np.zeros((len(rows), K), np.uint16)
     for i, k in enumerate(rows):
         x[i, k] = 0x3F80

@@ -148,6 +148,22 @@ def test_moe_invalid_ids_contribute_zero_and_set_error_word():
     assert np.array_equal(bits16(out)[2], res[2])
 
 
+def test_moe_ffn_duplicate_ids_in_a_token():
+    """A routing that lists an expert twice for a token: both slots contribute (the
+    schedule falls back to its general placement)."""
+    cfg = S.TINY.with_T(5)
+    L, D = _layer(cfg, seed=13)
+    ids = np.array([[2, 2], [1, 2], [3, 3], [0, 5], [2, 7]], np.int32)
+    wts = np.array([[0.25, 0.5], [0.6, 0.4], [1.0, 0.5], [0.3, 0.7], [0.9, 0.1]], np.float32)
+    B = _b()
+    out = B.moe_fp4_ffn(dev(L.x), dev(ids), dev(wts), D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                        cfg.group, cfg.fmt)
+    torch.cuda.synchronize()
+    want = O.moe_ffn(L.x, ids, wts.astype(np.float64), L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                     cfg.fmt)
+    check_bf16(bits16(out), want, what="duplicate ids")
+
+
 def test_moe_workspace_reused_across_shapes():
     B = _b()
     big = S.Q30_BATCH.with_T(16)
