@@ -319,12 +319,14 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 template <int MAXV>
 __device__ __forceinline__ void wave_route(const float* __restrict__ row, int E, int k, int lane,
                                            int* sel_e, float* sel_w) {
+  // all loads issued together (clamped index, result replaced afterwards)
+  float lv[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) lv[i] = row[min(lane + 64 * i, E - 1)];
   int key[MAXV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? logit_key(row[e]) : (int)0x80000000;
-  }
+  for (int i = 0; i < MAXV; ++i)
+    key[i] = (lane + 64 * i < E) ? logit_key(lv[i]) : (int)0x80000000;
   unsigned long long taken = 0;
   int my_key = 0, my_e = -1, top = 0;
   for (int j = 0; j < k; ++j) {

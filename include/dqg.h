@@ -85,17 +85,16 @@ int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* we
                hipStream_t stream);
 
 /*
- * Bytes of device workspace that moe_fp4_ffn / moe_fp4_layer need for these sizes.
- * Host only.  Returns 0 for invalid sizes.  The workspace holds a sticky int32 error
- * word at byte 0 (set to 1 when an expert id outside [0, E) was seen; the slot then
- * contributes zero), the device-built expert schedule, per-tile counters and fp32
- * partial sums.  Zero-fill it once before its first use; every call leaves it ready for
- * the next call with the same (H, I, E, k) and any T.  The single-launch T = 1 layer
- * keeps a completed-tile counter and double-buffered exchange rows in it, so a workspace
- * must not be shared by calls that may run at the same time, and one that was used for
- * other sizes must be zero-filled again.  Bit 1 of the error word is set when a wait of
- * the single-launch layer gave up (its output is then not valid).  Only the caller
- * clears the error word.
+ * Bytes of device workspace that moe_fp4_ffn / moe_fp4_layer need for T tokens with
+ * these sizes.  Host only.  Returns 0 for invalid sizes.
+ * The workspace holds a sticky int32 error word at byte 0 (bit 0: an expert id outside
+ * [0, E) was seen -- the slot then contributes zero; bit 1: a wait between workgroups gave
+ * up -- the output of that call is not valid), the device-built expert schedule, and
+ * exchange buffers that must hold zeros between calls.  Zero-fill a workspace once before
+ * its first use; every completed call leaves it ready for the next.  Its layout depends
+ * only on (H, I, E, k) and its size, so one workspace serves calls with any T up to the T
+ * it was sized for.  Calls that may run at the same time must not share a workspace.  Only
+ * the caller clears the error word.
  */
 size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
 
@@ -118,12 +117,14 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *     out[t] = bf16_rne( residual[t] + sum_{j<k} weights[t,j] * y_{t,j} ), j ascending,
  *     y_{t,j} = (SiLU(g) * u) W_down[e],  [g | u] = x[t] W_gate_up[e],  e = ids[t,j],
  *   accumulated in fp32.
- * Each expert's weights are read once per call whatever its token count; experts with
- * >= 16 tokens run on bf16 MFMA tiles, the others on vector-ALU tiles.
+ * Each expert's weights are streamed once per call for up to 32 of its tokens (the
+ * matrix-core tiles) or 8 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
+ * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles.
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
  * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
- * activations must satisfy |x| < 65504 (INT4 tiles multiply in fp16, accumulate in fp32).
+ * activations must satisfy |x| < 65504 (INT4 tiles multiply in fp16, accumulate in fp32;
+ * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).
  */
 int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int32_t* ids,
                 const float* weights, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
@@ -144,8 +145,8 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
                   size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of device workspace packed_gemv_int4 needs (0 is a valid answer: no
- * workspace).  Host only.  Returns 0 also for invalid sizes.
+ * Bytes of device workspace packed_gemv_int4 needs for T tokens (0: the call never splits
+ * K and needs none).  Host only.  Returns 0 also for invalid sizes.
  */
 size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
 
@@ -157,10 +158,14 @@ size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
  *   x  bf16 [T, K];  w uint8 [K/2, N];  s bf16 [K/G, N];  y bf16 [T, N] out
  *   y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation.
  * x must satisfy |x| < 65504 (the INT4 tiles multiply in fp16 with fp32 accumulation;
- * every bf16 in that range converts exactly).  When the query returns a non-zero size
- * the call splits K across workgroups: pass a workspace of at least that many bytes,
- * zero-filled before its first use (every call leaves it zero-filled again).  With a NULL
- * workspace the call runs without the K split (correct, fewer workgroups).  Deterministic.
+ * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).  T >= 16
+ * runs on fp16 MFMA tiles.  When the query returns a non-zero size the call splits K
+ * across workgroups: pass a workspace of at least that many bytes, zero-filled before its
+ * first use; every completed call leaves it zero-filled again, and one workspace serves
+ * calls with any T up to the T it was sized for.  Its first int32 is an error word (bit 1:
+ * a wait between workgroups gave up).  With a NULL workspace the call runs without the K
+ * split (correct, fewer workgroups).  Deterministic.  Calls that may run at the same time
+ * must not share a workspace.
  */
 int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
                      const uint16_t* s, int group, uint16_t* y, void* workspace,
