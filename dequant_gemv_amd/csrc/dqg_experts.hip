@@ -33,7 +33,7 @@
 namespace dqg {
 
 constexpr int EX_THREADS = 256;
-constexpr int EX_VT = 8;          // tokens per vector-ALU pass
+constexpr int EX_VT = 4;          // tokens per vector-ALU pass
 constexpr int EX_LDS = 8192;      // floats of LDS: the operand window, then the reductions
 constexpr int EX_MAX_SPLIT = 64;  // K splits of gate_up, at most
 constexpr int EX_MAX_SPLIT_GEMV = 64;  // K splits of the GEMV, at most

@@ -118,7 +118,7 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *     y_{t,j} = (SiLU(g) * u) W_down[e],  [g | u] = x[t] W_gate_up[e],  e = ids[t,j],
  *   accumulated in fp32.
  * Each expert's weights are streamed once per call for up to 32 of its tokens (the
- * matrix-core tiles) or 8 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
+ * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
  * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles.
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
