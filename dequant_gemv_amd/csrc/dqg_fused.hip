@@ -16,9 +16,10 @@
 //     row and exits; gate_up units never wait.
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
-//     rows).  Weights are loaded first; then 128 threads gather the KS partial gate/up rows
-//     of the unit's 512 h values (ascending ks), form h = SiLU(g)*u into LDS, and every
-//     lane scales its sum by its slot weight.  Units c < NC-1 publish a partial output
+//     rows).  Their weight loads wait for the first gate/up partial of their range (the
+//     gate_up loads, which are on the critical path, get the bandwidth first); then the
+//     threads gather the KS partial gate/up pairs of the unit's 512 h values (ascending
+//     ks), form h = SiLU(g)*u into LDS, and every lane scales its sum by its slot weight.  Units c < NC-1 publish a partial output
 //     row; unit c = NC-1 gathers them in ascending c, adds its own, the residual, and
 //     writes bf16 out.
 // Publication protocol: exchange buffers hold the bit pattern 0 when empty and producers
@@ -247,6 +248,21 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   const bool active = R < k * rows_per_slot;
   const int j = active ? R / rows_per_slot : 0;
   const int r0 = active ? R - j * rows_per_slot : 0;
+  // The down weights are needed only once h is complete: hold their loads until the
+  // first gate/up partial of this unit's range is published, so that the gate_up units,
+  // which are on the critical path, have the memory bandwidth to themselves until then.
+  {
+    const int f0 = 512 * c;
+    if (tid == 0 && f0 < k * I) {
+      const int jj = f0 / I, n = f0 - jj * I;
+      const float* p = gpart + ((size_t)((jj * NT + (n >> 7)) * KS + KS - 1)) * 256 + (n & 127);
+      for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
+        if (__float_as_uint(ld_sc1(p, 0)) != 0u) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+  }
   uint4 wvv[FX_ROWS];
   float sf[16];
   if (active) {
