@@ -418,6 +418,129 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   }
 }
 
+// ---- top-k routing with a short dependency chain: one wavefront per row ------------------
+// The same selection and weights as wave_route for E <= 64 * MAXV, without k serial
+// wave-wide rounds (each of which passes values between vector and scalar units):
+//  1. lane l holds the keys of elements l, l + 64, ...; groups of L = 64 / G adjacent lanes
+//     take their maximum, G = max(4, the smallest power of two >= k) <= 32 groups;
+//  2. theta = the k-th largest group maximum (the smallest one when G == k).  k distinct
+//     elements have keys >= theta, so all of the top k have keys >= theta (if fewer than k
+//     groups hold elements, theta is the smallest key and every element qualifies);
+//  3. the C >= k elements with keys >= theta are compacted into LDS (ballot prefix counts) as
+//     64-bit composites key << 32 | ~index, which are distinct and order the elements like
+//     the keys with ties to the lower index;
+//  4. candidate p's rank is the number of candidates with a larger composite; every element
+//     that beats a top-k element is a candidate, so ranks 0..k-1 are exactly the selection.
+// wave_topk_select leaves the selection in LDS, sel[r] = id and sel[64 + r] = key of rank r
+// (sel = the int view of cand + 64 * MAXV + 4); wave_topk_weights turns it into lane j < k's id
+// and weight (softmax over the k selected logits, top logit subtracted); wave_topk does both.
+// `cand` is the calling wavefront's own LDS scratch of 64 * MAXV + 68 eight-byte entries,
+// 16-byte aligned.
+// Needs 1 <= k <= 32.
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0xB1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0x4E, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0x124, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0x128, 0xF, 0xF, false));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+template <int MAXV>
+__device__ __forceinline__ int* wave_topk_select(const float* __restrict__ row, int E, int k,
+                                                 int lane, long long* cand) {
+  int key[MAXV];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) key[v] = logit_key(row[min(lane + 64 * v, E - 1)]);
+  int m = (int)0x80000000;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v)
+    if (lane + 64 * v < E) m = max(m, key[v]);
+  // group maxima over L lanes (L = 16, 8, 4 or 2 for G = 4, 8, 16, 32)
+  const int G = k <= 4 ? 4 : (k <= 8 ? 8 : (k <= 16 ? 16 : 32));
+  m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0xB1, 0xF, 0xF, false));
+  if (G <= 16) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x4E, 0xF, 0xF, false));
+  if (G <= 8) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x141, 0xF, 0xF, false));
+  if (G <= 4) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x140, 0xF, 0xF, false));
+  int* sel = reinterpret_cast<int*>(cand + 64 * MAXV + 4);  // [0, 64): ids, [64, 128): keys
+  int theta;
+  if (G == k) {
+    theta = wave_min_i32(m);
+  } else {
+    // rank the G group maxima (lane g < G takes group g's) and keep the k-th largest
+    const int L = 64 / G;
+    if (lane % L == 0) sel[lane / L] = m;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int mine = (lane < G) ? sel[lane] : (int)0x7FFFFFFF;
+    int gt0 = 0, gt1 = 0;
+    for (int h = 0; h < G; h += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(sel + h);
+      gt0 += (q.x > mine) + (q.y > mine);
+      gt1 += (q.z > mine) + (q.w > mine);
+    }
+    theta = wave_min_i32((lane < G && gt0 + gt1 < k) ? mine : (int)0x7FFFFFFF);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  // compaction of the candidates, in element order
+  int C = 0;
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) {
+    const int e = lane + 64 * v;
+    const bool c = e < E && key[v] >= theta;
+    const unsigned long long b = __ballot(c);
+    if (c) {
+      const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(b >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((unsigned)b, 0u));
+      cand[pos] = (long long)(((unsigned long long)(unsigned)key[v] << 32) |
+                              (unsigned long long)(0xFFFFFFFFu - (unsigned)e));
+    }
+    C += __popcll(b);
+  }
+  // four composites past the end that no candidate is below, so that the rank loop reads
+  // whole groups of four
+  if (lane < 4) cand[C + lane] = (long long)0x8000000000000000ll;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int p0 = 0; p0 < C; p0 += 64) {
+    const int p = p0 + lane;
+    if (p < C) {
+      const long long me = cand[p];
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      for (int h = 0; h < C; h += 4) {
+        const longlong2 u = *reinterpret_cast<const longlong2*>(cand + h);
+        const longlong2 w = *reinterpret_cast<const longlong2*>(cand + h + 2);
+        r0 += (u.x > me);
+        r1 += (u.y > me);
+        r2 += (w.x > me);
+        r3 += (w.y > me);
+      }
+      const int r = (r0 + r1) + (r2 + r3);
+      if (r < k) {
+        sel[r] = (int)(0xFFFFFFFFu - (unsigned)(unsigned long long)me);
+        sel[64 + r] = (int)(me >> 32);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  return sel;
+}
+
+__device__ __forceinline__ void wave_topk_weights(const int* sel, int k, int lane, int* sel_e,
+                                                  float* sel_w) {
+  const int my_e = (lane < k) ? sel[lane] : -1;
+  const int my_key = (lane < k) ? sel[64 + lane] : 0;
+  const float ex = (lane < k) ? expf(key_to_float(my_key) - key_to_float(sel[64])) : 0.0f;
+  const float s = wave_sum_f32(ex);
+  *sel_e = my_e;
+  *sel_w = ex / s;
+}
+
+template <int MAXV>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
+                                          long long* cand, int* sel_e, float* sel_w) {
+  wave_topk_weights(wave_topk_select<MAXV>(row, E, k, lane, cand), k, lane, sel_e, sel_w);
+}
+
 // ---- workgroup column sums ----------------------------------------------------------------
 // Lane tid owns columns chunk*16 .. chunk*16+15 of row-lane tid / CPR (chunk = tid % CPR).
 // Sum the 16 partials over all row-lanes: one LDS transpose (4 x b128 writes per lane, a

@@ -25,9 +25,11 @@
 // Publication protocol: exchange buffers hold the bit pattern 0 when empty and producers
 // never store 0 (+0.0 is stored as -0.0, which computes identically); consumers poll the
 // data itself with agent-coherent (sc1) loads, all of a gather's loads in flight at once.
-// Each buffer exists twice: a call uses copy p = (completed calls) & 1, read from a 64-bit
-// counter that every gathering down unit increments without waiting, and producers clear
-// their slots of copy 1-p, which the previous call used and the next call will use.  A
+// Each buffer exists twice: a call uses copy p = bit 20 of a 32-bit call counter, to which
+// the n_mt finishing down units add shares summing to exactly 2^20 (so bit 20 flips once
+// per call, also across wrap-around, and no unit of a call can see it flipped before every
+// unit has read it, since each finishing unit waits on all others); producers clear their
+// slots of copy 1-p, which the previous call used and the next call will use.  A
 // unit only waits on units with lower block ids, so in-order dispatch cannot deadlock;
 // waits are bounded and set bit 1 of the error word on timeout instead of hanging.
 #include <hip/hip_runtime.h>
@@ -175,37 +177,42 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   __shared__ int s_ids[32];
   __shared__ float s_w[32];
   __shared__ __align__(16) float s_red[FX_THREADS * 16];
-  __shared__ int s_par;
+  __shared__ __align__(16) long long s_route[64 * 8 + 68];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---- routing (wave 0 of every workgroup) and the buffer parity (wave 1) ----
-  if (wv == 0) {
-    int e;
-    float w;
-    route_row<512>(a.logits, a.E, k, lane, &e, &w);
-    if (lane < k) {
-      s_ids[lane] = e;
-      s_w[lane] = w;
-      if (blockIdx.x == 0 && a.ids_out) {
-        a.ids_out[lane] = e;
-        a.w_out[lane] = w;
+  // ---- routing by one wavefront per workgroup (E <= 512); which one varies with the block
+  // id, so that the routing waves of the workgroups sharing a compute unit tend to land on
+  // different SIMDs.  Only the down units (and workgroup 0, for the optional outputs) need
+  // the weights; a gate_up unit only needs its slot's id. ----
+  if (wv == (int)(blockIdx.x & 3)) {
+    const int* sel = (a.E <= 128) ? wave_topk_select<2>(a.logits, a.E, k, lane, s_route)
+                                  : wave_topk_select<8>(a.logits, a.E, k, lane, s_route);
+    if (blockIdx.x >= a.n_a || blockIdx.x == 0) {
+      int sel_e;
+      float sel_w;
+      wave_topk_weights(sel, k, lane, &sel_e, &sel_w);
+      if (lane < k) {
+        s_ids[lane] = sel_e;
+        s_w[lane] = sel_w;
+        if (blockIdx.x == 0 && a.ids_out) {
+          a.ids_out[lane] = sel_e;
+          a.w_out[lane] = sel_w;
+        }
       }
+    } else if (lane < k) {
+      s_ids[lane] = sel[lane];
     }
-  } else if (tid == 64) {
-    const unsigned long long calls =
-        __hip_atomic_load(a.calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_par = (int)((calls / (unsigned long long)a.n_mt) & 1ull);
   }
   __syncthreads();
-  const int par = s_par;
+  // The buffer parity is first needed when results are published or gathered: the counter
+  // load is issued here, after routing, and its value is taken only at that point (the empty
+  // asm keeps the compiler from waiting for it earlier), so that its latency overlaps the
+  // weight loads instead of delaying them.
+  unsigned calls = __hip_atomic_load(a.calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
   const size_t gsz = (size_t)k * NT * KS * 256;     // one copy of the gate/up partial rows
   const size_t psz = (size_t)a.n_mt * NC * 128;
-  float* gpart = a.gpart + par * gsz;
-  float* gold = a.gpart + (1 - par) * gsz;
-  float* pbuf = a.ypart + par * psz;
-  float* pold = a.ypart + (1 - par) * psz;
 
   const int bid = blockIdx.x;
   if (bid < a.n_a) {
@@ -224,6 +231,9 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
     scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((2 * r0) / a.group) * ld + col0, sf);
     uint32_t xr[FX_ROWS];
     const float corr = load_x_rows<FMT>(a.x, r0, xr);
+    // all loads above are issued before the first use (the scheduler would otherwise sink
+    // some of them to their uses, which serializes memory round trips)
+    __builtin_amdgcn_sched_barrier(0);
     float accb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
@@ -233,12 +243,19 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
     for (int c = 0; c < 16; ++c) accb[c] = sf[c] * (accb[c] + corr);
     const float mine = wg_colsum<16, FX_THREADS>(accb, s_red, tid);
     const size_t slot = (size_t)grp * KS + ks;
-    st_sc1(gpart, slot * 256 + tid, pub(mine));
-    st_sc1(gold, slot * 256 + tid, 0.0f);
+    asm volatile("" : "+v"(calls));
+    const int par = (int)((calls >> 20) & 1u);
+    st_sc1(a.gpart + par * gsz, slot * 256 + tid, pub(mine));
+    st_sc1(a.gpart + (1 - par) * gsz, slot * 256 + tid, 0.0f);
     return;
   }
 
   // ================= down unit (mt, c) =================
+  asm volatile("" : "+v"(calls));
+  const int par = (int)((calls >> 20) & 1u);
+  const float* gpart = a.gpart + par * gsz;
+  float* pbuf = a.ypart + par * psz;
+  float* pold = a.ypart + (1 - par) * psz;
   const int ub = bid - a.n_a;
   const int mt = ub / NC, c = ub - mt * NC;
   const int rl = tid >> 3, ch = tid & 7;
@@ -248,10 +265,11 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   const bool active = R < k * rows_per_slot;
   const int j = active ? R / rows_per_slot : 0;
   const int r0 = active ? R - j * rows_per_slot : 0;
-  // The down weights are needed only once h is complete: hold their loads until the
-  // first gate/up partial of this unit's range is published, so that the gate_up units,
-  // which are on the critical path, have the memory bandwidth to themselves until then.
-  {
+  // The down weights are needed only once h is complete: on layers whose gate_up weights
+  // take long enough to stream to matter (hold_down), hold their loads until the first
+  // gate/up partial of this unit's range is published, so that the gate_up units, which are
+  // on the critical path, have the memory bandwidth to themselves until then.
+  if (a.hold_down) {
     const int f0 = 512 * c;
     if (tid == 0 && f0 < k * I) {
       const int jj = f0 / I, n = f0 - jj * I;
@@ -369,7 +387,11 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   y += mine;
   if (a.res) y += bf16_to_f32(a.res[m]);
   a.out[m] = f32_to_bf16(y);
-  if (tid == 0) __hip_atomic_fetch_add(a.calls, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    const unsigned share = (1u << 20) / (unsigned)a.n_mt;
+    const unsigned add = (mt + 1 < a.n_mt) ? share : (1u << 20) - (unsigned)(a.n_mt - 1) * share;
+    __hip_atomic_fetch_add(a.calls, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 bool fused_supported(int H, int I, int k) {
@@ -392,7 +414,8 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int k) {
   f.n_chunks = (k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
   f.n_a = k * (I / 128) * f.ks;
   f.n_b = f.n_mt * f.n_chunks;
-  f.calls = reinterpret_cast<unsigned long long*>(p);
+  f.hold_down = (size_t)k * (H / 2) * (2 * (size_t)I) >= ((size_t)1 << 20);
+  f.calls = reinterpret_cast<unsigned int*>(p);
   size_t o = 256;
   f.gpart = reinterpret_cast<float*>(p + o);
   o += 2 * (size_t)k * (I / 128) * f.ks * 256 * 4;

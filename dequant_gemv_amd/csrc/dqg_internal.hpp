@@ -67,9 +67,10 @@ struct FusedArgs {
   float* w_out;
   float* gpart;         // [2][k * I/128 * ks][256] gate/up partial rows, two copies
   float* ypart;         // [2][H/128 * n_chunks][128] output partial rows, two copies
-  unsigned long long* calls;  // completed column tiles over all calls (parity source)
+  unsigned int* calls;  // call counter: every call adds 2^20 in total (parity source)
   int* err;
   int n_a, n_b, n_chunks, ks, n_mt;
+  int hold_down;        // down units load their weights only once gate/up results appear
 };
 bool fused_supported(int H, int I, int k);
 size_t fused_ws_bytes(int H, int I, int k);

@@ -326,3 +326,40 @@ def test_moe_mfma_deterministic():
     o1, _, _ = _run_layer(cfg, L, D)
     o2, _, _ = _run_layer(cfg, L, D)
     assert np.array_equal(o1, o2)
+
+
+def _route_logits(E, dist, rng):
+    if dist == "ties5":
+        return rng.choice(np.array([-1.0, 0.0, -0.0, 1.0, 0.5], np.float32), size=(1, E))
+    if dist == "equal":
+        return np.full((1, E), 0.25, np.float32)
+    if dist == "bf16":   # router logits rounded to bf16: many exact ties near the top
+        return S.bf16_bits_view_f32(S.f32_to_bf16_bits(rng.standard_normal((1, E)) * 2.0))
+    if dist == "ascending":  # the largest logits sit at the highest expert indices
+        return (np.arange(E, dtype=np.float32) * 0.01)[None, :]
+    return rng.standard_normal((1, E)).astype(np.float32)
+
+
+ROUTE_CASES = [(8, 2, "ties5"), (8, 8, "equal"), (70, 7, "ties5"), (128, 8, "bf16"),
+               (128, 8, "equal"), (128, 32, "normal"), (33, 32, "normal"), (256, 16, "ties5"),
+               (300, 5, "ascending"), (512, 10, "bf16"), (512, 32, "equal"),
+               (512, 1, "ascending"), (512, 10, "normal")]
+
+
+@pytest.mark.parametrize("E,k,dist", ROUTE_CASES, ids=[f"E{c[0]}-k{c[1]}-{c[2]}" for c in ROUTE_CASES])
+def test_fused_layer_routing_edge_cases(E, k, dist):
+    """The single-launch T=1 layer routes with its own workgroup-wide top-k: ids bit-exact
+    (ties to the lower index, -0.0 == +0.0), weights and output against the oracle, on tied,
+    all-equal, bf16-rounded and index-ordered logits, E not a multiple of 8, k up to 32."""
+    cfg = S.MoEConfig("route", T=1, E=E, H=256, I=128, k=k, fmt=S.FMT_FP4, group=32,
+                      scale_lo=0.005, scale_hi=0.02)
+    L = S.make_moe_layer(cfg, seed=E + k)
+    lg = _route_logits(E, dist, np.random.default_rng(E * 31 + k))
+    L = S.replace(L, logits=lg)
+    D = upload_layer(L)
+    out, ids, w = _run_layer(cfg, L, D)
+    oids, ow = O.topk_route(lg, k)
+    assert np.array_equal(ids, oids), f"ids {ids} vs oracle {oids}"
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    want, _, _ = _oracle_layer(cfg, L)
+    check_bf16(out, want, what=f"route E={E} k={k} {dist}")
