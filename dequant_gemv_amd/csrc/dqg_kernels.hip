@@ -13,13 +13,30 @@ namespace dqg {
 // =====================================================================================
 // top-k routing: one wavefront per token
 // =====================================================================================
+// LDS scratch entries (8 bytes) of one routing wavefront: wave_topk over E <= 64 * v
+constexpr int route_scratch(int v) { return 64 * v + 68; }
+
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __align__(16) long long scratch[4][route_scratch(8)];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
-  route_token(logits, t, E, k, lane, ids, wts);
+  if (E > 512) {
+    route_token(logits, t, E, k, lane, ids, wts);
+    return;
+  }
+  int e;
+  float w;
+  if (E <= 128)
+    wave_topk<2>(logits + (size_t)t * E, E, k, lane, scratch[wv], &e, &w);
+  else
+    wave_topk<8>(logits + (size_t)t * E, E, k, lane, scratch[wv], &e, &w);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = e;
+    wts[(size_t)t * k + lane] = w;
+  }
 }
 
 // =====================================================================================
@@ -31,6 +48,17 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 constexpr int SCHED_THREADS = 1024;
 
 constexpr int SCHED_LDS_IDS = 2048;  // slots whose ids are kept in LDS
+
+// Routing wavefronts of the schedule kernel and their LDS scratch (after the int arrays,
+// 16-byte aligned): E <= 128 uses all 16 waves, E <= 512 the first 8 (larger scratch each),
+// E > 512 the register-free selection with no scratch.
+__host__ __device__ constexpr int sched_route_waves(int E) { return E <= 128 ? 16 : (E <= 512 ? 8 : 0); }
+__host__ __device__ constexpr int sched_int_words(int E) {
+  return (3 * E + 4 + SCHED_THREADS + SCHED_LDS_IDS + 3) & ~3;
+}
+__host__ __device__ constexpr int sched_scratch_entries(int E) {
+  return E <= 128 ? route_scratch(2) : route_scratch(8);
+}
 
 // exclusive prefix sums over experts of cnt (-> pos) by wave 0 (lane l takes experts
 // [l * per, l * per + per)); with `records`, active experts also get their records.
@@ -82,10 +110,20 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   if (logits) {  // routing from logits, one wave per token
-    for (int t = wv; t < T; t += SCHED_THREADS / 64) {
+    const int RW = sched_route_waves(E);
+    long long* scratch = reinterpret_cast<long long*>(sm + sched_int_words(E)) +
+                         (size_t)wv * sched_scratch_entries(E);
+    const int stride = RW ? RW : SCHED_THREADS / 64;
+    for (int t = wv; t < T && (RW == 0 || wv < RW); t += stride) {
       int e;
       float w;
-      route_row<4096>(logits + (size_t)t * E, E, k, lane, &e, &w);
+      const float* row = logits + (size_t)t * E;
+      if (E <= 128)
+        wave_topk<2>(row, E, k, lane, scratch, &e, &w);
+      else if (E <= 512)
+        wave_topk<8>(row, E, k, lane, scratch, &e, &w);
+      else
+        route_row<4096>(row, E, k, lane, &e, &w);
       if (lane < k) {
         a.ids_w[(size_t)t * k + lane] = e;
         a.wts_w[(size_t)t * k + lane] = w;
@@ -254,7 +292,8 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 }
 
 hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st) {
-  const size_t sm = (size_t)(3 * a.E + 4 + SCHED_THREADS + SCHED_LDS_IDS) * sizeof(int);
+  const size_t sm = (size_t)sched_int_words(a.E) * sizeof(int) +
+                    (size_t)sched_route_waves(a.E) * sched_scratch_entries(a.E) * 8;
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), sm, st, a, logits);
   return hipGetLastError();
 }
