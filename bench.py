@@ -61,7 +61,9 @@ WORKLOADS = {
 DEFAULT_WORKLOAD = "q30_moe_layer_t1"
 KERNEL_SOURCES = {
     "fused_t1_kernel": ("dqg_fused.hip", "dqg_device.hpp", "dqg_internal.hpp"),
-    "gemv_kernel": ("dqg_kernels.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+    "gemv_ex_kernel": ("dqg_experts.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+    "moe_layer_multi_launch": ("dqg_kernels.hip", "dqg_experts.hip", "dqg_device.hpp",
+                               "dqg_internal.hpp"),
 }
 
 
@@ -339,9 +341,9 @@ def bench_gemv(w, args, dev, stream, B):
     us = ms_per_step * 1000.0 / len(sets)
     abytes = (K // 2) * N + (K // G) * N * 2
     gbps = abytes / (us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "gemv_kernel", "achieved": round(gbps, 1),
+    roofline = {"bound": "hbm", "kernel": "gemv_ex_kernel", "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                "traffic": read_traffic("gemv_kernel", args.workload), "bytes_per_launch": abytes,
+                "traffic": read_traffic("gemv_ex_kernel", args.workload), "bytes_per_launch": abytes,
                 "avg_launch_us": round(us, 3),
                 "timing": "events around the K timed graph replays / GEMV calls (one "
                           "launch per call)"}
@@ -367,8 +369,8 @@ def main():
                          "used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path "
-              "is single-GPU; see the sharding notes in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: every kernel "
+              "of this library runs on a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -174,10 +174,10 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
 }
 
 // matrix-core tile height of the expert kernels: none when no expert can reach mfma_min
-int mfma_tiles(const MoeArgs& a) {
-  if (a.mfma_min > a.T) return 0;
-  return a.T <= 16 ? 1 : 2;
-}
+// Matrix-core tiles per pass of a hot expert: one 16-row tile (an expert with more tokens
+// takes more passes, whose weight re-reads mostly hit L2); a second tile would raise the
+// register count of the combined kernel, and with it lower the occupancy of every expert.
+int mfma_tiles(const MoeArgs& a) { return a.mfma_min > a.T ? 0 : 1; }
 
 bool use_fused(int T, int H, int I, int E, int k, int format) {
   return T == 1 && E <= 512 && dqg::fused_supported(H, I, k) && !(format & DQG_PATH_NO_FUSED);

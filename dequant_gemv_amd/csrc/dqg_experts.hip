@@ -550,10 +550,10 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
                                (size_t)(H / a.group) * ld * 2),
                      (int)ld, a.group};
   const OpSrc src{view_rsrc(a.x, (size_t)a.T * H * 2), true, 2 * H, k};
-  // MT = 0: the vector-ALU kernel (experts below mfma_min); MT > 0: the matrix-core kernel
-  const bool use_mfma = cnt >= a.mfma_min;
-  if (use_mfma != (MT > 0)) return;
-  const int CH = MT > 0 ? 16 * MT : VT;
+  // Experts with at least mfma_min tokens take MT matrix-core tiles of 16 rows (MT > 0),
+  // the others VT-token vector-ALU passes, in the same launch.
+  const bool use_mfma = MT > 0 && cnt >= a.mfma_min;
+  const int CH = use_mfma ? 16 * MT : VT;
   const __amdgpu_buffer_rsrc_t pr = ex_rsrc(a.ws.part_gu);
 
   auto emit = [&](int slot, int c4, float4 g, float4 u) {
@@ -609,7 +609,7 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
     if (tid < nch) s_slot[tid] = slot_at(a, beg + m0 + tid);
     __syncthreads();
     if constexpr (MT > 0) {
-      {
+      if (use_mfma) {
         Acc<BODY_MFMA, MT> acc;
         stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 2>(v, col, col_ok, src, s_slot, nch, b0,
                                                          b1, khalf, lds, wa, acc);
@@ -638,7 +638,6 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
         continue;
       }
     }
-    if constexpr (MT > 0) continue;
     Acc<BODY_VALU, VT> acc;
     stream_valu<FMT, VT, 2, 2>(v, col, col_ok, src, s_slot, nch, b0, b1, khalf, lds, wa, acc);
     // two halves of 4 tokens: red[role][khalf][kg][token 0..3][column 0..127]
@@ -751,9 +750,8 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
                                (size_t)(I / a.group) * ld * 2),
                      (int)ld, a.group};
   const OpSrc src{view_rsrc(a.ws.hop, (size_t)TKc * I * 2), false, 2 * I, k};
-  const bool use_mfma = cnt >= a.mfma_min;
-  if (use_mfma != (MT > 0)) return;
-  const int CH = MT > 0 ? 16 * MT : VT;
+  const bool use_mfma = MT > 0 && cnt >= a.mfma_min;  // as in gate_up
+  const int CH = use_mfma ? 16 * MT : VT;
   auto emit = [&](int slot, int c4, float4 y) {
     st4_sc1(pr, ((s * TKc + slot) * H + m0c + c4) * 4, pub4(y));
   };
@@ -764,7 +762,10 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
     load_group<2>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
     if (tid < nch) s_slot[tid] = slot_at(a, beg + c0 + tid);
     __syncthreads();
+    bool done = false;
     if constexpr (MT > 0) {
+      if (use_mfma) {
+      done = true;
       Acc<BODY_MFMA, MT> acc;
       stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1,
                                                        wv, lds, wa, acc);
@@ -791,7 +792,9 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
         }
         __syncthreads();
       }
-    } else {
+      }
+    }
+    if (!done) {
       Acc<BODY_VALU, VT> acc;
       stream_valu<FMT, VT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1, wv, lds, wa, acc);
 #pragma unroll
@@ -983,28 +986,24 @@ static hipError_t launch_phase(const MoeArgs& a, int A, bool down, hipStream_t s
 
 template <int FMT>
 static hipError_t launch_ex_t(const MoeArgs& a0, int A, int mt, hipStream_t st) {
-  const bool valu = a0.mfma_min > 1;  // some expert can be below the threshold
+  // one launch per phase: with matrix-core tiles (mt > 0) the kernel serves the experts
+  // below the threshold with EX_VT-token vector-ALU passes in the same launch
   const int vt = valu_width(a0.T);
   MoeArgs a = a0;
   for (int down = 0; down < 2; ++down) {
-    hipError_t e = hipSuccess;
-    if (valu) {
-      a.combine = down && mt == 0;  // the last down launch runs the combiners
-      if (vt == 1) e = launch_phase<FMT, 0, 1>(a, A, down, st);
-      else if (vt == 2) e = launch_phase<FMT, 0, 2>(a, A, down, st);
-      else if (vt == 4) e = launch_phase<FMT, 0, 4>(a, A, down, st);
-      else e = launch_phase<FMT, 0, EX_VT>(a, A, down, st);
-    }
-    a.combine = down;
-    if (e == hipSuccess && mt == 1) e = launch_phase<FMT, 1, 1>(a, A, down, st);
-    if (e == hipSuccess && mt == 2) e = launch_phase<FMT, 2, 1>(a, A, down, st);
+    a.combine = down;  // the down launch also runs the per-token combiners
+    hipError_t e;
+    if (mt == 1) e = launch_phase<FMT, 1, EX_VT>(a, A, down, st);
+    else if (vt == 1) e = launch_phase<FMT, 0, 1>(a, A, down, st);
+    else if (vt == 2) e = launch_phase<FMT, 0, 2>(a, A, down, st);
+    else e = launch_phase<FMT, 0, EX_VT>(a, A, down, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st) {
-  if (mt < 0 || mt > 2) return hipErrorInvalidValue;
+  if (mt < 0 || mt > 1) return hipErrorInvalidValue;
   if (a.fmt == FMT_FP4) return launch_ex_t<FMT_FP4>(a, A, mt, st);
   if (a.fmt == FMT_INT4) return launch_ex_t<FMT_INT4>(a, A, mt, st);
   return hipErrorInvalidValue;

@@ -80,8 +80,9 @@ hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
                        hipStream_t st);
 hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st);
-// gate_up + down expert kernels; mt = 0: vector-ALU tiles only, 1 or 2: matrix-core tiles
-// of 16 mt tokens for experts with at least mfma_min tokens
+// gate_up + down expert kernels, one launch each; mt = 0: vector-ALU tiles only, mt = 1:
+// 16-token matrix-core tiles for experts with at least mfma_min tokens and vector-ALU
+// passes for the others, in the same launch
 hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st);
 int ex_max_split();
 constexpr unsigned EX_SPIN_LIMIT = 1u << 16;  // polling rounds before a wait gives up
