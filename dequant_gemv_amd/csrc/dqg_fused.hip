@@ -9,6 +9,8 @@
 // A whole T=1 layer moves only ~21 MB, so it is one launch whose workgroups read full
 // 128-byte lines and exchange data with as few round trips as possible.
 //
+// Every workgroup first routes the token itself (one wavefront, threshold + compaction +
+// rank selection; no other workgroup is waited for).
 // Workgroups (256 threads, 4 waves), every lane owning 16 columns x 8 byte rows:
 //   gate_up units (j, nt, ks): slot j, h columns [128 nt, 128 nt + 128) -- 128 bytes of
 //     gate and 128 bytes of up per byte row (16 lanes) -- over byte rows
@@ -16,8 +18,9 @@
 //     row and exits; gate_up units never wait.
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
-//     rows).  Their weight loads wait for the first gate/up partial of their range (the
-//     gate_up loads, which are on the critical path, get the bandwidth first); then the
+//     rows).  On layers with >= 1 MiB of gate_up weights, their weight loads wait for the
+//     first gate/up partial of their range (the gate_up loads, which are on the critical
+//     path, get the bandwidth first); then the
 //     threads gather the KS partial gate/up pairs of the unit's 512 h values (ascending
 //     ks), form h = SiLU(g)*u into LDS, and every lane scales its sum by its slot weight.  Units c < NC-1 publish a partial output
 //     row; unit c = NC-1 gathers them in ascending c, adds its own, the residual, and

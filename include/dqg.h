@@ -117,9 +117,12 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *     out[t] = bf16_rne( residual[t] + sum_{j<k} weights[t,j] * y_{t,j} ), j ascending,
  *     y_{t,j} = (SiLU(g) * u) W_down[e],  [g | u] = x[t] W_gate_up[e],  e = ids[t,j],
  *   accumulated in fp32.
- * Each expert's weights are streamed once per call for up to 32 of its tokens (the
+ * Each expert's weights are streamed once per call for up to 16 of its tokens (the
  * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
- * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles.
+ * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch per
+ * projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16 (FP4)
+ * or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch T = 1 layer
+ * (moe_fp4_layer).
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
  * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
