@@ -165,7 +165,7 @@ def cpu_baseline(budget_s: float = 12.0):
     layers, t_total, n = 0, 0.0, 0
     with threadpool_limits(limits=1):
         seed = 0
-        while t_total < budget_s and n < 64:
+        while t_total < budget_s and n < 512:
             ids_needed = O.topk_route(S.moe_layer_logits(cfg, seed), cfg.k)[0]
             L = S.make_moe_layer(cfg, seed, experts=np.unique(ids_needed))
             t0 = time.perf_counter()

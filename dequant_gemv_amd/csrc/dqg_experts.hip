@@ -830,8 +830,9 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
 // dense packed INT4 GEMV: y [T, N] = x [T, K] W, the E = 1 case of the expert tiles.
 // Grid: x = 128-column tile, y = K split; wave w takes blocks g0 + w + 4 r.  Splits are
 // summed by the last workgroup of a tile, in split order, which also resets the counter.
-// (Dequantized-GEMV page, "Custom GEMV kernel": one pass over the packed weight rows with
-// fp32 accumulation; here 4-bit weights decoded in registers.)
+// (FastInfer page, "Specialized matrix-vector result": a single-row matrix-vector product
+// over contiguous stored weights with fp32 reductions; here the weights are packed 4-bit
+// codes decoded in registers.)
 // ======================================================================================
 template <int MT, int VT>
 __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
