@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
     const float mine = wg_colsum<16, FX_THREADS>(accb, s_red, tid);
     const size_t slot = (size_t)grp * KS + ks;
     asm volatile("" : "+v"(calls));
-    const int par = (int)((calls >> 20) & 1u);
+    const int par = (int)((__builtin_amdgcn_readfirstlane(calls) >> 20) & 1u);  // uniform
     st_sc1(a.gpart + par * gsz, slot * 256 + tid, pub(mine));
     st_sc1(a.gpart + (1 - par) * gsz, slot * 256 + tid, 0.0f);
     return;
@@ -255,7 +255,8 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
 
   // ================= down unit (mt, c) =================
   asm volatile("" : "+v"(calls));
-  const int par = (int)((calls >> 20) & 1u);
+  // uniform, so that the exchange buffers' descriptors stay in scalar registers
+  const int par = (int)((__builtin_amdgcn_readfirstlane(calls) >> 20) & 1u);
   const float* gpart = a.gpart + par * gsz;
   float* pbuf = a.ypart + par * psz;
   float* pold = a.ypart + (1 - par) * psz;
