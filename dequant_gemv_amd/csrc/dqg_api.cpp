@@ -52,10 +52,11 @@ int expected_active(int T, int E, int k) {
   return std::max(1, std::min(std::min(E, T * k), (int)std::lround(E * (1.0 - miss))));
 }
 
-// K splits of a streaming kernel: one batch of `per_wg` blocks (16 byte rows each) per
-// workgroup when possible -- many small workgroups keep the most bytes in flight -- but
-// at most `max_split`, and few enough that the fp32 split partials (partial_bytes per
-// split) stay under 15% of the weight bytes the kernel streams.
+// K splits of a streaming kernel: `per_wg` blocks (16 byte rows each) per workgroup when
+// possible -- a few batches each, so that many workgroups keep bytes in flight while the
+// split partials and their finishers stay cheap -- but at most `max_split`, and few enough
+// that the fp32 split partials (partial_bytes per split) stay under 15% of the weight bytes
+// the kernel streams.
 int pick_ex_split(int nblk, int per_wg, int max_split, double weight_bytes,
                   double partial_bytes) {
   int S = (nblk + per_wg - 1) / per_wg;
@@ -115,9 +116,12 @@ MoePlan plan_moe(int T, int H, int I, int E, int k, size_t ws_bytes = 0) {
   }
   const int a_est = expected_active(T, E, k);
   const double gu_bytes = (double)a_est * H * I * 1.125, dn_bytes = gu_bytes / 2;
-  p.S_gu = std::min(pick_ex_split(H / 32, 4, dqg::ex_max_split(), gu_bytes, 8.0 * p.TK * I),
+  // blocks (16 byte rows) per workgroup: 8 for gate_up, 32 for down -- measured best over
+  // T = 4 .. 64 and the 128- and 512-expert shapes (smaller batches raise the partial
+  // traffic and the finisher work; down needs no K split at all for I <= 1024)
+  p.S_gu = std::min(pick_ex_split(H / 32, 8, dqg::ex_max_split(), gu_bytes, 8.0 * p.TK * I),
                     p.sgu_max);
-  p.S_dn = std::min(pick_ex_split(I / 32, 8, kMaxSplitDown, dn_bytes, 4.0 * p.TK * H), p.sdn_max);
+  p.S_dn = std::min(pick_ex_split(I / 32, 32, kMaxSplitDown, dn_bytes, 4.0 * p.TK * H), p.sdn_max);
   return p;
 }
 
@@ -237,7 +241,9 @@ GemvPlan plan_gemv(int T, int K, int N, size_t ws_bytes = 0) {
     }
     gemv_layout(g, K, N, lo);
   }
-  g.S = std::min(pick_ex_split(K / 32, 8, dqg::ex_max_split_gemv(), (double)K / 2 * N * 1.06,
+  // 16 blocks (two batches) per workgroup: measured best for N = 256 .. 34816, T = 1 and 4
+  // (8 or 4 blocks: more partial traffic and finishers; 32 or 64: too few workgroups)
+  g.S = std::min(pick_ex_split(K / 32, 16, dqg::ex_max_split_gemv(), (double)K / 2 * N * 1.06,
                                4.0 * T * N),
                  g.s_max);
   return g;

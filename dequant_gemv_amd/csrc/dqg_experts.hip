@@ -447,7 +447,8 @@ __device__ __forceinline__ void compute_group(const WBlock (&wb)[RBW], const uin
 // wave takes blocks bb + off + STEP * r (r < RBW) of batch bb.  A batch's weights go to
 // registers and its activation operands to an LDS window; the caller has loaded the first
 // batch into wa (so that those loads overlap its own set-up).  Splits are sized so that a
-// workgroup usually has one batch: many small workgroups keep the most bytes in flight.
+// workgroup streams a few batches (many workgroups keep the bytes in flight; fewer splits
+// keep the partial traffic low).
 // Leaves the LDS free (a barrier follows the last batch).
 template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP>
 __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool col_ok,
