@@ -431,12 +431,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
 //     the keys with ties to the lower index;
 //  4. candidate p's rank is the number of candidates with a larger composite; every element
 //     that beats a top-k element is a candidate, so ranks 0..k-1 are exactly the selection.
-// wave_topk_select leaves the selection in LDS, sel[r] = id and sel[64 + r] = key of rank r
-// (sel = the int view of cand + 64 * MAXV + 4); wave_topk_weights turns it into lane j < k's id
-// and weight (softmax over the k selected logits, top logit subtracted); wave_topk does both.
-// `cand` is the calling wavefront's own LDS scratch of 64 * MAXV + 68 eight-byte entries,
-// 16-byte aligned.
-// Needs 1 <= k <= 32.
+// wave_topk_select writes the selection to LDS, ids[r] and keys[r] for rank r < k (visible
+// to the calling wavefront on return); wave_topk_weights turns it into lane j < k's id and
+// weight (softmax over the k selected logits, top logit subtracted); wave_topk does both,
+// through its scratch.  `cand` is the calling wavefront's own LDS scratch of 64 * MAXV + 68
+// eight-byte entries, 16-byte aligned.  Needs 1 <= k <= 32.
 __device__ __forceinline__ int wave_min_i32(int v) {
   v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0xB1, 0xF, 0xF, false));
   v = min(v, __builtin_amdgcn_update_dpp((int)0x7FFFFFFF, v, 0x4E, 0xF, 0xF, false));
@@ -448,8 +447,9 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 }
 
 template <int MAXV>
-__device__ __forceinline__ int* wave_topk_select(const float* __restrict__ row, int E, int k,
-                                                 int lane, long long* cand) {
+__device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, int E, int k,
+                                                 int lane, long long* cand, int* ids,
+                                                 int* keys) {
   int key[MAXV];
 #pragma unroll
   for (int v = 0; v < MAXV; ++v) key[v] = logit_key(row[min(lane + 64 * v, E - 1)]);
@@ -463,7 +463,7 @@ __device__ __forceinline__ int* wave_topk_select(const float* __restrict__ row, 
   if (G <= 16) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x4E, 0xF, 0xF, false));
   if (G <= 8) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x141, 0xF, 0xF, false));
   if (G <= 4) m = max(m, __builtin_amdgcn_update_dpp((int)0x80000000, m, 0x140, 0xF, 0xF, false));
-  int* sel = reinterpret_cast<int*>(cand + 64 * MAXV + 4);  // [0, 64): ids, [64, 128): keys
+  int* sel = reinterpret_cast<int*>(cand + 64 * MAXV + 4);  // scratch for the group ranks
   int theta;
   if (G == k) {
     theta = wave_min_i32(m);
@@ -497,39 +497,65 @@ __device__ __forceinline__ int* wave_topk_select(const float* __restrict__ row, 
     }
     C += __popcll(b);
   }
-  // four composites past the end that no candidate is below, so that the rank loop reads
-  // whole groups of four
-  if (lane < 4) cand[C + lane] = (long long)0x8000000000000000ll;
+  // composites that no candidate is below fill the list to 32 entries and 4 past its end, so
+  // that the rank loops read whole groups
+  const long long below = (long long)0x8000000000000000ll;
+  if (lane < 4) cand[C + lane] = below;
+  if (lane >= C && lane < 32) cand[lane] = below;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int p0 = 0; p0 < C; p0 += 64) {
-    const int p = p0 + lane;
-    if (p < C) {
-      const long long me = cand[p];
-      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-      for (int h = 0; h < C; h += 4) {
-        const longlong2 u = *reinterpret_cast<const longlong2*>(cand + h);
-        const longlong2 w = *reinterpret_cast<const longlong2*>(cand + h + 2);
-        r0 += (u.x > me);
-        r1 += (u.y > me);
-        r2 += (w.x > me);
-        r3 += (w.y > me);
-      }
-      const int r = (r0 + r1) + (r2 + r3);
-      if (r < k) {
-        sel[r] = (int)(0xFFFFFFFFu - (unsigned)(unsigned long long)me);
-        sel[64 + r] = (int)(me >> 32);
+  if (C <= 32) {
+    // the usual case: every lane reads the 32 entries at once and compares them unrolled
+    const long long me = cand[lane < 32 ? lane : 31];
+    long long cv[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const longlong2 u = reinterpret_cast<const longlong2*>(cand)[i];
+      cv[2 * i] = u.x;
+      cv[2 * i + 1] = u.y;
+    }
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+#pragma unroll
+    for (int h = 0; h < 32; h += 4) {
+      r0 += (cv[h] > me);
+      r1 += (cv[h + 1] > me);
+      r2 += (cv[h + 2] > me);
+      r3 += (cv[h + 3] > me);
+    }
+    const int r = (r0 + r1) + (r2 + r3);
+    if (lane < C && r < k) {
+      ids[r] = (int)(0xFFFFFFFFu - (unsigned)(unsigned long long)me);
+      keys[r] = (int)(me >> 32);
+    }
+  } else {
+    for (int p0 = 0; p0 < C; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < C) {
+        const long long me = cand[p];
+        int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+        for (int h = 0; h < C; h += 4) {
+          const longlong2 u = *reinterpret_cast<const longlong2*>(cand + h);
+          const longlong2 w = *reinterpret_cast<const longlong2*>(cand + h + 2);
+          r0 += (u.x > me);
+          r1 += (u.y > me);
+          r2 += (w.x > me);
+          r3 += (w.y > me);
+        }
+        const int r = (r0 + r1) + (r2 + r3);
+        if (r < k) {
+          ids[r] = (int)(0xFFFFFFFFu - (unsigned)(unsigned long long)me);
+          keys[r] = (int)(me >> 32);
+        }
       }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  return sel;
 }
 
-__device__ __forceinline__ void wave_topk_weights(const int* sel, int k, int lane, int* sel_e,
-                                                  float* sel_w) {
-  const int my_e = (lane < k) ? sel[lane] : -1;
-  const int my_key = (lane < k) ? sel[64 + lane] : 0;
-  const float ex = (lane < k) ? expf(key_to_float(my_key) - key_to_float(sel[64])) : 0.0f;
+__device__ __forceinline__ void wave_topk_weights(const int* ids, const int* keys, int k,
+                                                  int lane, int* sel_e, float* sel_w) {
+  const int my_e = (lane < k) ? ids[lane] : -1;
+  const int my_key = (lane < k) ? keys[lane] : 0;
+  const float ex = (lane < k) ? expf(key_to_float(my_key) - key_to_float(keys[0])) : 0.0f;
   const float s = wave_sum_f32(ex);
   *sel_e = my_e;
   *sel_w = ex / s;
@@ -538,7 +564,9 @@ __device__ __forceinline__ void wave_topk_weights(const int* sel, int k, int lan
 template <int MAXV>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane,
                                           long long* cand, int* sel_e, float* sel_w) {
-  wave_topk_weights(wave_topk_select<MAXV>(row, E, k, lane, cand), k, lane, sel_e, sel_w);
+  int* sel = reinterpret_cast<int*>(cand + 64 * MAXV + 4);  // ids [0, 32), keys [64, 96)
+  wave_topk_select<MAXV>(row, E, k, lane, cand, sel, sel + 64);
+  wave_topk_weights(sel, sel + 64, k, lane, sel_e, sel_w);
 }
 
 // ---- workgroup column sums ----------------------------------------------------------------

@@ -178,6 +178,7 @@ __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n,
 template <int FMT>
 __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   __shared__ int s_ids[32];
+  __shared__ int s_key[32];
   __shared__ float s_w[32];
   __shared__ __align__(16) float s_red[FX_THREADS * 16];
   __shared__ __align__(16) long long s_route[64 * 8 + 68];
@@ -189,22 +190,21 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   // different SIMDs.  Only the down units (and workgroup 0, for the optional outputs) need
   // the weights; a gate_up unit only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
-    const int* sel = (a.E <= 128) ? wave_topk_select<2>(a.logits, a.E, k, lane, s_route)
-                                  : wave_topk_select<8>(a.logits, a.E, k, lane, s_route);
+    if (a.E <= 128)
+      wave_topk_select<2>(a.logits, a.E, k, lane, s_route, s_ids, s_key);
+    else
+      wave_topk_select<8>(a.logits, a.E, k, lane, s_route, s_ids, s_key);
     if (blockIdx.x >= a.n_a || blockIdx.x == 0) {
       int sel_e;
       float sel_w;
-      wave_topk_weights(sel, k, lane, &sel_e, &sel_w);
+      wave_topk_weights(s_ids, s_key, k, lane, &sel_e, &sel_w);
       if (lane < k) {
-        s_ids[lane] = sel_e;
         s_w[lane] = sel_w;
         if (blockIdx.x == 0 && a.ids_out) {
           a.ids_out[lane] = sel_e;
           a.w_out[lane] = sel_w;
         }
       }
-    } else if (lane < k) {
-      s_ids[lane] = sel[lane];
     }
   }
   __syncthreads();
