@@ -60,7 +60,7 @@ WORKLOADS = {
 }
 DEFAULT_WORKLOAD = "q30_moe_layer_t1"
 KERNEL_SOURCES = {
-    "fused_t1_kernel": ("dqg_fused.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+    "fused_layer_kernel": ("dqg_fused.hip", "dqg_device.hpp", "dqg_internal.hpp"),
     "gemv_ex_kernel": ("dqg_experts.hip", "dqg_device.hpp", "dqg_internal.hpp"),
     "moe_layer_multi_launch": ("dqg_kernels.hip", "dqg_experts.hip", "dqg_device.hpp",
                                "dqg_internal.hpp"),
@@ -296,12 +296,15 @@ def bench_moe(w, args, dev, stream, B):
     per_expert = expert_bytes(H, I, G)
     n_active = [distinct_experts(L["logits"], k) for L in layers]
     abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
-    fused = args.path == "auto" and T == 1 and E <= 512
+    # the single-launch layer takes T <= 4 (for T > 1 a token's down rows must fill whole
+    # 256-row chunks), E <= 512, H % 256 == 0, H <= 2048, I % 128 == 0
+    fused = (args.path == "auto" and T <= 4 and E <= 512 and H % 256 == 0 and H <= 2048
+             and I % 128 == 0 and (T == 1 or (k * (I // 2)) % 256 == 0))
     gbps = abytes / (us_per_layer * 1e-6) / 1e9
     # the single-launch path runs the whole layer in one kernel, so its average duration
     # is the timed region (events on the replay stream) / launches; the multi-launch path
     # is reported per layer (schedule + gate_up + down)
-    kernel = "fused_t1_kernel" if fused else "moe_layer_multi_launch"
+    kernel = "fused_layer_kernel" if fused else "moe_layer_multi_launch"
     roofline = {
         "bound": "hbm",
         "kernel": kernel,

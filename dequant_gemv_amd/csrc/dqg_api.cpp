@@ -184,7 +184,7 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
 int mfma_tiles(const MoeArgs& a) { return a.mfma_min > a.T ? 0 : 1; }
 
 bool use_fused(int T, int H, int I, int E, int k, int format) {
-  return T == 1 && E <= 512 && dqg::fused_supported(H, I, k) && !(format & DQG_PATH_NO_FUSED);
+  return E <= 512 && dqg::fused_supported_t(T, H, I, k) && !(format & DQG_PATH_NO_FUSED);
 }
 
 int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint8_t* wgu,
@@ -198,8 +198,8 @@ int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const ui
   f.ids_out = ids_out; f.w_out = w_out;
   char* b = static_cast<char*>(ws);
   f.err = reinterpret_cast<int*>(b + p.o_err);
-  dqg::fused_layout(f, b + p.o_fx, p.H, p.I, p.k);
-  return dqg::launch_fused_t1(f, st) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+  dqg::fused_layout(f, b + p.o_fx, p.H, p.I, p.k, p.T);
+  return dqg::launch_fused_layer(f, st) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }
 
 int run_moe(MoeArgs& a, const MoePlan& p, const float* logits, hipStream_t st) {

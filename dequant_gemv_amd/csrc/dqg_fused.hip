@@ -1,5 +1,5 @@
-// Single-launch packed-MoE layer for one token (T = 1): routing, fused gate_up, SiLU*up,
-// down projection and the top-k combine in one kernel.
+// Single-launch packed-MoE layer for up to FX_MAX_T = 4 tokens: routing, fused gate_up,
+// SiLU*up, down projection and the top-k combine in one kernel.
 //
 // FireEcho page, "The Goliath Kernel: Why It's Fast": one launch reads the expert ids from
 // device memory and indexes the contiguous packed buffer, with the dequant in registers
@@ -9,32 +9,37 @@
 // A whole T=1 layer moves only ~21 MB, so it is one launch whose workgroups read full
 // 128-byte lines and exchange data with as few round trips as possible.
 //
-// Every workgroup first routes the token itself (one wavefront, threshold + compaction +
-// rank selection; no other workgroup is waited for).
+// Slots s = t k + j (token t, rank j).  Every workgroup first routes its token itself (one
+// wavefront, threshold + compaction + rank selection; no other workgroup is waited for).
 // Workgroups (256 threads, 4 waves), every lane owning 16 columns x 8 byte rows:
-//   gate_up units (j, nt, ks): slot j, h columns [128 nt, 128 nt + 128) -- 128 bytes of
+//   gate_up units (s, nt, ks): slot s, h columns [128 nt, 128 nt + 128) -- 128 bytes of
 //     gate and 128 bytes of up per byte row (16 lanes) -- over byte rows
 //     [128 ks, 128 ks + 128) (16 row-lanes x 8 rows).  Each publishes its partial gate/up
-//     row and exits; gate_up units never wait.
+//     row and exits; gate_up units never wait.  (A slot is one unit set: an expert chosen by
+//     two tokens is read twice, mostly from cache the second time.)
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
-//     rows).  On layers with >= 1 MiB of gate_up weights, their weight loads wait for the
-//     first gate/up partial of their range (the gate_up loads, which are on the critical
-//     path, get the bandwidth first); then the
-//     threads gather the KS partial gate/up pairs of the unit's 512 h values (ascending
-//     ks), form h = SiLU(g)*u into LDS, and every lane scales its sum by its slot weight.  Units c < NC-1 publish a partial output
-//     row; unit c = NC-1 gathers them in ascending c, adds its own, the residual, and
-//     writes bf16 out.
+//     rows); for T > 1 a token's rows fill whole chunks.  On layers with >= 1 MiB of gate_up
+//     weights per token, their weight loads wait for the first gate/up partial of their
+//     range (the gate_up loads, which are on the critical path, get the bandwidth first);
+//     then the threads gather the KS partial gate/up pairs of the unit's 512 h values
+//     (ascending ks), form h = SiLU(g)*u into LDS, and every lane scales its sum by its slot
+//     weight.  A token's chunks publish partial output rows, except its last chunk of each
+//     column tile, which gathers them in ascending c, adds its own and the residual, and
+//     writes the token's bf16 output.
 // Publication protocol: exchange buffers hold the bit pattern 0 when empty and producers
 // never store 0 (+0.0 is stored as -0.0, which computes identically); consumers poll the
 // data itself with agent-coherent (sc1) loads, all of a gather's loads in flight at once.
 // Each buffer exists twice: a call uses copy p = bit 20 of a 32-bit call counter, to which
-// the n_mt finishing down units add shares summing to exactly 2^20 (so bit 20 flips once
+// the T x n_mt finishing down units add shares summing to exactly 2^20 (so bit 20 flips once
 // per call, also across wrap-around, and no unit of a call can see it flipped before every
-// unit has read it, since each finishing unit waits on all others); producers clear their
-// slots of copy 1-p, which the previous call used and the next call will use.  A
-// unit only waits on units with lower block ids, so in-order dispatch cannot deadlock;
-// waits are bounded and set bit 1 of the error word on timeout instead of hanging.
+// unit has read it, since each finishing unit waits on all others of its token, and those
+// on every gate_up unit of the token); producers clear their slots of copy 1-p, which the
+// previous call used and the next call will use.  Each token count T has its own counter
+// and buffers in the workspace, so that calls with different T never leave data in each
+// other's slots.  A unit only waits on units with lower block ids, so in-order dispatch
+// cannot deadlock; waits are bounded and set bit 1 of the error word on timeout instead of
+// hanging.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -176,7 +181,7 @@ __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n,
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   __shared__ int s_ids[32];
   __shared__ int s_key[32];
   __shared__ float s_w[32];
@@ -184,25 +189,36 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   __shared__ __align__(16) long long s_route[64 * 8 + 68];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
+  const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
+  const int bid = blockIdx.x;
+  // the token this workgroup works for: a gate_up unit's slot's, a down unit's chunk's
+  // (chunks never span tokens when T > 1)
+  const int tok = (a.T == 1) ? 0
+                  : (bid < a.n_a) ? (bid / KS / NT) / k
+                                  : ((bid - a.n_a) % NC) / a.chunks_per_token;
 
-  // ---- routing by one wavefront per workgroup (E <= 512); which one varies with the block
-  // id, so that the routing waves of the workgroups sharing a compute unit tend to land on
-  // different SIMDs.  Only the down units (and workgroup 0, for the optional outputs) need
-  // the weights; a gate_up unit only needs its slot's id. ----
+  // ---- routing of that token by one wavefront per workgroup (E <= 512); which one varies
+  // with the block id, so that the routing waves of the workgroups sharing a compute unit
+  // tend to land on different SIMDs.  Only the down units need the weights; a gate_up unit
+  // only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
+    const float* row = a.logits + (size_t)tok * a.E;
     if (a.E <= 128)
-      wave_topk_select<2>(a.logits, a.E, k, lane, s_route, s_ids, s_key);
+      wave_topk_select<2>(row, a.E, k, lane, s_route, s_ids, s_key);
     else
-      wave_topk_select<8>(a.logits, a.E, k, lane, s_route, s_ids, s_key);
-    if (blockIdx.x >= a.n_a || blockIdx.x == 0) {
+      wave_topk_select<8>(row, a.E, k, lane, s_route, s_ids, s_key);
+    if (bid >= a.n_a) {
       int sel_e;
       float sel_w;
       wave_topk_weights(s_ids, s_key, k, lane, &sel_e, &sel_w);
+      const int ub = bid - a.n_a;
+      // the token's last chunk of column tile 0 writes the optional routing outputs
+      const bool report = ub / NC == 0 && ub % NC == (tok + 1) * a.chunks_per_token - 1;
       if (lane < k) {
         s_w[lane] = sel_w;
-        if (blockIdx.x == 0 && a.ids_out) {
-          a.ids_out[lane] = sel_e;
-          a.w_out[lane] = sel_w;
+        if (report && a.ids_out) {
+          a.ids_out[tok * k + lane] = sel_e;
+          a.w_out[tok * k + lane] = sel_w;
         }
       }
     }
@@ -213,16 +229,15 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   // asm keeps the compiler from waiting for it earlier), so that its latency overlaps the
   // weight loads instead of delaying them.
   unsigned calls = __hip_atomic_load(a.calls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
-  const size_t gsz = (size_t)k * NT * KS * 256;     // one copy of the gate/up partial rows
+  const int S = a.T * k;                             // slots of the call
+  const size_t gsz = (size_t)S * NT * KS * 256;      // one copy of the gate/up partial rows
   const size_t psz = (size_t)a.n_mt * NC * 128;
 
-  const int bid = blockIdx.x;
   if (bid < a.n_a) {
-    // ================= gate_up unit (j, nt, ks) =================
+    // ================= gate_up unit (slot s = tok k + j, nt, ks) =================
     const int ks = bid % KS, grp = bid / KS;
-    const int j = grp / NT, nt = grp - j * NT;
-    const int e = s_ids[j];
+    const int s = grp / NT, nt = grp - s * NT;
+    const int e = s_ids[s - tok * k];
     const int rl = tid >> 4, ch = tid & 15;
     const size_t ld = 2 * (size_t)I;
     const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
@@ -233,7 +248,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
     float sf[16];
     scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((2 * r0) / a.group) * ld + col0, sf);
     uint32_t xr[FX_ROWS];
-    const float corr = load_x_rows<FMT>(a.x, r0, xr);
+    const float corr = load_x_rows<FMT>(a.x + (size_t)tok * H, r0, xr);
     // all loads above are issued before the first use (the scheduler would otherwise sink
     // some of them to their uses, which serializes memory round trips)
     __builtin_amdgcn_sched_barrier(0);
@@ -266,16 +281,17 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   const int col0 = 128 * mt + 16 * ch;
   const int R = c * FX_DROWS + FX_ROWS * rl;     // row in the concatenated slot list
   const int rows_per_slot = I / 2;
-  const bool active = R < k * rows_per_slot;
-  const int j = active ? R / rows_per_slot : 0;
-  const int r0 = active ? R - j * rows_per_slot : 0;
+  const bool active = R < S * rows_per_slot;
+  const int sl = active ? R / rows_per_slot : tok * k;  // slot of the row
+  const int j = sl - tok * k;                           // its rank within the token
+  const int r0 = active ? R - sl * rows_per_slot : 0;
   // The down weights are needed only once h is complete: on layers whose gate_up weights
   // take long enough to stream to matter (hold_down), hold their loads until the first
   // gate/up partial of this unit's range is published, so that the gate_up units, which are
   // on the critical path, have the memory bandwidth to themselves until then.
   if (a.hold_down) {
     const int f0 = 512 * c;
-    if (tid == 0 && f0 < k * I) {
+    if (tid == 0 && f0 < S * I) {
       const int jj = f0 / I, n = f0 - jj * I;
       const float* p = gpart + ((size_t)((jj * NT + (n >> 7)) * KS + KS - 1)) * 256 + (n & 127);
       for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
@@ -299,7 +315,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   {
     const int f = 512 * c + 2 * tid;
     float2 h2 = make_float2(0.0f, 0.0f);
-    if (f < k * I) {
+    if (f < S * I) {
       const int jj = f / I, n = f - jj * I, nt = n >> 7, nc = n & 127;
       const __amdgpu_buffer_rsrc_t gr = rsrc(gpart);
       const int base = (((jj * NT + nt) * KS) * 256 + nc) * 4;
@@ -372,28 +388,32 @@ __global__ void __launch_bounds__(FX_THREADS) fused_t1_kernel(FusedArgs a) {
   const float mine = wg_colsum<8, FX_THREADS>(acc, s_red, tid);
   if (tid >= 128) return;
   const int m = 128 * mt + tid;
+  const int NCt = a.chunks_per_token, c_first = tok * NCt;
   const size_t row0 = (size_t)mt * NC;
-  if (c != NC - 1) {
+  if (c != c_first + NCt - 1) {
     st_sc1(pbuf, (row0 + c) * 128 + tid, pub(mine));
     st_sc1(pold, (row0 + c) * 128 + tid, 0.0f);
     return;
   }
-  // last chunk of the tile: gather the earlier chunks' rows (all in flight), ascending c
+  // the token's last chunk of the tile: gather its earlier chunks' rows (all in flight),
+  // ascending c
   float y = 0.0f;
-  for (int c0 = 0; c0 < NC - 1; c0 += 16) {
-    const int n = min(16, NC - 1 - c0);
+  for (int c0 = 0; c0 < NCt - 1; c0 += 16) {
+    const int n = min(16, NCt - 1 - c0);
     float pv[16];
-    if (!gather_sc1(pbuf + (row0 + c0) * 128 + tid, 128, n, pv)) atomicOr(a.err, 2);
+    if (!gather_sc1(pbuf + (row0 + c_first + c0) * 128 + tid, 128, n, pv)) atomicOr(a.err, 2);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (i < n) y += pv[i];
   }
   y += mine;
-  if (a.res) y += bf16_to_f32(a.res[m]);
-  a.out[m] = f32_to_bf16(y);
-  if (tid == 0) {
-    const unsigned share = (1u << 20) / (unsigned)a.n_mt;
-    const unsigned add = (mt + 1 < a.n_mt) ? share : (1u << 20) - (unsigned)(a.n_mt - 1) * share;
+  const size_t o = (size_t)tok * H + m;
+  if (a.res) y += bf16_to_f32(a.res[o]);
+  a.out[o] = f32_to_bf16(y);
+  if (tid == 0) {  // the T x n_mt finishing units add shares summing to 2^20
+    const unsigned nf = (unsigned)(a.T * a.n_mt), fi = (unsigned)(tok * a.n_mt + mt);
+    const unsigned share = (1u << 20) / nf;
+    const unsigned add = (fi + 1 < nf) ? share : (1u << 20) - (nf - 1) * share;
     __hip_atomic_fetch_add(a.calls, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -402,36 +422,54 @@ bool fused_supported(int H, int I, int k) {
   return H % 256 == 0 && I % 128 == 0 && H / 2 / FX_KROWS <= FX_MAX_KS && k <= 32;
 }
 
-size_t fused_ws_bytes(int H, int I, int k) {
+// T > 1: a token's down rows must fill whole chunks, so that no chunk spans two tokens
+bool fused_supported_t(int T, int H, int I, int k) {
+  return fused_supported(H, I, k) && T >= 1 && T <= FX_MAX_T &&
+         (T == 1 || (k * (I / 2)) % FX_DROWS == 0);
+}
+
+// Workspace of the single-launch layer: one region per token count T (1 .. FX_MAX_T), each
+// with its call counter and its two copies of the exchange buffers.  Calls with different T
+// use different slots, so they must not share the buffers that are kept empty between calls.
+static size_t fused_region_bytes(int H, int I, int k, int T) {
   const int KS = H / 2 / FX_KROWS, NT = I / 128, n_mt = H / 128;
-  const int NC = (k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
+  const int NC = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
   size_t o = 256;                                         // call counter
-  o += 2 * (size_t)k * NT * KS * 256 * 4;                 // gate/up partial rows
+  o += 2 * (size_t)T * k * NT * KS * 256 * 4;             // gate/up partial rows
   o += 2 * (size_t)n_mt * NC * 128 * 4;                   // output partial rows
   return (o + 255) & ~(size_t)255;
 }
 
-void fused_layout(FusedArgs& f, void* ws, int H, int I, int k) {
+size_t fused_ws_bytes(int H, int I, int k) {
+  size_t o = 0;
+  for (int T = 1; T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, k, T);
+  return o;
+}
+
+void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T) {
   char* p = static_cast<char*>(ws);
+  for (int t = 1; t < T; ++t) p += fused_region_bytes(H, I, k, t);
+  f.T = T;
   f.ks = H / 2 / FX_KROWS;
   f.n_mt = H / 128;
-  f.n_chunks = (k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
-  f.n_a = k * (I / 128) * f.ks;
+  f.n_chunks = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
+  f.chunks_per_token = f.n_chunks / T;
+  f.n_a = T * k * (I / 128) * f.ks;
   f.n_b = f.n_mt * f.n_chunks;
   f.hold_down = (size_t)k * (H / 2) * (2 * (size_t)I) >= ((size_t)1 << 20);
   f.calls = reinterpret_cast<unsigned int*>(p);
   size_t o = 256;
   f.gpart = reinterpret_cast<float*>(p + o);
-  o += 2 * (size_t)k * (I / 128) * f.ks * 256 * 4;
+  o += 2 * (size_t)T * k * (I / 128) * f.ks * 256 * 4;
   f.ypart = reinterpret_cast<float*>(p + o);
 }
 
-hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st) {
+hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st) {
   const int grid = f.n_a + f.n_b;
   if (f.fmt == FMT_FP4)
-    hipLaunchKernelGGL(fused_t1_kernel<FMT_FP4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
+    hipLaunchKernelGGL(fused_layer_kernel<FMT_FP4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
   else
-    hipLaunchKernelGGL(fused_t1_kernel<FMT_INT4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
+    hipLaunchKernelGGL(fused_layer_kernel<FMT_INT4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
   return hipGetLastError();
 }
 

@@ -70,12 +70,15 @@ struct FusedArgs {
   unsigned int* calls;  // call counter: every call adds 2^20 in total (parity source)
   int* err;
   int n_a, n_b, n_chunks, ks, n_mt;
+  int T, chunks_per_token;  // tokens (1 .. FX_MAX_T) and down chunks per token
   int hold_down;        // down units load their weights only once gate/up results appear
 };
+constexpr int FX_MAX_T = 4;  // tokens of the single-launch layer, at most
 bool fused_supported(int H, int I, int k);
+bool fused_supported_t(int T, int H, int I, int k);
 size_t fused_ws_bytes(int H, int I, int k);
-void fused_layout(FusedArgs& f, void* ws, int H, int I, int k);
-hipError_t launch_fused_t1(const FusedArgs& f, hipStream_t st);
+void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T);
+hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st);
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
                        hipStream_t st);

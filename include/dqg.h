@@ -59,7 +59,7 @@ typedef enum dqg_format {
 /* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
  * default, 0, picks the path from the shapes).  FORCE_GEMV runs every expert on the
  * vector-ALU tiles, FORCE_MFMA runs every expert with at least one token on the bf16
- * matrix-core tiles, NO_FUSED disables the single-launch T=1 layer. */
+ * matrix-core tiles, NO_FUSED disables the single-launch layer (T <= 4). */
 #define DQG_PATH_FORCE_GEMV 0x100
 #define DQG_PATH_FORCE_MFMA 0x200
 #define DQG_PATH_NO_FUSED 0x400
@@ -121,8 +121,8 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
  * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch per
  * projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16 (FP4)
- * or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch T = 1 layer
- * (moe_fp4_layer).
+ * or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch layer
+ * (moe_fp4_layer, T <= 4).
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
  * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
@@ -137,9 +137,12 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
 
 /*
  * moe_fp4_layer -- topk_route followed by moe_fp4_ffn in one call (routing computed on
- * the device from `logits` fp32 [T, E]; same rules as topk_route).  For T == 1 the
- * whole layer runs as a single kernel launch.  ids_out (int32 [T, k]) and weights_out
- * (fp32 [T, k]) are optional outputs of the routing (NULL to skip).
+ * the device from `logits` fp32 [T, E]; same rules as topk_route).  For T <= 4 the
+ * whole layer runs as a single kernel launch when E <= 512, H % 256 == 0, H <= 2048,
+ * I % 128 == 0 and (for T > 1) k * I / 2 is a multiple of 256; every slot then streams its
+ * expert itself (an expert chosen by several tokens is read once per token).  Other calls
+ * route inside the schedule of the multi-launch path.  ids_out (int32 [T, k]) and
+ * weights_out (fp32 [T, k]) are optional outputs of the routing (NULL to skip).
  */
 int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
                   const uint8_t* w_gate_up, const uint16_t* s_gate_up, const uint8_t* w_down,

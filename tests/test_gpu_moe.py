@@ -363,3 +363,48 @@ def test_fused_layer_routing_edge_cases(E, k, dist):
     np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
     want, _, _ = _oracle_layer(cfg, L)
     check_bf16(out, want, what=f"route E={E} k={k} {dist}")
+
+
+# ---- single-launch layer for T = 1 .. 4 ---------------------------------------------------
+FUSED_T_CASES = [("q30", S.Q30_BATCH, 2), ("q30", S.Q30_BATCH, 3), ("q30", S.Q30_BATCH, 4),
+                 ("w512", S.replace(S.W512, layers=1), 2), ("w512", S.replace(S.W512, layers=1), 4)]
+
+
+@pytest.mark.parametrize("name,cfg,T", FUSED_T_CASES, ids=[f"{c[0]}-T{c[2]}" for c in FUSED_T_CASES])
+def test_fused_layer_small_batch(name, cfg, T):
+    """T = 2 .. 4 through the single-launch layer (one unit set per slot; a token's down
+    chunks combine into its output row): ids bit-exact, weights and output against the oracle,
+    with a residual, and equal to the multi-launch path within the tolerance."""
+    B = _b()
+    cfg = cfg.with_T(T)
+    L, D = _layer(cfg, seed=5 + T)
+    res = S.f32_to_bf16_bits(np.random.default_rng(T).standard_normal((T, cfg.H)))
+    out, ids, w = _run_layer(cfg, L, D, residual=dev(res).view(torch.bfloat16))
+    want, oids, ow = _oracle_layer(cfg, L, residual_bits=res)
+    assert np.array_equal(ids, oids), "expert selection must match bit-exactly"
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    check_bf16(out, want, what=f"{name} fused T={T}")
+    multi, _, _ = _run_layer(cfg, L, D, flags=B.PATH_NO_FUSED,
+                             residual=dev(res).view(torch.bfloat16))
+    check_bf16(multi, want, what=f"{name} multi-launch T={T}")
+
+
+def test_fused_layer_calls_with_changing_T_share_a_workspace():
+    """Single-launch calls with T = 1, 4, 2, 4, 3, 1, 2 on one workspace (each T keeps its own
+    exchange buffers, which stay empty between its calls): every call meets the oracle."""
+    B = _b()
+    cfg = S.Q30_BATCH
+    ws = B.moe_workspace(4, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    layers = {}
+    for T in (1, 2, 3, 4):
+        c = cfg.with_T(T)
+        L = S.make_moe_layer(c, seed=40 + T)
+        D = upload_layer(L)
+        layers[T] = (c, L, D, _oracle_layer(c, L)[0])
+    for it, T in enumerate((1, 4, 2, 4, 3, 1, 2, 4)):
+        c, L, D, want = layers[T]
+        out = B.moe_fp4_layer(dev(L.x), dev(L.logits), c.k, D["w_gu"], D["s_gu"], D["w_d"],
+                              D["s_d"], c.group, c.fmt, workspace=ws)
+        torch.cuda.synchronize()
+        check_bf16(bits16(out), want, what=f"call {it} T={T}")
+    assert int(ws[:4].view(torch.int32).item()) == 0
