@@ -408,3 +408,15 @@ def test_fused_layer_calls_with_changing_T_share_a_workspace():
         torch.cuda.synchronize()
         check_bf16(bits16(out), want, what=f"call {it} T={T}")
     assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_fused_layer_int4_q30_shape(T):
+    """INT4 weights (group 32) through the single-launch layer at the 128-expert shape:
+    the fp16 activation pairs and the per-row bias correction, T = 1, 2, 4."""
+    cfg = S.replace(S.Q30_BATCH, fmt=S.FMT_INT4, scale_lo=0.002, scale_hi=0.01).with_T(T)
+    L, D = _layer(cfg, seed=60 + T)
+    out, ids, w = _run_layer(cfg, L, D)
+    want, oids, ow = _oracle_layer(cfg, L)
+    assert np.array_equal(ids, oids)
+    check_bf16(out, want, what=f"int4 q30 T={T}")
