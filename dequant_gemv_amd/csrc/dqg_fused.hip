@@ -13,9 +13,9 @@
 // wavefront, threshold + compaction + rank selection; no other workgroup is waited for).
 // Workgroups (256 threads, 4 waves), every lane owning 16 columns x 8 byte rows:
 //   gate_up units (s, nt, ks): slot s, h columns [128 nt, 128 nt + 128) -- 128 bytes of
-//     gate and 128 bytes of up per byte row (16 lanes) -- over byte rows
-//     [128 ks, 128 ks + 128) (16 row-lanes x 8 rows).  Each publishes its partial gate/up
-//     row and exits; gate_up units never wait.  (A slot is one unit set: an expert chosen by
+//     gate and 128 bytes of up per byte row (16 lanes) -- over 16 GUR byte rows from
+//     16 GUR ks on (16 row-lanes x GUR rows; GUR = 8 for one token, 16 for several).  Each
+//     publishes its partial gate/up row and exits; gate_up units never wait.  (A slot is one unit set: an expert chosen by
 //     two tokens is read twice, mostly from cache the second time.)
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
@@ -62,16 +62,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-constexpr int FX_ROWS = 8;        // byte rows per lane
-constexpr int FX_KROWS = 128;     // gate_up byte rows per unit (16 row-lanes x 8)
-constexpr int FX_DROWS = 256;     // down byte rows per unit (32 row-lanes x 8)
-constexpr int FX_MAX_KS = 8;      // gate_up K splits (H <= 2048 on this path)
+// A gate_up unit covers 16 row-lanes x GUR byte rows; GUR = 8 for one token and 16 for
+// several, where there are T times more slots and fewer, larger units keep all of them
+// resident (measured at the 128-expert shape: T = 4 is 12 % faster with 16, T = 1 the same).
+constexpr int FX_D_ROWS = 8;                    // byte rows per lane, down unit
+constexpr int FX_DROWS = 32 * FX_D_ROWS;        // down byte rows per unit (32 row-lanes)
+constexpr int fx_krows(int gur) { return 16 * gur; }
+constexpr int fx_max_ks(int gur) { return 2048 / 2 / fx_krows(gur); }  // H <= 2048
+static inline int fx_gu_rows(int H, int T) { return (T > 1 && (H / 2) % fx_krows(16) == 0) ? 16 : 8; }
 
-template <int FMT>
-__device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[FX_ROWS],
-                                           const uint32_t (&xr)[FX_ROWS], float (&acc)[16]) {
+template <int FMT, int ROWS>
+__device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[ROWS], const uint32_t (&xr)[ROWS],
+                                           float (&acc)[16]) {
 #pragma unroll
-  for (int r = 0; r < FX_ROWS; ++r) {
+  for (int r = 0; r < ROWS; ++r) {
     const uint32_t d[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
     if constexpr (FMT == FMT_FP4) {
       const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xr[r]);
@@ -95,11 +99,11 @@ __device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[FX_ROWS],
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[FX_ROWS],
-                                             const float (&hf)[2 * FX_ROWS], float (&acc)[16]) {
+template <int FMT, int ROWS>
+__device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[ROWS], const float (&hf)[2 * ROWS],
+                                             float (&acc)[16]) {
 #pragma unroll
-  for (int r = 0; r < FX_ROWS; ++r) {
+  for (int r = 0; r < ROWS; ++r) {
     const uint32_t d[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
     const float x0 = hf[2 * r], x1 = hf[2 * r + 1];
 #pragma unroll
@@ -127,9 +131,10 @@ __device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[FX_ROWS],
   }
 }
 
-__device__ __forceinline__ void load_rows(const uint8_t* wp, size_t ld, uint4 (&wv)[FX_ROWS]) {
+template <int ROWS>
+__device__ __forceinline__ void load_rows(const uint8_t* wp, size_t ld, uint4 (&wv)[ROWS]) {
 #pragma unroll
-  for (int r = 0; r < FX_ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
+  for (int r = 0; r < ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
 }
 
 __device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16]) {
@@ -143,17 +148,20 @@ __device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16]) {
   }
 }
 
-// x pairs of byte rows r0 .. r0+7 (+ the INT4 bias correction of those rows)
-template <int FMT>
-__device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t (&xr)[FX_ROWS]) {
+// x pairs of byte rows r0 .. r0+ROWS-1 (+ the INT4 bias correction of those rows)
+template <int FMT, int ROWS>
+__device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t (&xr)[ROWS]) {
+  static_assert(ROWS % 4 == 0, "x pairs are loaded 4 at a time");
   const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(x) + r0);
-  const uint4 v0 = xp[0], v1 = xp[1];
-  xr[0] = v0.x; xr[1] = v0.y; xr[2] = v0.z; xr[3] = v0.w;
-  xr[4] = v1.x; xr[5] = v1.y; xr[6] = v1.z; xr[7] = v1.w;
+#pragma unroll
+  for (int i = 0; i < ROWS / 4; ++i) {
+    const uint4 v = xp[i];
+    xr[4 * i] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
+  }
   float corr = 0.0f;
   if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-    for (int r = 0; r < FX_ROWS; ++r) {
+    for (int r = 0; r < ROWS; ++r) {
       const f16x2_t h = {(_Float16)bf16_lo(xr[r]), (_Float16)bf16_hi(xr[r])};
       xr[r] = __builtin_bit_cast(uint32_t, h);
       corr = fmaf(-INT4_F16_BIAS_LO, (float)h.x, corr);
@@ -163,16 +171,17 @@ __device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t
   return corr;
 }
 
-// Poll n (<= 16) published floats p[i * stride] until none is the empty pattern; all loads
-// of one round are in flight together.  Returns false on timeout.
+// Poll n (<= FX_GATHER) published floats p[i * stride] until none is the empty pattern; all
+// loads of one round are in flight together.  Returns false on timeout.
+constexpr int FX_GATHER = 32;
 __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n, float* v) {
   for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
     bool ready = true;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < FX_GATHER; ++i)
       if (i < n) v[i] = ld_sc1(p, (size_t)i * stride);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < FX_GATHER; ++i)
       if (i < n) ready = ready && (__float_as_uint(v[i]) != 0u);
     if (ready) return true;
     __builtin_amdgcn_s_sleep(1);
@@ -180,8 +189,9 @@ __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n,
   return false;
 }
 
-template <int FMT>
+template <int FMT, int GUR>
 __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
+  constexpr int KROWS = fx_krows(GUR), MAX_KS = fx_max_ks(GUR);
   __shared__ int s_ids[32];
   __shared__ int s_key[32];
   __shared__ float s_w[32];
@@ -241,21 +251,21 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const int rl = tid >> 4, ch = tid & 15;
     const size_t ld = 2 * (size_t)I;
     const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
-    const int r0 = ks * FX_KROWS + FX_ROWS * rl;
+    const int r0 = ks * KROWS + GUR * rl;
     const uint8_t* w = a.wgu + (size_t)e * (H / 2) * ld;
-    uint4 wvv[FX_ROWS];
+    uint4 wvv[GUR];
     load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
     float sf[16];
     scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((2 * r0) / a.group) * ld + col0, sf);
-    uint32_t xr[FX_ROWS];
-    const float corr = load_x_rows<FMT>(a.x + (size_t)tok * H, r0, xr);
+    uint32_t xr[GUR];
+    const float corr = load_x_rows<FMT, GUR>(a.x + (size_t)tok * H, r0, xr);
     // all loads above are issued before the first use (the scheduler would otherwise sink
     // some of them to their uses, which serializes memory round trips)
     __builtin_amdgcn_sched_barrier(0);
     float accb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
-    rows_dot_x<FMT>(wvv, xr, accb);
+    rows_dot_x<FMT, GUR>(wvv, xr, accb);
     // reduce the 16 row-lanes; thread i then owns partial column i (i < 128 gate, else up)
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = sf[c] * (accb[c] + corr);
@@ -279,7 +289,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   const int mt = ub / NC, c = ub - mt * NC;
   const int rl = tid >> 3, ch = tid & 7;
   const int col0 = 128 * mt + 16 * ch;
-  const int R = c * FX_DROWS + FX_ROWS * rl;     // row in the concatenated slot list
+  const int R = c * FX_DROWS + FX_D_ROWS * rl;   // row in the concatenated slot list
   const int rows_per_slot = I / 2;
   const bool active = R < S * rows_per_slot;
   const int sl = active ? R / rows_per_slot : tok * k;  // slot of the row
@@ -290,7 +300,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // gate/up partial of this unit's range is published, so that the gate_up units, which are
   // on the critical path, have the memory bandwidth to themselves until then.
   if (a.hold_down) {
-    const int f0 = 512 * c;
+    const int f0 = 2 * FX_DROWS * c;
     if (tid == 0 && f0 < S * I) {
       const int jj = f0 / I, n = f0 - jj * I;
       const float* p = gpart + ((size_t)((jj * NT + (n >> 7)) * KS + KS - 1)) * 256 + (n & 127);
@@ -301,19 +311,19 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     __syncthreads();
   }
-  uint4 wvv[FX_ROWS];
+  uint4 wvv[FX_D_ROWS];
   float sf[16];
   if (active) {
     const int e = s_ids[j];
     load_rows(a.wd + (size_t)e * rows_per_slot * H + (size_t)r0 * H + col0, H, wvv);
     scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((2 * r0) / a.group) * H + col0, sf);
   }
-  // gather h for this unit's rows: flat h index f = 2 R covers [512 c, 512 c + 512); thread
-  // t owns f = 512 c + 2t, +1 (two columns of one slot); the KS partial gate and up pairs
-  // are polled together and summed in ascending ks
-  float* hl = s_red;  // 512 floats, reused as the reduction buffer afterwards
-  {
-    const int f = 512 * c + 2 * tid;
+  // gather h for this unit's rows: flat h index f = 2 R covers 2 FX_DROWS values from
+  // 2 FX_DROWS c on; thread t < FX_DROWS owns f = 2 FX_DROWS c + 2t, +1 (two columns of one
+  // slot); the KS partial gate and up pairs are polled together and summed in ascending ks
+  float* hl = s_red;  // 2 FX_DROWS floats, reused as the reduction buffer afterwards
+  if (tid < FX_DROWS) {
+    const int f = 2 * FX_DROWS * c + 2 * tid;
     float2 h2 = make_float2(0.0f, 0.0f);
     if (f < S * I) {
       const int jj = f / I, n = f - jj * I, nt = n >> 7, nc = n & 127;
@@ -322,9 +332,9 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
       f32x2_t g2 = {0.0f, 0.0f}, u2 = {0.0f, 0.0f};
       bool ok = false;
       for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
-        f32x2_t gv[FX_MAX_KS], uv[FX_MAX_KS];
+        f32x2_t gv[MAX_KS], uv[MAX_KS];
 #pragma unroll
-        for (int q = 0; q < FX_MAX_KS; ++q) {
+        for (int q = 0; q < MAX_KS; ++q) {
           if (q < KS) {
             gv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024, 0, CPOL_SC1);
             uv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024 + 512, 0, CPOL_SC1);
@@ -332,7 +342,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
         }
         bool ready = true;
 #pragma unroll
-        for (int q = 0; q < FX_MAX_KS; ++q)
+        for (int q = 0; q < MAX_KS; ++q)
           if (q < KS)
             ready = ready && __float_as_uint(gv[q].x) && __float_as_uint(gv[q].y) &&
                     __float_as_uint(uv[q].x) && __float_as_uint(uv[q].y);
@@ -340,7 +350,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
           g2 = gv[0];
           u2 = uv[0];
 #pragma unroll
-          for (int q = 1; q < FX_MAX_KS; ++q)
+          for (int q = 1; q < MAX_KS; ++q)
             if (q < KS) {
               g2 += gv[q];
               u2 += uv[q];
@@ -360,10 +370,10 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
   if (active) {
-    float hf[2 * FX_ROWS];
+    float hf[2 * FX_D_ROWS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 v = reinterpret_cast<const float4*>(hl)[4 * rl + i];
+    for (int i = 0; i < FX_D_ROWS / 2; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(hl)[(FX_D_ROWS / 2) * rl + i];
       hf[4 * i + 0] = v.x;
       hf[4 * i + 1] = v.y;
       hf[4 * i + 2] = v.z;
@@ -372,13 +382,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     float corr = 0.0f;
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-      for (int i = 0; i < 2 * FX_ROWS; ++i) corr += hf[i];
+      for (int i = 0; i < 2 * FX_D_ROWS; ++i) corr += hf[i];
       corr *= -8.0f;
     }
     float accb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) accb[q] = 0.0f;
-    rows_dot_f32<FMT>(wvv, hf, accb);
+    rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
     const float wj = s_w[j];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = wj * (sf[q] * (accb[q] + corr));
@@ -398,12 +408,12 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // the token's last chunk of the tile: gather its earlier chunks' rows (all in flight),
   // ascending c
   float y = 0.0f;
-  for (int c0 = 0; c0 < NCt - 1; c0 += 16) {
-    const int n = min(16, NCt - 1 - c0);
-    float pv[16];
+  for (int c0 = 0; c0 < NCt - 1; c0 += FX_GATHER) {
+    const int n = min(FX_GATHER, NCt - 1 - c0);
+    float pv[FX_GATHER];
     if (!gather_sc1(pbuf + (row0 + c_first + c0) * 128 + tid, 128, n, pv)) atomicOr(a.err, 2);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < FX_GATHER; ++i)
       if (i < n) y += pv[i];
   }
   y += mine;
@@ -419,7 +429,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
 }
 
 bool fused_supported(int H, int I, int k) {
-  return H % 256 == 0 && I % 128 == 0 && H / 2 / FX_KROWS <= FX_MAX_KS && k <= 32;
+  return H % 256 == 0 && H <= 2048 && I % 128 == 0 && k <= 32;
 }
 
 // T > 1: a token's down rows must fill whole chunks, so that no chunk spans two tokens
@@ -432,7 +442,7 @@ bool fused_supported_t(int T, int H, int I, int k) {
 // with its call counter and its two copies of the exchange buffers.  Calls with different T
 // use different slots, so they must not share the buffers that are kept empty between calls.
 static size_t fused_region_bytes(int H, int I, int k, int T) {
-  const int KS = H / 2 / FX_KROWS, NT = I / 128, n_mt = H / 128;
+  const int KS = H / 2 / fx_krows(fx_gu_rows(H, T)), NT = I / 128, n_mt = H / 128;
   const int NC = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
   size_t o = 256;                                         // call counter
   o += 2 * (size_t)T * k * NT * KS * 256 * 4;             // gate/up partial rows
@@ -450,7 +460,7 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T) {
   char* p = static_cast<char*>(ws);
   for (int t = 1; t < T; ++t) p += fused_region_bytes(H, I, k, t);
   f.T = T;
-  f.ks = H / 2 / FX_KROWS;
+  f.ks = H / 2 / fx_krows(fx_gu_rows(H, T));
   f.n_mt = H / 128;
   f.n_chunks = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
   f.chunks_per_token = f.n_chunks / T;
@@ -466,10 +476,18 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T) {
 
 hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st) {
   const int grid = f.n_a + f.n_b;
-  if (f.fmt == FMT_FP4)
-    hipLaunchKernelGGL(fused_layer_kernel<FMT_FP4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
-  else
-    hipLaunchKernelGGL(fused_layer_kernel<FMT_INT4>, dim3(grid), dim3(FX_THREADS), 0, st, f);
+  const bool big = fx_gu_rows(f.H, f.T) == 16;
+  if (f.fmt == FMT_FP4) {
+    if (big)
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 16>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+    else
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+  } else {
+    if (big)
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 16>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+    else
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+  }
   return hipGetLastError();
 }
 
