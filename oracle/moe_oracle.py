@@ -30,6 +30,11 @@ What each function follows (page titles as printed at the head of each page):
 * dense GEMV -- FastInfer, "Specialized matrix-vector result" (a vector times a stored
   weight matrix, FP32-or-better products and reductions); the weight is the packed INT4
   ``[K/2, N]`` layout above with group 128.
+* router logits from the hidden state -- FireEcho, "Architecture": the MoE FFN is a packed
+  MoE with fused dispatch.  The pages do not spell out the router; it is read as the
+  plain linear router of an MoE layer, ``logits = x W_r`` with a bf16 ``W_r [H, E]`` and no
+  bias, and the selection is made on those logits (here in float64) by the top-k rule
+  above.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against hand-worked decode
 tables, closed forms, library special cases, invariants and exact-rational brute force.
@@ -121,11 +126,13 @@ def dequant(packed: np.ndarray, scale_bits: np.ndarray, group: int, fmt: int,
 # ------------------------------------------------------------------------------------
 # routing
 # ------------------------------------------------------------------------------------
-def topk_route(logits: np.ndarray, k: int):
+def topk_route(logits: np.ndarray, k: int, dtype=np.float32):
     """Per token: the k largest raw logits (ties to the lower expert index; -0.0 and +0.0
-    tie), in rank order, and weights = softmax over those k logits.
+    tie), in rank order, and weights = softmax over those k logits.  The logits are taken
+    in ``dtype``: float32 for logits handed to the library as fp32, float64 for logits the
+    oracle computes itself from the hidden state.
     Returns ``(ids int32 [T, k], weights float64 [T, k])``."""
-    lg = np.asarray(logits, dtype=np.float32)
+    lg = np.asarray(logits, dtype=dtype)
     T, E = lg.shape
     if not (1 <= k <= E):
         raise ValueError("need 1 <= k <= E")
@@ -210,6 +217,23 @@ def moe_layer(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: int
     ids, w = topk_route(logits, k)
     out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache)
     return out, ids, w
+
+
+def router_logits(x_bits, wr_bits) -> np.ndarray:
+    """logits[t, e] = sum_c x[t, c] * W_r[c, e] over the bf16 hidden state ``x [T, H]`` and
+    the bf16 router weight ``W_r [H, E]`` (uint16 bit patterns), in float64.
+    Returns ``float64 [T, E]``."""
+    return bf16_to_f64(x_bits) @ bf16_to_f64(wr_bits)
+
+
+def moe_layer_from_hidden(x_bits, wr_bits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
+                          residual_bits=None, cache: Optional[ExpertCache] = None):
+    """The router on the hidden state, top-k on its float64 logits, then the expert FFN
+    and the weighted combine.  Returns ``(out float64 [T, H], ids, weights, logits)``."""
+    logits = router_logits(x_bits, wr_bits)
+    ids, w = topk_route(logits, k, dtype=np.float64)
+    out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache)
+    return out, ids, w, logits
 
 
 def moe_stack(x_bits, layers: Sequence, k: int, group: int, fmt: int):

@@ -92,6 +92,17 @@ def moe_exact(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: str
     return out, all_ids, all_w
 
 
+def router_exact(x_bits, wr_bits):
+    """logits[t][e] = sum_c x[t][c] W_r[c][e] over bf16 bit patterns, exact, then float."""
+    H, E = len(wr_bits), len(wr_bits[0])
+    W = [[bf16_fraction(wr_bits[c][e]) for e in range(E)] for c in range(H)]
+    out = []
+    for xr in x_bits:
+        x = [bf16_fraction(v) for v in xr]
+        out.append([float(sum(x[c] * W[c][e] for c in range(H))) for e in range(E)])
+    return out
+
+
 def gemv_exact(x_bits, packed, scales, group: int, fmt: str = "int4"):
     W = dequant_exact(packed, scales, group, fmt)
     K, N = len(W), len(W[0])

@@ -256,6 +256,74 @@ def test_moe_matches_exact_bruteforce(seed):
     assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
 
 
+# --------------------------------------------------------------------------------------
+# router logits from the hidden state
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_router_logits_match_exact_bruteforce(seed):
+    rng = np.random.default_rng(300 + seed)
+    T, H, E = int(rng.integers(1, 4)), int(rng.choice([8, 16, 24])), int(rng.choice([4, 8]))
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H)))
+    wr = S.f32_to_bf16_bits(rng.normal(0.0, 0.3, size=(H, E)))
+    got = O.router_logits(x, wr)
+    want = np.array(BF.router_exact(x.tolist(), wr.tolist()))
+    mag = np.abs(S.bf16_bits_view_f32(x).astype(np.float64)) @ \
+        np.abs(S.bf16_bits_view_f32(wr).astype(np.float64))
+    assert got.shape == (T, E)
+    assert np.all(np.abs(got - want) <= 1e-15 * mag + 1e-300)
+
+
+def test_router_one_hot_hidden_state_picks_a_weight_row():
+    H, E = 64, 16
+    wr = S.make_router_weights(H, E, seed=3)
+    Wr = S.bf16_bits_view_f32(wr).astype(np.float64)
+    for c in (0, 1, 31, 63):
+        x = np.zeros((1, H), np.float32)
+        x[0, c] = 1.0
+        got = O.router_logits(S.f32_to_bf16_bits(x), wr)
+        assert np.array_equal(got[0], Wr[c])
+    # a column sum: x of all ones
+    got = O.router_logits(S.f32_to_bf16_bits(np.ones((1, H), np.float32)), wr)
+    np.testing.assert_allclose(got[0], Wr.sum(axis=0), rtol=1e-14, atol=1e-15)
+
+
+def test_route_in_float64_separates_values_tied_in_float32():
+    lg = np.array([[1.0, 1.0 + 2.0 ** -30, 0.5]])
+    ids32, _ = O.topk_route(lg, 2)
+    ids64, w64 = O.topk_route(lg, 2, dtype=np.float64)
+    assert ids32.tolist() == [[0, 1]]          # both round to 1.0f: the lower index first
+    assert ids64.tolist() == [[1, 0]]
+    np.testing.assert_allclose(w64[0], scipy.special.softmax(lg[0, [1, 0]]), rtol=1e-15)
+
+
+def test_router_weights_recipe_gives_unit_spread_logits():
+    H, E = 2048, 128
+    wr = S.make_router_weights(H, E, seed=0)
+    Wr = S.bf16_bits_view_f32(wr).astype(np.float64)
+    assert abs(Wr.std() * np.sqrt(H) - 1.0) < 0.01
+    x = S.f32_to_bf16_bits(np.random.default_rng(0).standard_normal((8, H)))
+    lg = O.router_logits(x, wr)
+    assert 0.9 < lg.std() < 1.1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_layer_from_hidden_matches_exact_bruteforce(seed):
+    rng = np.random.default_rng(400 + seed)
+    T, E, k, G, H, I = int(rng.integers(1, 4)), 4, int(rng.integers(1, 4)), 4, 16, 8
+    fmt = O.FMT_INT4 if seed % 2 == 0 else O.FMT_FP4
+    key = "int4" if fmt == O.FMT_INT4 else "fp4"
+    x, _, w_gu, s_gu, w_d, s_d = _tiny_random(rng, T, E, H, I, G, key)
+    wr = S.f32_to_bf16_bits(rng.normal(0.0, 0.5, size=(H, E)))
+    out, ids, w, lg = O.moe_layer_from_hidden(x, wr, k, w_gu, s_gu, w_d, s_d, G, fmt)
+    blg = BF.router_exact(x.tolist(), wr.tolist())
+    bout, bids, bw = BF.moe_exact(x.tolist(), blg, k, w_gu.tolist(), s_gu.tolist(),
+                                  w_d.tolist(), s_d.tolist(), G, key)
+    assert ids.tolist() == bids
+    np.testing.assert_allclose(w, bw, rtol=1e-13)
+    scale = max(1e-300, float(np.sqrt(np.mean(np.square(bout)))))
+    assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
+
+
 def test_expert_permutation_invariance():
     cfg = S.TINY
     L = S.make_moe_layer(cfg, seed=7)

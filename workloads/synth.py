@@ -238,6 +238,15 @@ def make_routing(rng: np.random.Generator, T: int, E: int, k: int):
     return ids, w
 
 
+def make_router_weights(H: int, E: int, seed: int = 0, layer: int = 0) -> np.ndarray:
+    """A bf16 router weight ``W_r [H, E]`` (uint16 bits) drawn i.i.d. N(0, 1/sqrt(H)) from its
+    own stream ``default_rng([seed, layer, 0x52])`` (the layer draws are unchanged), so that
+    an N(0, 1) hidden state gives logits of about unit spread, like the logits the other
+    workloads draw directly."""
+    rng = np.random.default_rng([seed, layer, 0x52])
+    return f32_to_bf16_bits(rng.normal(0.0, 1.0 / np.sqrt(H), size=(H, E)))
+
+
 def moe_layer_logits(cfg: MoEConfig, seed: int = 0, layer: int = 0) -> np.ndarray:
     """The logits make_moe_layer(cfg, seed, layer) draws, without drawing the experts."""
     s = seed if cfg.layers == 1 else 1000 * seed + layer
