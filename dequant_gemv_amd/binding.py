@@ -42,6 +42,10 @@ SIGNATURES = {
                          _P]),
     "moe_fp4_layer": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P,
                            _Z, _P]),
+    "router_logits_workspace_bytes": (_Z, [_I, _I, _I]),
+    "router_logits": (_I, [_P, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "moe_fp4_layer_from_hidden": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P,
+                                       _P, _P, _P, _P, _Z, _P]),
     "packed_gemv_int4_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
@@ -188,6 +192,57 @@ def moe_fp4_layer(x, logits, k: int, w_gate_up, s_gate_up, w_down, s_down, group
         _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down),
         _ptr(s_down), group, fmt | flags, _ptr(residual), _ptr(out), _ptr(ids_out),
         _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+def router_logits_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(LIB.router_logits_workspace_bytes(T, H, E))
+
+
+def router_logits(x, w_router, logits=None, workspace=None) -> torch.Tensor:
+    T, H = x.shape
+    E = w_router.shape[1]
+    _need(x, "x", 2)
+    _need(w_router, "w_router", 2, (H, E), x.device)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _need(logits, "logits", 4, (T, E), x.device)
+    if workspace is None:
+        n = router_logits_workspace_bytes(T, H, E)
+        if n == 0:
+            raise ValueError("unsupported router sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", 1, None, x.device)
+    _check("router_logits", LIB.router_logits(
+        _ptr(x), T, H, E, _ptr(w_router), _ptr(logits), _ptr(workspace), workspace.numel(),
+        _stream(x)))
+    return logits
+
+
+def moe_fp4_layer_from_hidden(x, w_router, k: int, w_gate_up, s_gate_up, w_down, s_down,
+                              group: int, fmt: int, residual=None, out=None, logits_out=None,
+                              ids_out=None, weights_out=None, workspace=None,
+                              flags: int = 0) -> torch.Tensor:
+    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group)
+    _need(w_router, "w_router", 2, (H, E), x.device)
+    if residual is not None:
+        _need(residual, "residual", 2, (T, H), x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", 2, (T, H), x.device)
+    if logits_out is not None:
+        _need(logits_out, "logits_out", 4, (T, E), x.device)
+    if ids_out is not None:
+        _need(ids_out, "ids_out", 4, (T, k), x.device)
+    if weights_out is not None:
+        _need(weights_out, "weights_out", 4, (T, k), x.device)
+    if workspace is None:
+        workspace = moe_workspace(T, H, I, E, k, x.device)
+    _need(workspace, "workspace", 1, None, x.device)
+    _check("moe_fp4_layer_from_hidden", LIB.moe_fp4_layer_from_hidden(
+        _ptr(x), _ptr(w_router), T, H, I, E, k, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down),
+        _ptr(s_down), group, fmt | flags, _ptr(residual), _ptr(out), _ptr(logits_out),
+        _ptr(ids_out), _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(x)))
     return out
 
 

@@ -32,7 +32,8 @@ struct MoePlan {
   int T, H, I, E, k, TK, A;
   int tiles_gu, tiles_dn, S_gu, S_dn;
   int t_cap, sgu_max, sdn_max;
-  size_t o_err, o_fx, o_nact, o_rec, o_slots, o_nvalid, o_ids, o_wts, o_h, o_pgu, o_pdn, total;
+  size_t o_err, o_fx, o_nact, o_rec, o_slots, o_nvalid, o_ids, o_wts, o_h, o_pgu, o_pdn;
+  size_t o_rtp, o_rtl, total;  // router partials [splits][t_cap][E] and logits [t_cap][E]
   bool ok;  // partial buffers addressable with 32-bit byte offsets
 };
 
@@ -81,7 +82,7 @@ void moe_layout(MoePlan& p, int t_cap) {
   p.sdn_max = moe_split_max(I / 32, 8, kMaxSplitDown, tkc, 4LL * H);
   size_t o = 0;
   p.o_err = o;     o += 256;
-  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, k) : 0));
+  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, p.E, k) : 0));
   p.o_nact = o;    o += 256;
   p.o_rec = o;     o = up256(o + 16 * (size_t)a_cap);
   p.o_slots = o;   o = up256(o + sizeof(int) * tkc);
@@ -91,6 +92,8 @@ void moe_layout(MoePlan& p, int t_cap) {
   p.o_h = o;       o = up256(o + sizeof(uint16_t) * (size_t)tkc * I);
   p.o_pgu = o;     o = up256(o + sizeof(float) * (size_t)p.sgu_max * tkc * 2 * I);
   p.o_pdn = o;     o = up256(o + sizeof(float) * (size_t)p.sdn_max * tkc * H);
+  p.o_rtp = o;     o = up256(o + sizeof(float) * (size_t)dqg::router_splits(H) * t_cap * p.E);
+  p.o_rtl = o;     o = up256(o + sizeof(float) * (size_t)t_cap * p.E);
   p.total = o;
 }
 
@@ -187,18 +190,21 @@ bool use_fused(int T, int H, int I, int E, int k, int format) {
   return E <= 512 && dqg::fused_supported_t(T, H, I, k) && !(format & DQG_PATH_NO_FUSED);
 }
 
-int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint8_t* wgu,
-              const uint16_t* sgu, const uint8_t* wd, const uint16_t* sd, int group, int format,
-              const uint16_t* res, uint16_t* out, int32_t* ids_out, float* w_out, void* ws,
-              hipStream_t st) {
+// logits == nullptr: the router units compute them from wr (fused_router_supported(E))
+int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint16_t* wr,
+              float* logits_out, const uint8_t* wgu, const uint16_t* sgu, const uint8_t* wd,
+              const uint16_t* sd, int group, int format, const uint16_t* res, uint16_t* out,
+              int32_t* ids_out, float* w_out, void* ws, hipStream_t st) {
   dqg::FusedArgs f{};
   f.x = x; f.logits = logits; f.H = p.H; f.I = p.I; f.E = p.E; f.k = p.k; f.group = group;
+  f.wr = logits ? nullptr : wr;
+  f.logits_out = logits ? nullptr : logits_out;
   f.fmt = format & 0xFF;
   f.wgu = wgu; f.sgu = sgu; f.wd = wd; f.sd = sd; f.res = res; f.out = out;
   f.ids_out = ids_out; f.w_out = w_out;
   char* b = static_cast<char*>(ws);
   f.err = reinterpret_cast<int*>(b + p.o_err);
-  dqg::fused_layout(f, b + p.o_fx, p.H, p.I, p.k, p.T);
+  dqg::fused_layout(f, b + p.o_fx, p.H, p.I, p.E, p.k, p.T, f.wr != nullptr);
   return dqg::launch_fused_layer(f, st) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }
 
@@ -326,8 +332,8 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   if (use_fused(T, H, I, E, k, format))
-    return run_fused(p, x, logits, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
-                     out, ids_out, weights_out, workspace, stream);
+    return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
+                     format, residual, out, ids_out, weights_out, workspace, stream);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
                             out, workspace);
   a.ids_w = ids_out ? ids_out : a.ws.ids;
@@ -335,6 +341,61 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   a.ids = a.ids_w;
   a.wts = a.wts_w;
   return run_moe(a, p, logits, stream);
+}
+
+size_t router_logits_workspace_bytes(int T, int H, int E) {
+  if (T < 1 || H < 8 || E < 8 || H % 8 || E % 8 || E > kMaxE || T > kMaxTK) return 0;
+  return up256(sizeof(float) * (size_t)dqg::router_splits(H) * T * E);
+}
+
+int router_logits(const uint16_t* x, int T, int H, int E, const uint16_t* w_router,
+                  float* logits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !w_router || !logits) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || H < 1 || E < 1) return DQG_ERR_INVALID_ARG;
+  const size_t need = router_logits_workspace_bytes(T, H, E);
+  if (need == 0) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_router) || ((uintptr_t)logits & 3u))
+    return DQG_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < need) return DQG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DQG_ERR_MISALIGNED;
+  return dqg::launch_router(x, T, H, w_router, E, static_cast<float*>(workspace), logits,
+                            stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+}
+
+int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T, int H, int I,
+                              int E, int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                              const uint8_t* w_down, const uint16_t* s_down, int group,
+                              int format, const uint16_t* residual, uint16_t* out,
+                              float* logits_out, int32_t* ids_out, float* weights_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!w_router) return DQG_ERR_INVALID_ARG;
+  int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
+                            format, residual, out, workspace, workspace_bytes);
+  if (rc != DQG_OK) return rc;
+  if (E % 8) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(w_router)) return DQG_ERR_MISALIGNED;
+  if (((uintptr_t)logits_out & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
+    return DQG_ERR_MISALIGNED;
+  const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
+  char* b = static_cast<char*>(workspace);
+  if (use_fused(T, H, I, E, k, format) && dqg::fused_router_supported(E))
+    return run_fused(p, x, nullptr, w_router, logits_out, w_gate_up, s_gate_up, w_down, s_down,
+                     group, format, residual, out, ids_out, weights_out, workspace, stream);
+  // the router call, then the layer on its logits
+  float* lg = logits_out ? logits_out : reinterpret_cast<float*>(b + p.o_rtl);
+  if (dqg::launch_router(x, T, H, w_router, E, reinterpret_cast<float*>(b + p.o_rtp), lg,
+                         stream) != hipSuccess)
+    return DQG_ERR_HIP;
+  if (use_fused(T, H, I, E, k, format))
+    return run_fused(p, x, lg, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
+                     format, residual, out, ids_out, weights_out, workspace, stream);
+  MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
+                            out, workspace);
+  a.ids_w = ids_out ? ids_out : a.ws.ids;
+  a.wts_w = weights_out ? weights_out : a.ws.wts;
+  a.ids = a.ids_w;
+  a.wts = a.wts_w;
+  return run_moe(a, p, lg, stream);
 }
 
 size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group) {

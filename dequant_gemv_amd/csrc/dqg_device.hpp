@@ -446,13 +446,12 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return min(min(a, b), min(c, d));
 }
 
+// wave_topk_select_keys takes the keys already in registers: key[v] of element lane + 64 v
+// (any value for elements >= E).
 template <int MAXV>
-__device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, int E, int k,
-                                                 int lane, long long* cand, int* ids,
-                                                 int* keys) {
-  int key[MAXV];
-#pragma unroll
-  for (int v = 0; v < MAXV; ++v) key[v] = logit_key(row[min(lane + 64 * v, E - 1)]);
+__device__ __forceinline__ void wave_topk_select_keys(const int (&key)[MAXV], int E, int k,
+                                                      int lane, long long* cand, int* ids,
+                                                      int* keys) {
   int m = (int)0x80000000;
 #pragma unroll
   for (int v = 0; v < MAXV; ++v)
@@ -551,6 +550,16 @@ __device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, 
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+template <int MAXV>
+__device__ __forceinline__ void wave_topk_select(const float* __restrict__ row, int E, int k,
+                                                 int lane, long long* cand, int* ids,
+                                                 int* keys) {
+  int key[MAXV];
+#pragma unroll
+  for (int v = 0; v < MAXV; ++v) key[v] = logit_key(row[min(lane + 64 * v, E - 1)]);
+  wave_topk_select_keys<MAXV>(key, E, k, lane, cand, ids, keys);
+}
+
 __device__ __forceinline__ void wave_topk_weights(const int* ids, const int* keys, int k,
                                                   int lane, int* sel_e, float* sel_w) {
   const int my_e = (lane < k) ? ids[lane] : -1;
@@ -594,6 +603,73 @@ __device__ __forceinline__ float wg_colsum(const float (&acc)[16], float* red, i
     for (int r = 0; r < RL; ++r) s += v[r];
   }
   return s;
+}
+
+// ---- router logits: one unit of the router GEMV --------------------------------------------
+// logits[t, e] = sum_c x[t, c] W_r[c, e] (W_r bf16 [H, E], fp32 accumulation) is split into
+// units of RT_ROWS rows of W_r and 128 columns.  A unit runs on 256 threads, 16 row-lanes x
+// 16 column-lanes; a lane owns 8 consecutive rows and 8 consecutive columns (one 16-byte load
+// per row).  Fixed order: fma over the lane's rows ascending, then the 16 row-lanes summed
+// ascending through LDS.  The full logit is the sum of the units' partials over the row
+// splits in ascending order, starting from +0.0 -- the same on every path that uses it, so
+// the logits (and with them the routing) are bitwise identical between the single-launch
+// layer and the separate router call.
+constexpr int RT_ROWS = 128;
+constexpr int RT_MAX_T = 4;  // tokens per unit
+// Partial of rows [RT_ROWS rs, +RT_ROWS) and columns [128 ct, +128) for tokens t0 .. t0+nt-1
+// (nt <= RT_MAX_T): on return thread c < 128 holds column 128 ct + c of token t0 + t in
+// part[t] (0 for columns >= E).  red: 16 * 128 floats of LDS.  Needs H % 8 == 0, E % 8 == 0,
+// 16-byte aligned x and W_r.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void router_unit(const uint16_t* __restrict__ x, int H,
+                                            const uint16_t* __restrict__ wr, int E, int rs,
+                                            int ct, int t0, int nt, float* red, int tid,
+                                            float (&part)[RT_MAX_T]) {
+  const int rl = tid >> 4, ch = tid & 15;
+  const int r0 = RT_ROWS * rs + 8 * rl, c0 = 128 * ct + 8 * ch;
+  const bool on = r0 < H && c0 < E;
+  uint4 w[8];
+  uint4 xv[RT_MAX_T];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = on ? *reinterpret_cast<const uint4*>(wr + (size_t)(r0 + i) * E + c0)
+              : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < RT_MAX_T; ++t)
+    xv[t] = (on && t < nt) ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H + r0)
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < RT_MAX_T; ++t) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xi = (i & 1) ? bf16_hi(xw[i >> 1]) : bf16_lo(xw[i >> 1]);
+      const uint32_t ww[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j] = fmaf(xi, (j & 1) ? bf16_hi(ww[j >> 1]) : bf16_lo(ww[j >> 1]), acc[j]);
+    }
+    if (t < nt) {  // uniform
+      float4* dst = reinterpret_cast<float4*>(red + rl * 128 + ch * 8);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      __syncthreads();
+      float s = 0.0f;
+      if (tid < 128) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = red[r * 128 + tid];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += v[r];
+      }
+      part[t] = s;
+      __syncthreads();
+    } else {
+      part[t] = 0.0f;
+    }
+  }
 }
 
 // ---- cross-workgroup exchange ----------------------------------------------------------

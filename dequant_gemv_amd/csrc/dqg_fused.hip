@@ -200,7 +200,24 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
-  const int bid = blockIdx.x;
+  const size_t rsz = (size_t)a.rs * a.T * a.E;       // one copy of the router partial rows
+
+  if ((int)blockIdx.x < a.n_r) {
+    // ================= router unit: rows [128 rs, 128 rs + 128) of W_r, all T tokens =====
+    const unsigned c0 = ld_cnt(a.calls);
+    float pv[RT_MAX_T];
+    router_unit(a.x, H, a.wr, a.E, blockIdx.x, 0, 0, a.T, s_red, tid, pv);
+    const int par = (int)((__builtin_amdgcn_readfirstlane(c0) >> 20) & 1u);
+    if (tid < a.E) {
+      for (int t = 0; t < a.T; ++t) {
+        const size_t o = ((size_t)blockIdx.x * a.T + t) * a.E + tid;
+        st_sc1(a.rpart + par * rsz, o, pub(pv[t]));
+        st_sc1(a.rpart + (1 - par) * rsz, o, 0.0f);
+      }
+    }
+    return;
+  }
+  const int bid = blockIdx.x - a.n_r;
   // the token this workgroup works for: a gate_up unit's slot's, a down unit's chunk's
   // (chunks never span tokens when T > 1)
   const int tok = (a.T == 1) ? 0
@@ -212,11 +229,49 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // tend to land on different SIMDs.  Only the down units need the weights; a gate_up unit
   // only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
-    const float* row = a.logits + (size_t)tok * a.E;
-    if (a.E <= 128)
-      wave_topk_select<2>(row, a.E, k, lane, s_route, s_ids, s_key);
-    else
-      wave_topk_select<8>(row, a.E, k, lane, s_route, s_ids, s_key);
+    float lg[2] = {0.0f, 0.0f};  // router mode: this lane's logits (elements lane, lane + 64)
+    if (a.wr) {
+      // gather the token's logits from the router units' partial rows (E <= 128), summed
+      // over the row splits in ascending order from +0.0
+      const unsigned c0 = ld_cnt(a.calls);
+      const int par = (int)((__builtin_amdgcn_readfirstlane(c0) >> 20) & 1u);
+      const float* rp = a.rpart + par * rsz + (size_t)tok * a.E;
+      const size_t st = (size_t)a.T * a.E;
+      const bool in0 = lane < a.E, in1 = lane + 64 < a.E;
+      bool ok = false;
+      for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
+        float v0[16], v1[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          v0[q] = (q < a.rs && in0) ? ld_sc1(rp, q * st + lane) : 1.0f;
+          v1[q] = (q < a.rs && in1) ? ld_sc1(rp, q * st + lane + 64) : 1.0f;
+        }
+        bool ready = true;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          ready = ready && __float_as_uint(v0[q]) != 0u && __float_as_uint(v1[q]) != 0u;
+        if (__all(ready)) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (q < a.rs) {
+              lg[0] += v0[q];
+              lg[1] += v1[q];
+            }
+          ok = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!ok && lane == 0) atomicOr(a.err, 2);
+      const int key[2] = {logit_key(lg[0]), logit_key(lg[1])};
+      wave_topk_select_keys<2>(key, a.E, k, lane, s_route, s_ids, s_key);
+    } else {
+      const float* row = a.logits + (size_t)tok * a.E;
+      if (a.E <= 128)
+        wave_topk_select<2>(row, a.E, k, lane, s_route, s_ids, s_key);
+      else
+        wave_topk_select<8>(row, a.E, k, lane, s_route, s_ids, s_key);
+    }
     if (bid >= a.n_a) {
       int sel_e;
       float sel_w;
@@ -226,10 +281,12 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
       const bool report = ub / NC == 0 && ub % NC == (tok + 1) * a.chunks_per_token - 1;
       if (lane < k) {
         s_w[lane] = sel_w;
-        if (report && a.ids_out) {
-          a.ids_out[tok * k + lane] = sel_e;
-          a.w_out[tok * k + lane] = sel_w;
-        }
+        if (report && a.ids_out) a.ids_out[tok * k + lane] = sel_e;  // each output optional
+        if (report && a.w_out) a.w_out[tok * k + lane] = sel_w;
+      }
+      if (report && a.logits_out) {
+        if (lane < a.E) a.logits_out[(size_t)tok * a.E + lane] = lg[0];
+        if (lane + 64 < a.E) a.logits_out[(size_t)tok * a.E + lane + 64] = lg[1];
       }
     }
   }
@@ -428,6 +485,8 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   }
 }
 
+bool fused_router_supported(int E) { return E <= 128 && E % 8 == 0; }
+
 bool fused_supported(int H, int I, int k) {
   return H % 256 == 0 && H <= 2048 && I % 128 == 0 && k <= 32;
 }
@@ -441,25 +500,29 @@ bool fused_supported_t(int T, int H, int I, int k) {
 // Workspace of the single-launch layer: one region per token count T (1 .. FX_MAX_T), each
 // with its call counter and its two copies of the exchange buffers.  Calls with different T
 // use different slots, so they must not share the buffers that are kept empty between calls.
-static size_t fused_region_bytes(int H, int I, int k, int T) {
+static size_t fused_region_bytes(int H, int I, int E, int k, int T) {
   const int KS = H / 2 / fx_krows(fx_gu_rows(H, T)), NT = I / 128, n_mt = H / 128;
   const int NC = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
   size_t o = 256;                                         // call counter
   o += 2 * (size_t)T * k * NT * KS * 256 * 4;             // gate/up partial rows
   o += 2 * (size_t)n_mt * NC * 128 * 4;                   // output partial rows
+  if (fused_router_supported(E))                          // router partial rows
+    o += 2 * (size_t)router_splits(H) * T * E * 4;
   return (o + 255) & ~(size_t)255;
 }
 
-size_t fused_ws_bytes(int H, int I, int k) {
+size_t fused_ws_bytes(int H, int I, int E, int k) {
   size_t o = 0;
-  for (int T = 1; T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, k, T);
+  for (int T = 1; T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, E, k, T);
   return o;
 }
 
-void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T) {
+void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, bool with_router) {
   char* p = static_cast<char*>(ws);
-  for (int t = 1; t < T; ++t) p += fused_region_bytes(H, I, k, t);
+  for (int t = 1; t < T; ++t) p += fused_region_bytes(H, I, E, k, t);
   f.T = T;
+  f.rs = router_splits(H);
+  f.n_r = with_router ? f.rs : 0;
   f.ks = H / 2 / fx_krows(fx_gu_rows(H, T));
   f.n_mt = H / 128;
   f.n_chunks = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
@@ -472,10 +535,12 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T) {
   f.gpart = reinterpret_cast<float*>(p + o);
   o += 2 * (size_t)T * k * (I / 128) * f.ks * 256 * 4;
   f.ypart = reinterpret_cast<float*>(p + o);
+  o += 2 * (size_t)f.n_mt * f.n_chunks * 128 * 4;
+  f.rpart = fused_router_supported(E) ? reinterpret_cast<float*>(p + o) : nullptr;
 }
 
 hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st) {
-  const int grid = f.n_a + f.n_b;
+  const int grid = f.n_r + f.n_a + f.n_b;
   const bool big = fx_gu_rows(f.H, f.T) == 16;
   if (f.fmt == FMT_FP4) {
     if (big)

@@ -52,10 +52,14 @@ struct GemvArgs {
   int* err;             // error word (bit 1: a wait gave up), may be null
 };
 
-// Single-launch T = 1 layer (routing + expert FFN + combine); see dqg_fused.hip.
+// Single-launch layer for T <= 4 (routing + expert FFN + combine); see dqg_fused.hip.
 struct FusedArgs {
   const uint16_t* x;
-  const float* logits;
+  const float* logits;  // fp32 [T, E], or null when the router units compute them
+  const uint16_t* wr;   // router weight bf16 [H, E] (router units), or null
+  float* logits_out;    // optional fp32 [T, E] copy of the router's logits (may be null)
+  float* rpart;         // [2][rs][T][E] router partial rows, two copies
+  int n_r, rs;          // router units (the first n_r workgroups) and row splits
   int H, I, E, k, group, fmt;
   const uint8_t* wgu;
   const uint16_t* sgu;
@@ -76,8 +80,10 @@ struct FusedArgs {
 constexpr int FX_MAX_T = 4;  // tokens of the single-launch layer, at most
 bool fused_supported(int H, int I, int k);
 bool fused_supported_t(int T, int H, int I, int k);
-size_t fused_ws_bytes(int H, int I, int k);
-void fused_layout(FusedArgs& f, void* ws, int H, int I, int k, int T);
+bool fused_router_supported(int E);
+size_t fused_ws_bytes(int H, int I, int E, int k);
+// lays out the call's region; with_router: the first workgroups compute the logits
+void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, bool with_router);
 hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st);
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
@@ -94,5 +100,9 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st);
 int ex_max_split_gemv();
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st);
+// router logits[T, E] = x W_r through partials [router_splits(H)][T][E] (see router_unit)
+int router_splits(int H);
+hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, int E, float* part,
+                         float* logits, hipStream_t st);
 
 }  // namespace dqg

@@ -240,6 +240,41 @@ __device__ __forceinline__ void colsum_tokens(const float (&acc)[NT][16], float*
 }
 
 // =====================================================================================
+// router logits from the hidden state (FireEcho page, "Architecture": the MoE FFN with
+// fused dispatch, read as the plain linear router x W_r): one workgroup per router unit
+// (row split rs, 128-column tile ct, group of up to 4 tokens) writes its partials
+// part[(rs T + t) E + e]; the reduction adds them in ascending rs from +0.0.  Same
+// arithmetic as the router units of the single-launch layer (router_unit).
+// =====================================================================================
+__global__ void __launch_bounds__(256) router_partial_kernel(const uint16_t* __restrict__ x,
+                                                             int T, int H,
+                                                             const uint16_t* __restrict__ wr,
+                                                             int E, float* __restrict__ part) {
+  __shared__ __align__(16) float red[16 * 128];
+  const int rs = blockIdx.x, ct = blockIdx.y, t0 = RT_MAX_T * blockIdx.z;
+  const int nt = min(RT_MAX_T, T - t0);
+  float pv[RT_MAX_T];
+  router_unit(x, H, wr, E, rs, ct, t0, nt, red, threadIdx.x, pv);
+  const int e = 128 * ct + threadIdx.x;
+  if (threadIdx.x < 128 && e < E) {
+#pragma unroll
+    for (int t = 0; t < RT_MAX_T; ++t)
+      if (t < nt) part[((size_t)rs * T + t0 + t) * E + e] = pv[t];
+  }
+}
+
+__global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restrict__ part,
+                                                            int RS, int T, int E,
+                                                            float* __restrict__ logits) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t n = (size_t)T * E;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int rs = 0; rs < RS; ++rs) s += part[(size_t)rs * n + i];
+  logits[i] = s;
+}
+
+// =====================================================================================
 // test aid: dequantize with the compute kernels' decode
 // =====================================================================================
 template <int FMT>
@@ -295,6 +330,21 @@ hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st
   const size_t sm = (size_t)sched_int_words(a.E) * sizeof(int) +
                     (size_t)sched_route_waves(a.E) * sched_scratch_entries(a.E) * 8;
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(SCHED_THREADS), sm, st, a, logits);
+  return hipGetLastError();
+}
+
+int router_splits(int H) { return (H + RT_ROWS - 1) / RT_ROWS; }
+
+hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, int E, float* part,
+                         float* logits, hipStream_t st) {
+  const int RS = router_splits(H);
+  const dim3 grid(RS, (E + 127) / 128, (T + RT_MAX_T - 1) / RT_MAX_T);
+  hipLaunchKernelGGL(router_partial_kernel, grid, dim3(256), 0, st, x, T, H, wr, E, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)T * E;
+  hipLaunchKernelGGL(router_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     part, RS, T, E, logits);
   return hipGetLastError();
 }
 

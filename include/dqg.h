@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DQG_ABI_VERSION 1
+#define DQG_ABI_VERSION 2
 
 typedef enum dqg_status {
   DQG_OK = 0,
@@ -85,8 +85,8 @@ int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* we
                hipStream_t stream);
 
 /*
- * Bytes of device workspace that moe_fp4_ffn / moe_fp4_layer need for T tokens with
- * these sizes.  Host only.  Returns 0 for invalid sizes.
+ * Bytes of device workspace that moe_fp4_ffn / moe_fp4_layer / moe_fp4_layer_from_hidden
+ * need for T tokens with these sizes.  Host only.  Returns 0 for invalid sizes.
  * The workspace holds a sticky int32 error word at byte 0 (bit 0: an expert id outside
  * [0, E) was seen -- the slot then contributes zero; bit 1: a wait between workgroups gave
  * up -- the output of that call is not valid), the device-built expert schedule, and
@@ -149,6 +149,46 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
                   const uint16_t* s_down, int group, int format, const uint16_t* residual,
                   uint16_t* out, int32_t* ids_out, float* weights_out, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of device workspace router_logits needs (the router's fp32 partial rows, 4 bytes x
+ * ceil(H / 128) x T x E).  Host only.  Returns 0 for unsupported sizes (H or E not a
+ * multiple of 8, E > 4096).
+ */
+size_t router_logits_workspace_bytes(int T, int H, int E);
+
+/*
+ * router_logits -- the MoE router on the hidden state (FireEcho page, "Architecture": the
+ * packed MoE FFN dispatches from the hidden state; read as the plain linear router, no bias).
+ *   x        bf16 [T, H];  w_router bf16 [H, E] (E contiguous)
+ *   logits   fp32 [T, E] out: logits[t, e] = sum_c x[t, c] * w_router[c, e]
+ * fp32 accumulation in a fixed order: 128-row partials (each an ordered fma chain over 8
+ * rows per lane, then 16 lanes summed in order) added in ascending row order from +0.0 --
+ * the same arithmetic as the router inside moe_fp4_layer_from_hidden, so both give
+ * bitwise-identical logits.  Needs H % 8 == 0, E % 8 == 0, E <= 4096, x and w_router
+ * 16-byte aligned, and a workspace of router_logits_workspace_bytes (scratch, no state
+ * kept between calls).  Two launches on `stream`.  Deterministic.
+ */
+int router_logits(const uint16_t* x, int T, int H, int E, const uint16_t* w_router,
+                  float* logits, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_fp4_layer_from_hidden -- router_logits followed by moe_fp4_layer, the routing taken
+ * from the hidden state x itself.  Same arguments and rules as moe_fp4_layer, with
+ * w_router bf16 [H, E] in place of logits (E % 8 == 0), the same workspace (size query
+ * moe_fp4_ffn_workspace_bytes), and logits_out (fp32 [T, E], nullable) an optional copy of
+ * the router's logits.  When the single-launch layer applies (see moe_fp4_layer) and
+ * E <= 128, the router runs inside that launch: its first ceil(H / 128) workgroups compute
+ * 128-row partials of the logits and every other workgroup adds them up before its
+ * top-k, so the layer stays one launch.  Otherwise the router call runs first.  The
+ * logits, and so the routing, are bitwise identical on both paths.
+ */
+int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T, int H, int I,
+                              int E, int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                              const uint8_t* w_down, const uint16_t* s_down, int group,
+                              int format, const uint16_t* residual, uint16_t* out,
+                              float* logits_out, int32_t* ids_out, float* weights_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of device workspace packed_gemv_int4 needs for T tokens (0: the call never splits

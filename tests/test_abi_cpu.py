@@ -24,7 +24,8 @@ def test_header_lists_expected_entry_points():
     fns = header_functions()
     for name in ("topk_route", "moe_fp4_ffn", "moe_fp4_layer", "packed_gemv_int4",
                  "packed_dequant_f32", "moe_fp4_ffn_workspace_bytes",
-                 "packed_gemv_int4_workspace_bytes", "dqg_status_string", "dqg_abi_version"):
+                 "packed_gemv_int4_workspace_bytes", "dqg_status_string", "dqg_abi_version",
+                 "router_logits", "router_logits_workspace_bytes", "moe_fp4_layer_from_hidden"):
         assert name in fns
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_header_function():
 
 
 def test_abi_version_and_status_strings():
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
     assert B.status_string(0) == "DQG_OK"
     assert B.status_string(-3) == "DQG_ERR_MISALIGNED"
     assert B.status_string(12345) == "DQG_ERR_UNKNOWN"
@@ -104,6 +105,38 @@ def test_moe_layer_validation():
     assert call(k=9) == B.DQG_ERR_INVALID_ARG
     assert call(x=MIS) == B.DQG_ERR_MISALIGNED
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
+
+
+def test_router_validation():
+    f = B.LIB.router_logits
+    q = B.router_logits_workspace_bytes(1, 2048, 128)
+    assert q == 16 * 128 * 4                                  # 16 row splits x 128 logits
+    assert B.router_logits_workspace_bytes(4, 2048, 128) == 4 * q
+    assert B.router_logits_workspace_bytes(1, 2048, 60) == 0  # E % 8
+    assert B.router_logits_workspace_bytes(1, 2044, 64) == 0  # H % 8
+    assert B.router_logits_workspace_bytes(1, 2048, 8192) == 0
+    assert f(0, 1, 2048, 128, A, A, A, q, None) == B.DQG_ERR_INVALID_ARG
+    assert f(A, 0, 2048, 128, A, A, A, q, None) == B.DQG_ERR_INVALID_ARG
+    assert f(A, 1, 2048, 60, A, A, A, q, None) == B.DQG_ERR_UNSUPPORTED
+    assert f(MIS, 1, 2048, 128, A, A, A, q, None) == B.DQG_ERR_MISALIGNED
+    assert f(A, 1, 2048, 128, A, A, A, q - 4, None) == B.DQG_ERR_WORKSPACE
+    assert f(A, 1, 2048, 128, A, A, 0, q, None) == B.DQG_ERR_WORKSPACE
+
+
+def test_moe_layer_from_hidden_validation():
+    f = B.LIB.moe_fp4_layer_from_hidden
+    ok = dict(x=A, wr=A, T=1, H=256, I=128, E=8, k=2, lo=0)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["wr"], a["T"], a["H"], a["I"], a["E"], a["k"], A, A, A, A, 32, 1, 0, A,
+                 a["lo"], 0, 0, A, 1 << 30, None)
+    assert call(wr=0) == B.DQG_ERR_INVALID_ARG
+    assert call(k=9) == B.DQG_ERR_INVALID_ARG
+    assert call(E=12, k=2) == B.DQG_ERR_UNSUPPORTED          # E % 8
+    assert call(wr=MIS) == B.DQG_ERR_MISALIGNED
+    assert call(lo=A + 2) == B.DQG_ERR_MISALIGNED
+    # the MoE workspace query covers the router's partial rows and logits
+    assert B.moe_fp4_ffn_workspace_bytes(64, 2048, 768, 128, 8) >= 64 * 17 * 128 * 4
 
 
 def test_topk_validation():

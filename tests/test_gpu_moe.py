@@ -76,6 +76,26 @@ def test_moe_t1_unfused_path_matches_oracle_and_fused(name, cfg):
     check_bf16(unfused, want, what=f"{name} unfused")
 
 
+@pytest.mark.parametrize("give", ["ids", "weights"])
+def test_layer_routing_outputs_are_optional_each(give):
+    """ids_out and weights_out may be passed one without the other (single launch, T = 1
+    and T = 4, and the multi-launch path)."""
+    B = _b()
+    for cfg, flags in ((S.Q30, 0), (S.Q30.with_T(4), 0), (S.Q30, B.PATH_NO_FUSED)):
+        L, D = _layer(cfg, seed=2)
+        _, oids, ow = _oracle_layer(cfg, L)
+        t = torch.full((cfg.T, cfg.k), -7, dtype=torch.int32 if give == "ids" else torch.float32,
+                       device="cuda")
+        kw = {"ids_out": t} if give == "ids" else {"weights_out": t}
+        B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                        D["s_d"], cfg.group, cfg.fmt, flags=flags, **kw)
+        torch.cuda.synchronize()
+        if give == "ids":
+            assert np.array_equal(t.cpu().numpy(), oids)
+        else:
+            np.testing.assert_allclose(t.cpu().numpy(), ow, rtol=4e-6, atol=1e-7)
+
+
 def test_fused_and_unfused_calls_share_a_workspace():
     """Alternating single-launch T=1 calls with multi-launch calls (T=1 and T=4) on one
     workspace: the self-resetting counters of the single-launch layer stay valid."""
