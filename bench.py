@@ -50,6 +50,10 @@ WORKLOADS = {
                           scales=(0.002, 0.01), logits="zipf", layers=48, chain=True),
     "w512_stack_t8": dict(kind="moe", T=8, E=512, H=2048, I=512, k=10, group=32, fmt=FP4,
                           scales=(0.002, 0.01), logits="zipf", layers=48, chain=True),
+    "q30_router_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                                scales=(0.002, 0.01), logits="router", layers=48),
+    "q30_router_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                                scales=(0.002, 0.01), logits="router", layers=48),
     "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
                               scales=(0.005, 0.02), logits="normal", layers=48),
     "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),
@@ -110,7 +114,8 @@ def _logits(w, g, device):
 def build_moe_workload(w, seed: int = 0, device="cuda"):
     """Layer weight sets drawn on the device: packed bytes uniform over 0..255 (every
     nibble uniform), scales uniform in the workload's range rounded to bf16, x ~ N(0,1)
-    in bf16, logits as in _logits, one set per layer."""
+    in bf16, logits as in _logits, one set per layer.  Router workloads ("router") draw a
+    router weight W_r ~ N(0, 1/sqrt(H)) in bf16 [H, E] per layer instead of logits."""
     import torch
     T, E, H, I, G = w["T"], w["E"], w["H"], w["I"], w["group"]
     lo, hi = w["scales"]
@@ -125,7 +130,9 @@ def build_moe_workload(w, seed: int = 0, device="cuda"):
             w_d=torch.randint(0, 256, (E, I // 2, H), dtype=torch.uint8, device=device,
                               generator=g),
             s_d=_bf16_scales((E, I // G, H), lo, hi, g, device),
-            logits=_logits(w, g, device),
+            logits=None if w["logits"] == "router" else _logits(w, g, device),
+            wr=(torch.randn((H, E), device=device, generator=g) / H ** 0.5).to(torch.bfloat16)
+            if w["logits"] == "router" else None,
         ))
     x = torch.randn((T, H), device=device, generator=g).to(torch.bfloat16)
     return x, out
@@ -261,11 +268,19 @@ def bench_moe(w, args, dev, stream, B):
     x, layers = build_moe_workload(w, device=dev)
     ws = B.moe_workspace(T, H, I, E, k, dev)
     chain = w.get("chain", False)
+    router = w["logits"] == "router"
     xs = [x] + [torch.empty_like(x) for _ in layers]
+    lbuf = torch.empty((T, E), dtype=torch.float32, device=dev)
+    rws = B.router_logits_workspace(T, H, E, dev) if router else None
     torch.cuda.synchronize()
 
     def call(l, L):
         xin = xs[l] if chain else x
+        if router:
+            B.moe_fp4_layer_from_hidden(xin, L["wr"], k, L["w_gu"], L["s_gu"], L["w_d"],
+                                        L["s_d"], G, fmt, residual=xin if chain else None,
+                                        out=xs[l + 1], workspace=ws, flags=flags)
+            return
         B.moe_fp4_layer(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
                         residual=xin if chain else None, out=xs[l + 1], workspace=ws,
                         flags=flags)
@@ -277,6 +292,15 @@ def bench_moe(w, args, dev, stream, B):
     ms_per_step = time_graph(one_pass, stream, args.steps, args.warmup)
     n_layers = len(layers)
     us_per_layer = ms_per_step * 1000.0 / n_layers
+    separate_us = None
+    if router:
+        # context: the same layers as two calls, the router call then the logits-taking layer
+        def two_calls():
+            for l, L in enumerate(layers):
+                B.router_logits(x, L["wr"], logits=lbuf, workspace=rws)
+                B.moe_fp4_layer(x, lbuf, k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
+                                out=xs[l + 1], workspace=ws, flags=flags)
+        separate_us = time_graph(two_calls, stream, args.steps, args.warmup) * 1000.0 / n_layers
 
     # context only: events right before and after each eager layer call (includes the
     # host launch overhead that the graph replay hides)
@@ -294,8 +318,11 @@ def bench_moe(w, args, dev, stream, B):
     eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
 
     per_expert = expert_bytes(H, I, G)
-    n_active = [distinct_experts(L["logits"], k) for L in layers]
+    lgs = [L["logits"] if not router else x.float() @ L["wr"].float() for L in layers]
+    n_active = [distinct_experts(lg, k) for lg in lgs]
     abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
+    if router:
+        abytes += H * E * 2                         # the router weight
     # the single-launch layer takes T <= 4 (for T > 1 a token's down rows must fill whole
     # 256-row chunks), E <= 512, H % 256 == 0, H <= 2048, I % 128 == 0
     fused = (args.path == "auto" and T <= 4 and E <= 512 and H % 256 == 0 and H <= 2048
@@ -319,6 +346,9 @@ def bench_moe(w, args, dev, stream, B):
                   "by the layer calls they contain (steps x layers)",
         "eager_call_us_median": round(eager_us, 3),
     }
+    if router:
+        roofline["router_in_launch"] = fused and E <= 128 and E % 8 == 0
+        roofline["router_call_then_layer_us"] = round(separate_us, 3)
     config = {"workload": args.workload, "T": T, "E": E, "H": H, "I": I, "k": k,
               "format": "fp4_e2m1" if w["fmt"] == FP4 else "int4", "group": G,
               "layers_per_step": n_layers, "chained": chain, "path": args.path,

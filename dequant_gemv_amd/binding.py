@@ -199,6 +199,13 @@ def router_logits_workspace_bytes(T: int, H: int, E: int) -> int:
     return int(LIB.router_logits_workspace_bytes(T, H, E))
 
 
+def router_logits_workspace(T: int, H: int, E: int, device) -> torch.Tensor:
+    n = router_logits_workspace_bytes(T, H, E)
+    if n == 0:
+        raise ValueError("unsupported router sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
 def router_logits(x, w_router, logits=None, workspace=None) -> torch.Tensor:
     T, H = x.shape
     E = w_router.shape[1]
@@ -208,10 +215,7 @@ def router_logits(x, w_router, logits=None, workspace=None) -> torch.Tensor:
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _need(logits, "logits", 4, (T, E), x.device)
     if workspace is None:
-        n = router_logits_workspace_bytes(T, H, E)
-        if n == 0:
-            raise ValueError("unsupported router sizes")
-        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+        workspace = router_logits_workspace(T, H, E, x.device)
     _need(workspace, "workspace", 1, None, x.device)
     _check("router_logits", LIB.router_logits(
         _ptr(x), T, H, E, _ptr(w_router), _ptr(logits), _ptr(workspace), workspace.numel(),
