@@ -269,8 +269,16 @@ __global__ void __launch_bounds__(256) router_reduce_kernel(const float* __restr
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t n = (size_t)T * E;
   if (i >= n) return;
+  // all loads of a group of 16 splits in flight together; sums in ascending split order
   float s = 0.0f;
-  for (int rs = 0; rs < RS; ++rs) s += part[(size_t)rs * n + i];
+  for (int r0 = 0; r0 < RS; r0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = (r0 + q < RS) ? part[(size_t)(r0 + q) * n + i] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (r0 + q < RS) s += v[q];
+  }
   logits[i] = s;
 }
 
