@@ -323,9 +323,9 @@ def bench_moe(w, args, dev, stream, B):
     abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
     if router:
         abytes += H * E * 2                         # the router weight
-    # the single-launch layer takes T <= 4 (for T > 1 a token's down rows must fill whole
+    # the single-launch layer takes T <= 8 (for T > 1 a token's down rows must fill whole
     # 256-row chunks), E <= 512, H % 256 == 0, H <= 2048, I % 128 == 0
-    fused = (args.path == "auto" and T <= 4 and E <= 512 and H % 256 == 0 and H <= 2048
+    fused = (args.path == "auto" and T <= 8 and E <= 512 and H % 256 == 0 and H <= 2048
              and I % 128 == 0 and (T == 1 or (k * (I // 2)) % 256 == 0))
     gbps = abytes / (us_per_layer * 1e-6) / 1e9
     # the single-launch path runs the whole layer in one kernel, so its average duration
@@ -347,7 +347,7 @@ def bench_moe(w, args, dev, stream, B):
         "eager_call_us_median": round(eager_us, 3),
     }
     if router:
-        roofline["router_in_launch"] = fused and E <= 128 and E % 8 == 0
+        roofline["router_in_launch"] = fused and E <= 128 and E % 8 == 0 and T <= 4
         roofline["router_call_then_layer_us"] = round(separate_us, 3)
     config = {"workload": args.workload, "T": T, "E": E, "H": H, "I": I, "k": k,
               "format": "fp4_e2m1" if w["fmt"] == FP4 else "int4", "group": G,

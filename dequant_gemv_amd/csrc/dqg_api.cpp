@@ -82,7 +82,9 @@ void moe_layout(MoePlan& p, int t_cap) {
   p.sdn_max = moe_split_max(I / 32, 8, kMaxSplitDown, tkc, 4LL * H);
   size_t o = 0;
   p.o_err = o;     o += 256;
-  p.o_fx = o;      o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, p.E, k) : 0));
+  // single-launch exchange regions for the token counts this capacity allows
+  p.o_fx = o;
+  o = up256(o + (dqg::fused_supported(H, I, k) ? dqg::fused_ws_bytes(H, I, p.E, k, t_cap) : 0));
   p.o_nact = o;    o += 256;
   p.o_rec = o;     o = up256(o + 16 * (size_t)a_cap);
   p.o_slots = o;   o = up256(o + sizeof(int) * tkc);
@@ -190,7 +192,7 @@ bool use_fused(int T, int H, int I, int E, int k, int format) {
   return E <= 512 && dqg::fused_supported_t(T, H, I, k) && !(format & DQG_PATH_NO_FUSED);
 }
 
-// logits == nullptr: the router units compute them from wr (fused_router_supported(E))
+// logits == nullptr: the router units compute them from wr (fused_router_supported(E, T))
 int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint16_t* wr,
               float* logits_out, const uint8_t* wgu, const uint16_t* sgu, const uint8_t* wd,
               const uint16_t* sd, int group, int format, const uint16_t* res, uint16_t* out,
@@ -378,7 +380,7 @@ int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   char* b = static_cast<char*>(workspace);
-  if (use_fused(T, H, I, E, k, format) && dqg::fused_router_supported(E))
+  if (use_fused(T, H, I, E, k, format) && dqg::fused_router_supported(E, T))
     return run_fused(p, x, nullptr, w_router, logits_out, w_gate_up, s_gate_up, w_down, s_down,
                      group, format, residual, out, ids_out, weights_out, workspace, stream);
   // the router call, then the layer on its logits

@@ -1,4 +1,4 @@
-// Single-launch packed-MoE layer for up to FX_MAX_T = 4 tokens: routing, fused gate_up,
+// Single-launch packed-MoE layer for up to FX_MAX_T = 8 tokens: routing, fused gate_up,
 // SiLU*up, down projection and the top-k combine in one kernel.
 //
 // FireEcho page, "The Goliath Kernel: Why It's Fast": one launch reads the expert ids from
@@ -485,7 +485,9 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   }
 }
 
-bool fused_router_supported(int E) { return E <= 128 && E % 8 == 0; }
+// router units in the launch: E <= 128 (two logits per lane of the routing wavefront) and
+// at most RT_MAX_T tokens (one router unit covers every token of the call)
+bool fused_router_supported(int E, int T) { return E <= 128 && E % 8 == 0 && T <= RT_MAX_T; }
 
 bool fused_supported(int H, int I, int k) {
   return H % 256 == 0 && H <= 2048 && I % 128 == 0 && k <= 32;
@@ -506,14 +508,14 @@ static size_t fused_region_bytes(int H, int I, int E, int k, int T) {
   size_t o = 256;                                         // call counter
   o += 2 * (size_t)T * k * NT * KS * 256 * 4;             // gate/up partial rows
   o += 2 * (size_t)n_mt * NC * 128 * 4;                   // output partial rows
-  if (fused_router_supported(E))                          // router partial rows
+  if (fused_router_supported(E, T))                       // router partial rows
     o += 2 * (size_t)router_splits(H) * T * E * 4;
   return (o + 255) & ~(size_t)255;
 }
 
-size_t fused_ws_bytes(int H, int I, int E, int k) {
+size_t fused_ws_bytes(int H, int I, int E, int k, int t_max) {
   size_t o = 0;
-  for (int T = 1; T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, E, k, T);
+  for (int T = 1; T <= t_max && T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, E, k, T);
   return o;
 }
 
@@ -536,7 +538,7 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, boo
   o += 2 * (size_t)T * k * (I / 128) * f.ks * 256 * 4;
   f.ypart = reinterpret_cast<float*>(p + o);
   o += 2 * (size_t)f.n_mt * f.n_chunks * 128 * 4;
-  f.rpart = fused_router_supported(E) ? reinterpret_cast<float*>(p + o) : nullptr;
+  f.rpart = fused_router_supported(E, T) ? reinterpret_cast<float*>(p + o) : nullptr;
 }
 
 hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st) {

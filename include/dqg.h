@@ -59,7 +59,7 @@ typedef enum dqg_format {
 /* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
  * default, 0, picks the path from the shapes).  FORCE_GEMV runs every expert on the
  * vector-ALU tiles, FORCE_MFMA runs every expert with at least one token on the bf16
- * matrix-core tiles, NO_FUSED disables the single-launch layer (T <= 4). */
+ * matrix-core tiles, NO_FUSED disables the single-launch layer (T <= 8). */
 #define DQG_PATH_FORCE_GEMV 0x100
 #define DQG_PATH_FORCE_MFMA 0x200
 #define DQG_PATH_NO_FUSED 0x400
@@ -122,7 +122,7 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch per
  * projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16 (FP4)
  * or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch layer
- * (moe_fp4_layer, T <= 4).
+ * (moe_fp4_layer, T <= 8).
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
  * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
@@ -137,7 +137,7 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
 
 /*
  * moe_fp4_layer -- topk_route followed by moe_fp4_ffn in one call (routing computed on
- * the device from `logits` fp32 [T, E]; same rules as topk_route).  For T <= 4 the
+ * the device from `logits` fp32 [T, E]; same rules as topk_route).  For T <= 8 the
  * whole layer runs as a single kernel launch when E <= 512, H % 256 == 0, H <= 2048,
  * I % 128 == 0 and (for T > 1) k * I / 2 is a multiple of 256; every slot then streams its
  * expert itself (an expert chosen by several tokens is read once per token).  Other calls
@@ -178,7 +178,7 @@ int router_logits(const uint16_t* x, int T, int H, int E, const uint16_t* w_rout
  * w_router bf16 [H, E] in place of logits (E % 8 == 0), the same workspace (size query
  * moe_fp4_ffn_workspace_bytes), and logits_out (fp32 [T, E], nullable) an optional copy of
  * the router's logits.  When the single-launch layer applies (see moe_fp4_layer) and
- * E <= 128, the router runs inside that launch: its first ceil(H / 128) workgroups compute
+ * E <= 128 and T <= 4, the router runs inside that launch: its first ceil(H / 128) workgroups compute
  * 128-row partials of the logits and every other workgroup adds them up before its
  * top-k, so the layer stays one launch.  Otherwise the router call runs first.  The
  * logits, and so the routing, are bitwise identical on both paths.

@@ -385,14 +385,16 @@ def test_fused_layer_routing_edge_cases(E, k, dist):
     check_bf16(out, want, what=f"route E={E} k={k} {dist}")
 
 
-# ---- single-launch layer for T = 1 .. 4 ---------------------------------------------------
+# ---- single-launch layer for T = 1 .. 8 ---------------------------------------------------
 FUSED_T_CASES = [("q30", S.Q30_BATCH, 2), ("q30", S.Q30_BATCH, 3), ("q30", S.Q30_BATCH, 4),
-                 ("w512", S.replace(S.W512, layers=1), 2), ("w512", S.replace(S.W512, layers=1), 4)]
+                 ("q30", S.Q30_BATCH, 5), ("q30", S.Q30_BATCH, 7), ("q30", S.Q30_BATCH, 8),
+                 ("w512", S.replace(S.W512, layers=1), 2), ("w512", S.replace(S.W512, layers=1), 4),
+                 ("w512", S.replace(S.W512, layers=1), 6), ("w512", S.replace(S.W512, layers=1), 8)]
 
 
 @pytest.mark.parametrize("name,cfg,T", FUSED_T_CASES, ids=[f"{c[0]}-T{c[2]}" for c in FUSED_T_CASES])
 def test_fused_layer_small_batch(name, cfg, T):
-    """T = 2 .. 4 through the single-launch layer (one unit set per slot; a token's down
+    """T = 2 .. 8 through the single-launch layer (one unit set per slot; a token's down
     chunks combine into its output row): ids bit-exact, weights and output against the oracle,
     with a residual, and equal to the multi-launch path within the tolerance."""
     B = _b()
@@ -410,18 +412,19 @@ def test_fused_layer_small_batch(name, cfg, T):
 
 
 def test_fused_layer_calls_with_changing_T_share_a_workspace():
-    """Single-launch calls with T = 1, 4, 2, 4, 3, 1, 2 on one workspace (each T keeps its own
-    exchange buffers, which stay empty between its calls): every call meets the oracle."""
+    """Single-launch calls with T = 1, 4, 2, 8, 4, 3, 1, 6, 2, 8 on one workspace (each T keeps
+    its own exchange buffers, which stay empty between its calls): every call meets the
+    oracle."""
     B = _b()
     cfg = S.Q30_BATCH
-    ws = B.moe_workspace(4, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    ws = B.moe_workspace(8, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
     layers = {}
-    for T in (1, 2, 3, 4):
+    for T in (1, 2, 3, 4, 6, 8):
         c = cfg.with_T(T)
         L = S.make_moe_layer(c, seed=40 + T)
         D = upload_layer(L)
         layers[T] = (c, L, D, _oracle_layer(c, L)[0])
-    for it, T in enumerate((1, 4, 2, 4, 3, 1, 2, 4)):
+    for it, T in enumerate((1, 4, 2, 8, 4, 3, 1, 6, 2, 8)):
         c, L, D, want = layers[T]
         out = B.moe_fp4_layer(dev(L.x), dev(L.logits), c.k, D["w_gu"], D["s_gu"], D["w_d"],
                               D["s_d"], c.group, c.fmt, workspace=ws)

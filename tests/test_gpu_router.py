@@ -145,12 +145,13 @@ def test_single_launch_and_router_call_give_identical_logits(name, cfg, seed):
 
 
 @pytest.mark.parametrize("name,cfg,seed", [("q30_t8", S.Q30.with_T(8), 2),
+                                           ("q30_t16", S.Q30.with_T(16), 0),
                                            ("w512_t1", S.replace(S.W512, layers=1), 0),
                                            ("w512_t4", S.replace(S.W512, layers=1, T=4), 1)])
 def test_layer_from_hidden_other_paths(name, cfg, seed):
     """Shapes outside the single launch with router units (T > 4, or E > 128): the router
-    call, then the layer on its logits (multi-launch for T = 8; the single launch without
-    router units for the 512-expert shape at T <= 4)."""
+    call, then the layer on its logits (the single launch without router units for T <= 8,
+    the multi-launch path beyond)."""
     B = _b()
     cfg, L, wr, D = _layer(cfg, seed)
     T, E, k = cfg.T, cfg.E, cfg.k
