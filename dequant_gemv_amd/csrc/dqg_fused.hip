@@ -37,7 +37,10 @@
 // on every gate_up unit of the token); producers clear their slots of copy 1-p, which the
 // previous call used and the next call will use.  Each token count T has its own counter
 // and buffers in the workspace, so that calls with different T never leave data in each
-// other's slots.  A unit only waits on units with lower block ids, so in-order dispatch
+// other's slots.  The router's partial rows follow the same scheme with a counter of their
+// own that only calls with router units advance, so that calls without them (which leave
+// those rows alone) cannot put a later router call on a copy that still holds old rows.
+// A unit only waits on units with lower block ids, so in-order dispatch
 // cannot deadlock; waits are bounded and set bit 1 of the error word on timeout instead of
 // hanging.
 #include <hip/hip_runtime.h>
@@ -204,7 +207,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
 
   if ((int)blockIdx.x < a.n_r) {
     // ================= router unit: rows [128 rs, 128 rs + 128) of W_r, all T tokens =====
-    const unsigned c0 = ld_cnt(a.calls);
+    const unsigned c0 = ld_cnt(a.rcalls);
     float pv[RT_MAX_T];
     router_unit(a.x, H, a.wr, a.E, blockIdx.x, 0, 0, a.T, s_red, tid, pv);
     const int par = (int)((__builtin_amdgcn_readfirstlane(c0) >> 20) & 1u);
@@ -233,7 +236,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     if (a.wr) {
       // gather the token's logits from the router units' partial rows (E <= 128), summed
       // over the row splits in ascending order from +0.0
-      const unsigned c0 = ld_cnt(a.calls);
+      const unsigned c0 = ld_cnt(a.rcalls);
       const int par = (int)((__builtin_amdgcn_readfirstlane(c0) >> 20) & 1u);
       const float* rp = a.rpart + par * rsz + (size_t)tok * a.E;
       const size_t st = (size_t)a.T * a.E;
@@ -482,6 +485,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const unsigned share = (1u << 20) / nf;
     const unsigned add = (fi + 1 < nf) ? share : (1u << 20) - (nf - 1) * share;
     __hip_atomic_fetch_add(a.calls, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.wr) __hip_atomic_fetch_add(a.rcalls, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -533,6 +537,7 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, boo
   f.n_b = f.n_mt * f.n_chunks;
   f.hold_down = (size_t)k * (H / 2) * (2 * (size_t)I) >= ((size_t)1 << 20);
   f.calls = reinterpret_cast<unsigned int*>(p);
+  f.rcalls = reinterpret_cast<unsigned int*>(p + 64);  // the router's own parity counter
   size_t o = 256;
   f.gpart = reinterpret_cast<float*>(p + o);
   o += 2 * (size_t)T * k * (I / 128) * f.ks * 256 * 4;

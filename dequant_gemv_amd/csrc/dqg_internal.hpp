@@ -72,6 +72,7 @@ struct FusedArgs {
   float* gpart;         // [2][k * I/128 * ks][256] gate/up partial rows, two copies
   float* ypart;         // [2][H/128 * n_chunks][128] output partial rows, two copies
   unsigned int* calls;  // call counter: every call adds 2^20 in total (parity source)
+  unsigned int* rcalls; // router call counter: calls with router units add 2^20
   int* err;
   int n_a, n_b, n_chunks, ks, n_mt;
   int T, chunks_per_token;  // tokens (1 .. FX_MAX_T) and down chunks per token

@@ -76,6 +76,25 @@ def test_moe_t1_unfused_path_matches_oracle_and_fused(name, cfg):
     check_bf16(unfused, want, what=f"{name} unfused")
 
 
+@pytest.mark.parametrize("flags_name", ["auto", "gemv", "mfma"])
+def test_every_expert_active(flags_name):
+    """T = 16 tokens routed to all 128 experts, 1 token each (the grid's whole expert range
+    active; vector-ALU passes of one token, or forced matrix-core tiles)."""
+    B = _b()
+    flags = {"auto": 0, "gemv": B.PATH_FORCE_GEMV, "mfma": B.PATH_FORCE_MFMA}[flags_name]
+    cfg = S.Q30.with_T(16)
+    L = S.make_moe_layer(cfg, seed=11)
+    D = upload_layer(L)
+    T, k = cfg.T, cfg.k
+    ids = ((np.arange(T)[:, None] * k + np.arange(k)[None, :]) % cfg.E).astype(np.int32)
+    w = np.random.default_rng(3).dirichlet(np.ones(k), size=T).astype(np.float32)
+    out = B.moe_fp4_ffn(dev(L.x), dev(ids), dev(w), D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                        cfg.group, cfg.fmt, flags=flags)
+    torch.cuda.synchronize()
+    want = O.moe_ffn(L.x, ids, w, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group, cfg.fmt)
+    check_bf16(bits16(out), want, what=f"128 active experts, {flags_name}")
+
+
 @pytest.mark.parametrize("give", ["ids", "weights"])
 def test_layer_routing_outputs_are_optional_each(give):
     """ids_out and weights_out may be passed one without the other (single launch, T = 1

@@ -199,3 +199,30 @@ def test_router_layer_and_logits_layer_share_a_workspace():
     want, _, _ = O.moe_layer(L.x, L.logits, cfg1.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg1.group,
                              cfg1.fmt)
     check_bf16(first["g1"], want, what="logits-given call")
+
+
+def test_router_rows_after_an_interleaved_logits_call():
+    """Router calls, then a logits-taking call, then a router call with another hidden state
+    on one workspace: the router rows the last call reads are its own (the router's copies
+    alternate with router calls only), so its logits equal the separate router call's."""
+    B = _b()
+    cfg, L, wr, D = _layer(S.Q30, 4)
+    xa = dev(L.x)
+    xb_bits = S.f32_to_bf16_bits(np.random.default_rng(123).standard_normal((1, cfg.H)))
+    xb = dev(xb_bits)
+    ws = B.moe_workspace(1, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    args = (D["w_gu"], D["s_gu"], D["w_d"], D["s_d"], cfg.group, cfg.fmt)
+    lg = torch.empty((1, cfg.E), dtype=torch.float32, device="cuda")
+    want_b = B.router_logits(xb, dev(wr)).cpu().numpy()
+    for rep in range(3):
+        B.moe_fp4_layer_from_hidden(xa, dev(wr), cfg.k, *args, workspace=ws)
+        B.moe_fp4_layer_from_hidden(xa, dev(wr), cfg.k, *args, workspace=ws)
+        B.moe_fp4_layer(xa, dev(L.logits), cfg.k, *args, workspace=ws)
+        out_b = B.moe_fp4_layer_from_hidden(xb, dev(wr), cfg.k, *args, logits_out=lg,
+                                            workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(lg.cpu().numpy().view(np.uint32), want_b.view(np.uint32)), rep
+    want, _, _, _ = O.moe_layer_from_hidden(xb_bits, wr, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d,
+                                            cfg.group, cfg.fmt)
+    check_bf16(bits16(out_b), want, what="router call after a logits call")
+    assert int(ws[:4].view(torch.int32).item()) == 0
