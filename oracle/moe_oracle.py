@@ -18,6 +18,10 @@ What each function follows (page titles as printed at the head of each page):
 * FP4 values -- FireEcho, "Quantization Formats" names the FP4 format only; its element
   type is read as OCP Microscaling E2M1 (sign bit, 2 exponent bits with bias 1, 1 mantissa
   bit; exponent field 0 is subnormal).
+* FP8 values -- the same table lists an 8-bit "Goliath FP8" format (there used for the KV
+  cache); as a weight format its element is read as OCP FP8 E4M3 (sign bit, 4 exponent bits
+  with bias 7, 3 mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN and there
+  is no infinity), one byte per weight, ``[E, K, N]`` with the same bf16 group scales.
 * INT4 values -- symmetric, ``nibble - 8``; the page's simplified snippet multiplies the
   raw nibble by the scale, which is not used (it is labelled a simplification).
 * group scales -- one bf16 scale per ``group`` consecutive K indices and per column.
@@ -48,6 +52,7 @@ import numpy as np
 
 FMT_INT4 = 0
 FMT_FP4 = 1
+FMT_FP8 = 2
 
 
 # ------------------------------------------------------------------------------------
@@ -66,16 +71,40 @@ def e2m1_value(code: int) -> float:
     return math.copysign(mag, -1.0 if sign else 1.0)
 
 
+def e4m3_value(code: int) -> float:
+    """OCP FP8 E4M3: bit 7 sign, bits 6-3 exponent (bias 7), bits 2-0 mantissa.  Exponent
+    field 0 is subnormal: value = mantissa / 8 * 2**-6.  Exponent 15 with mantissa 7 is NaN;
+    exponent 15 otherwise is an ordinary binade (no infinity), up to 448."""
+    sign = (code >> 7) & 1
+    exp = (code >> 3) & 15
+    man = code & 7
+    if exp == 15 and man == 7:
+        return math.nan
+    if exp == 0:
+        mag = (man / 8.0) * 2.0 ** -6
+    else:
+        mag = (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return math.copysign(mag, -1.0 if sign else 1.0)
+
+
 def int4_value(code: int) -> float:
     """Symmetric INT4: stored nibble n means n - 8."""
     return float(code - 8)
 
 
 def decode_table(fmt: int) -> np.ndarray:
-    fn = e2m1_value if fmt == FMT_FP4 else int4_value
+    """Value of every code: 16 entries (4-bit formats) or 256 (FP8; NaN codes give NaN)."""
+    if fmt == FMT_FP8:
+        return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
     if fmt not in (FMT_FP4, FMT_INT4):
         raise ValueError(fmt)
+    fn = e2m1_value if fmt == FMT_FP4 else int4_value
     return np.array([fn(c) for c in range(16)], dtype=np.float64)
+
+
+def codes_per_byte(fmt: int) -> int:
+    """K indices per stored byte: 2 for the 4-bit formats, 1 for FP8."""
+    return 1 if fmt == FMT_FP8 else 2
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -109,16 +138,19 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
 
 def dequant(packed: np.ndarray, scale_bits: np.ndarray, group: int, fmt: int,
             cols: Optional[np.ndarray] = None) -> np.ndarray:
-    """Dequantize one packed matrix ``[K/2, N]`` with scales ``[K/G, N]`` into float64
-    ``[K, N]``: ``W[k, n] = value(code[k, n]) * scale[k // group, n]``.
+    """Dequantize one packed matrix ``[K/2, N]`` (FP8: ``[K, N]``, one code per byte) with
+    scales ``[K/G, N]`` into float64 ``[K, N]``:
+    ``W[k, n] = value(code[k, n]) * scale[k // group, n]``.
     ``cols`` optionally selects output columns (for sampled checks of large N)."""
     if cols is not None:
         packed = packed[:, cols]
         scale_bits = scale_bits[:, cols]
-    codes = unpack_codes(packed)
+    codes = np.asarray(packed, dtype=np.uint8) if fmt == FMT_FP8 else unpack_codes(packed)
     K = codes.shape[0]
     assert K % group == 0 and scale_bits.shape[0] == K // group
     vals = decode_table(fmt)[codes]
+    if np.isnan(vals).any():
+        raise ValueError("NaN weight code")
     scales = np.repeat(bf16_to_f64(scale_bits), group, axis=0)
     return vals * scales
 

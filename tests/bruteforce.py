@@ -38,8 +38,22 @@ def bf16_fraction(bits: int) -> Fraction:
     return Fraction(struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0])
 
 
+def e4m3_fraction(code: int) -> Fraction:
+    """FP8 E4M3 from its bit fields, exactly (the hand-worked rows of
+    golden/e4m3_worked.txt follow the same definition).  NaN codes are rejected."""
+    s, ex, m = code >> 7, (code >> 3) & 15, code & 7
+    if ex == 15 and m == 7:
+        raise ValueError("NaN code")
+    mag = Fraction(m, 8) * Fraction(1, 64) if ex == 0 else \
+        (1 + Fraction(m, 8)) * (Fraction(2) ** (ex - 7))
+    return -mag if s else mag
+
+
 def dequant_exact(packed, scales, group: int, fmt: str):
-    """packed [K/2][N] bytes, scales [K/G][N] bf16 bits -> exact W [K][N] (Fractions)."""
+    """packed [K/2][N] bytes (fp8: [K][N]), scales [K/G][N] bf16 bits -> exact W [K][N]."""
+    if fmt == "fp8":
+        return [[e4m3_fraction(int(b)) * bf16_fraction(scales[k // group][n])
+                 for n, b in enumerate(row)] for k, row in enumerate(packed)]
     tab = _TABLES[fmt]
     Kp, N = len(packed), len(packed[0])
     W = [[None] * N for _ in range(2 * Kp)]

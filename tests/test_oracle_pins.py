@@ -257,6 +257,71 @@ def test_moe_matches_exact_bruteforce(seed):
 
 
 # --------------------------------------------------------------------------------------
+# FP8 E4M3
+# --------------------------------------------------------------------------------------
+def _e4m3_golden():
+    rows = []
+    for line in open(os.path.join(HERE, "golden", "e4m3_worked.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            c, v, b = line.split()
+            rows.append((int(c, 16), v, b))
+    return rows
+
+
+def test_e4m3_hand_worked_codes():
+    tab = O.decode_table(O.FMT_FP8)
+    for code, v, b in _e4m3_golden():
+        if v == "nan":
+            assert math.isnan(tab[code])
+            continue
+        assert tab[code] == float(v) and math.copysign(1, tab[code]) == math.copysign(1, float(v))
+        W = O.dequant(np.array([[code]], np.uint8), np.array([[0x3C80]], np.uint16), 1, O.FMT_FP8)
+        assert struct.unpack("<I", struct.pack("<f", W[0, 0]))[0] == int(b, 16)
+
+
+def test_e4m3_table_matches_torch_float8():
+    tab = O.decode_table(O.FMT_FP8)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(tab), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(tab[ok], ref[ok])
+    assert np.array_equal(np.signbit(tab[ok]), np.signbit(ref[ok]))
+    assert np.sum(np.isnan(tab)) == 2 and np.nanmax(tab) == 448.0
+
+
+def test_fp8_dequant_layout_is_one_code_per_byte_row():
+    rng = np.random.default_rng(7)
+    K, N, G = 64, 16, 32
+    codes = S.fp8_codes(rng, (K, N))
+    scales = S.f32_to_bf16_bits(rng.uniform(0.1, 1.0, size=(K // G, N)))
+    W = O.dequant(codes, scales, G, O.FMT_FP8)
+    ex = BF.dequant_exact(codes.tolist(), scales.tolist(), G, "fp8")
+    assert W.shape == (K, N)
+    assert all(W[kk, n] == float(ex[kk][n]) for kk in range(K) for n in range(N))
+    with pytest.raises(ValueError):
+        O.dequant(np.full((32, 1), 0x7F, np.uint8), np.ones((1, 1), np.uint16), 32, O.FMT_FP8)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_moe_matches_exact_bruteforce(seed):
+    rng = np.random.default_rng(500 + seed)
+    T, E, k, G, H, I = int(rng.integers(1, 4)), 3, 2, 4, 8, 4
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H)))
+    w_gu = np.stack([S.fp8_codes(rng, (H, 2 * I)) for _ in range(E)])
+    w_d = np.stack([S.fp8_codes(rng, (I, H)) for _ in range(E)])
+    s_gu = S.f32_to_bf16_bits(rng.uniform(0.05, 0.5, size=(E, H // G, 2 * I)))
+    s_d = S.f32_to_bf16_bits(rng.uniform(0.05, 0.5, size=(E, I // G, H)))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    out, ids, w = O.moe_layer(x, lg, k, w_gu, s_gu, w_d, s_d, G, O.FMT_FP8)
+    bout, bids, bw = BF.moe_exact(x.tolist(), lg.tolist(), k, w_gu.tolist(), s_gu.tolist(),
+                                  w_d.tolist(), s_d.tolist(), G, "fp8")
+    assert ids.tolist() == bids
+    scale = max(1e-300, float(np.sqrt(np.mean(np.square(bout)))))
+    assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
+
+
+# --------------------------------------------------------------------------------------
 # router logits from the hidden state
 # --------------------------------------------------------------------------------------
 @pytest.mark.parametrize("seed", range(4))

@@ -28,6 +28,7 @@ import numpy as np
 
 FMT_INT4 = 0  # value = (nibble - 8) * scale
 FMT_FP4 = 1   # value = E2M1(nibble) * scale
+FMT_FP8 = 2   # value = E4M3(byte) * scale, one byte per weight
 
 
 # --------------------------------------------------------------------------------------
@@ -83,10 +84,15 @@ class MoEConfig:
         return replace(self, T=T)
 
     @property
+    def kb(self) -> int:
+        """K indices per stored byte (2 for the 4-bit formats, 1 for FP8)."""
+        return 1 if self.fmt == FMT_FP8 else 2
+
+    @property
     def bytes_per_expert(self) -> int:
         """Packed weight + scale bytes of one expert (gate_up and down)."""
-        H, I, G = self.H, self.I, self.group
-        return (H // 2) * (2 * I) + (H // G) * (2 * I) * 2 + (I // 2) * H + (I // G) * H * 2
+        H, I, G, b = self.H, self.I, self.group, self.kb
+        return (H // b) * (2 * I) + (H // G) * (2 * I) * 2 + (I // b) * H + (I // G) * H * 2
 
 
 @dataclass(frozen=True)
@@ -108,6 +114,7 @@ TINY = MoEConfig("tiny", T=1, E=8, H=256, I=128, k=2, fmt=FMT_INT4, group=32,
 Q30 = MoEConfig("q30", T=1, E=128, H=2048, I=768, k=8, fmt=FMT_FP4, group=32,
                 scale_lo=0.002, scale_hi=0.01)
 Q30_BATCH = replace(Q30, name="q30_batch", T=16, logits="normal+bias")
+Q30_FP8 = replace(Q30, name="q30_fp8", fmt=FMT_FP8)
 W512 = MoEConfig("w512", T=1, E=512, H=2048, I=512, k=10, fmt=FMT_FP4, group=32,
                  scale_lo=0.002, scale_hi=0.01, logits="zipf", layers=48, residual=True)
 GEMV_N = (256, 8192, 34816)
@@ -132,6 +139,14 @@ class MoELayer:
     w_d: np.ndarray              # uint8  [E, I/2, H]
     s_d: np.ndarray              # uint16 [E, I/G, H]
     meta: dict = field(default_factory=dict)
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """FP8 E4M3 weight codes: N(0, 2) values rounded to E4M3 (nearest-even, by torch's
+    float8_e4m3fn cast; input encoding only).  |value| < 448, so no NaN code appears."""
+    import torch
+    v = (2.0 * rng.standard_normal(shape)).astype(np.float32)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def _scales(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
@@ -168,18 +183,21 @@ def make_moe_layer(cfg: MoEConfig, seed: int = 0, layer: int = 0, with_x: bool =
     if not with_x:
         rng.standard_normal((T, H))  # keep the draw order identical
     logits = make_logits(cfg, rng, T)
-    w_gu = np.zeros((E, H // 2, 2 * I), np.uint8)
+    b = cfg.kb
+    w_gu = np.zeros((E, H // b, 2 * I), np.uint8)
     s_gu = np.zeros((E, H // G, 2 * I), np.uint16)
-    w_d = np.zeros((E, I // 2, H), np.uint8)
+    w_d = np.zeros((E, I // b, H), np.uint8)
     s_d = np.zeros((E, I // G, H), np.uint16)
+    codes = fp8_codes if cfg.fmt == FMT_FP8 else \
+        (lambda g, shape: g.integers(0, 256, size=shape, dtype=np.uint8))
     want = None if experts is None else set(int(e) for e in np.asarray(experts).ravel())
     for e in range(E):
         sub = rng.spawn(1)[0]
         if want is not None and e not in want:
             continue
-        w_gu[e] = sub.integers(0, 256, size=(H // 2, 2 * I), dtype=np.uint8)
+        w_gu[e] = codes(sub, (H // b, 2 * I))
         s_gu[e] = _scales(sub, (H // G, 2 * I), cfg.scale_lo, cfg.scale_hi)
-        w_d[e] = sub.integers(0, 256, size=(I // 2, H), dtype=np.uint8)
+        w_d[e] = codes(sub, (I // b, H))
         s_d[e] = _scales(sub, (I // G, H), cfg.scale_lo, cfg.scale_hi)
     return MoELayer(cfg, seed, x, logits, w_gu, s_gu, w_d, s_d, meta={"rng_seed": s})
 
