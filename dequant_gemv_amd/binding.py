@@ -25,6 +25,7 @@ DQG_ERR_WORKSPACE = -4
 DQG_ERR_HIP = -5
 FMT_INT4 = 0
 FMT_FP4_E2M1 = 1
+FMT_FP8_E4M3 = 2
 PATH_FORCE_GEMV = 0x100
 PATH_FORCE_MFMA = 0x200
 PATH_NO_FUSED = 0x400
@@ -136,23 +137,24 @@ def moe_workspace(T: int, H: int, I: int, E: int, k: int, device) -> torch.Tenso
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group):
+def _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, fmt):
     T, H = x.shape
     E, hp, two_i = w_gate_up.shape
     I = two_i // 2
-    if hp * 2 != H:
-        raise ValueError("w_gate_up must be [E, H/2, 2I]")
+    b = 1 if fmt == FMT_FP8_E4M3 else 2   # K indices per stored byte
+    if hp * b != H:
+        raise ValueError(f"w_gate_up must be [E, H/{b}, 2I]" if b > 1 else "w_gate_up must be [E, H, 2I]")
     _need(x, "x", 2)
-    _need(w_gate_up, "w_gate_up", 1, (E, H // 2, 2 * I), x.device)
+    _need(w_gate_up, "w_gate_up", 1, (E, H // b, 2 * I), x.device)
     _need(s_gate_up, "s_gate_up", 2, (E, H // group, 2 * I), x.device)
-    _need(w_down, "w_down", 1, (E, I // 2, H), x.device)
+    _need(w_down, "w_down", 1, (E, I // b, H), x.device)
     _need(s_down, "s_down", 2, (E, I // group, H), x.device)
     return T, H, I, E
 
 
 def moe_fp4_ffn(x, ids, weights, w_gate_up, s_gate_up, w_down, s_down, group: int, fmt: int,
                 residual=None, out=None, workspace=None, flags: int = 0) -> torch.Tensor:
-    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group)
+    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, fmt)
     k = ids.shape[1]
     _need(ids, "ids", 4, (T, k), x.device)
     _need(weights, "weights", 4, (T, k), x.device)
@@ -174,7 +176,7 @@ def moe_fp4_ffn(x, ids, weights, w_gate_up, s_gate_up, w_down, s_down, group: in
 def moe_fp4_layer(x, logits, k: int, w_gate_up, s_gate_up, w_down, s_down, group: int, fmt: int,
                   residual=None, out=None, ids_out=None, weights_out=None, workspace=None,
                   flags: int = 0) -> torch.Tensor:
-    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group)
+    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, fmt)
     _need(logits, "logits", 4, (T, E), x.device)
     if residual is not None:
         _need(residual, "residual", 2, (T, H), x.device)
@@ -227,7 +229,7 @@ def moe_fp4_layer_from_hidden(x, w_router, k: int, w_gate_up, s_gate_up, w_down,
                               group: int, fmt: int, residual=None, out=None, logits_out=None,
                               ids_out=None, weights_out=None, workspace=None,
                               flags: int = 0) -> torch.Tensor:
-    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group)
+    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, fmt)
     _need(w_router, "w_router", 2, (H, E), x.device)
     if residual is not None:
         _need(residual, "residual", 2, (T, H), x.device)
@@ -278,7 +280,7 @@ def packed_gemv_int4(x, w, s, group: int, y=None, workspace=None) -> torch.Tenso
 
 def packed_dequant_f32(w, s, group: int, fmt: int, out=None) -> torch.Tensor:
     Kp, N = w.shape
-    K = 2 * Kp
+    K = Kp if fmt == FMT_FP8_E4M3 else 2 * Kp
     _need(w, "w", 1)
     _need(s, "s", 2, (K // group, N), w.device)
     if out is None:

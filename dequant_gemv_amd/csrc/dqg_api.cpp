@@ -138,7 +138,8 @@ int check_moe_common(const uint16_t* x, int T, int H, int I, int E, int k, const
   if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return DQG_ERR_INVALID_ARG;
   const int fmt = format & 0xFF;
   const int flags = format & ~0xFF;
-  if (fmt != DQG_FMT_INT4 && fmt != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;
+  if (fmt != DQG_FMT_INT4 && fmt != DQG_FMT_FP4_E2M1 && fmt != DQG_FMT_FP8_E4M3)
+    return DQG_ERR_UNSUPPORTED;
   if (flags & ~(DQG_PATH_FORCE_GEMV | DQG_PATH_FORCE_MFMA | DQG_PATH_NO_FUSED))
     return DQG_ERR_UNSUPPORTED;
   if ((flags & DQG_PATH_FORCE_GEMV) && (flags & DQG_PATH_FORCE_MFMA)) return DQG_ERR_INVALID_ARG;
@@ -189,7 +190,8 @@ MoeArgs make_moe_args(const MoePlan& p, const uint16_t* x, const uint8_t* wgu,
 int mfma_tiles(const MoeArgs& a) { return a.mfma_min > a.T ? 0 : 1; }
 
 bool use_fused(int T, int H, int I, int E, int k, int format) {
-  return E <= 512 && dqg::fused_supported_t(T, H, I, k) && !(format & DQG_PATH_NO_FUSED);
+  return E <= 512 && dqg::fused_supported_t(T, H, I, k, format & 0xFF) &&
+         !(format & DQG_PATH_NO_FUSED);
 }
 
 // logits == nullptr: the router units compute them from wr (fused_router_supported(E, T))
@@ -312,6 +314,7 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
   int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
                             format, residual, out, workspace, workspace_bytes);
   if (rc != DQG_OK) return rc;
+  if ((format & 0xFF) == DQG_FMT_FP8_E4M3) return DQG_ERR_UNSUPPORTED;  // single launch only
   if (((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u)) return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
@@ -332,6 +335,8 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   if (rc != DQG_OK) return rc;
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
+  if ((format & 0xFF) == DQG_FMT_FP8_E4M3 && !use_fused(T, H, I, E, k, format))
+    return DQG_ERR_UNSUPPORTED;  // FP8 weights: single launch only
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   if (use_fused(T, H, I, E, k, format))
     return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
@@ -378,6 +383,8 @@ int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T
   if (!aligned16(w_router)) return DQG_ERR_MISALIGNED;
   if (((uintptr_t)logits_out & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
+  if ((format & 0xFF) == DQG_FMT_FP8_E4M3 && !use_fused(T, H, I, E, k, format))
+    return DQG_ERR_UNSUPPORTED;  // FP8 weights: single launch only
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   char* b = static_cast<char*>(workspace);
   if (use_fused(T, H, I, E, k, format) && dqg::fused_router_supported(E, T))
@@ -432,7 +439,8 @@ int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int gr
                        int format, float* out, hipStream_t stream) {
   if (!w || !s || !out) return DQG_ERR_INVALID_ARG;
   if (K < 2 || N < 1) return DQG_ERR_INVALID_ARG;
-  if (format != DQG_FMT_INT4 && format != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;
+  if (format != DQG_FMT_INT4 && format != DQG_FMT_FP4_E2M1 && format != DQG_FMT_FP8_E4M3)
+    return DQG_ERR_UNSUPPORTED;
   if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
   if (K % group || N % 16) return DQG_ERR_UNSUPPORTED;
   if (!aligned16(w) || !aligned16(s) || !aligned16(out)) return DQG_ERR_MISALIGNED;

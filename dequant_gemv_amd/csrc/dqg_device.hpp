@@ -33,7 +33,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum { FMT_INT4 = 0, FMT_FP4 = 1 };
+enum { FMT_INT4 = 0, FMT_FP4 = 1, FMT_FP8 = 2 };
 enum { X_BF16 = 0, X_F16 = 1, X_F32 = 2 };
 
 constexpr int BLK_ROWS = 16;  // byte rows per block (32 K indices)
@@ -58,6 +58,17 @@ template <int B>
 __device__ __forceinline__ f32x2_t fp4_pair_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
 }
+// FP8 E4M3 (OCP) bytes 2W and 2W+1 of w -> bf16 / f32 pair (exact: 4 significant bits)
+template <int W>
+__device__ __forceinline__ bf16x2_t fp8_pair_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, W);
+}
+template <int W>
+__device__ __forceinline__ f32x2_t fp8_pair_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, W);
+}
+// K indices per stored byte
+__host__ __device__ constexpr int fmt_kb(int fmt) { return fmt == FMT_FP8 ? 1 : 2; }
 // byte B of w -> fp16 pair (1024 + low nibble, 64 + high nibble)
 template <int B>
 __device__ __forceinline__ f16x2_t int4_pair_f16_biased(uint32_t w) {

@@ -102,6 +102,46 @@ __device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[ROWS], const uint32
   }
 }
 
+// FP8 gate_up rows: rows 2i and 2i+1 meet the x pair xr[i]; their bytes are interleaved per
+// column (v_perm_b32) so that one conversion gives the bf16 pair (w[2i][c], w[2i+1][c]).
+template <int ROWS>
+__device__ __forceinline__ void rows_dot_x_fp8(const uint4 (&wv)[ROWS], const uint32_t (&xr)[ROWS],
+                                               float (&acc)[16]) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 2; ++i) {
+    const uint32_t a[4] = {wv[2 * i].x, wv[2 * i].y, wv[2 * i].z, wv[2 * i].w};
+    const uint32_t b[4] = {wv[2 * i + 1].x, wv[2 * i + 1].y, wv[2 * i + 1].z, wv[2 * i + 1].w};
+    const bf16x2_t xp = __builtin_bit_cast(bf16x2_t, xr[i]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = __builtin_amdgcn_perm(b[q], a[q], 0x05010400u);  // a0 b0 a1 b1
+      const uint32_t hi = __builtin_amdgcn_perm(b[q], a[q], 0x07030602u);  // a2 b2 a3 b3
+      acc[4 * q + 0] = dot2_bf16(fp8_pair_bf16<0>(lo), xp, acc[4 * q + 0]);
+      acc[4 * q + 1] = dot2_bf16(fp8_pair_bf16<1>(lo), xp, acc[4 * q + 1]);
+      acc[4 * q + 2] = dot2_bf16(fp8_pair_bf16<0>(hi), xp, acc[4 * q + 2]);
+      acc[4 * q + 3] = dot2_bf16(fp8_pair_bf16<1>(hi), xp, acc[4 * q + 3]);
+    }
+  }
+}
+
+// FP8 down rows: row r (one h value) times its 16 bytes, decoded to f32 pairs
+template <int ROWS>
+__device__ __forceinline__ void rows_dot_f32_fp8(const uint4 (&wv)[ROWS], const float (&hf)[ROWS],
+                                                 float (&acc)[16]) {
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const uint32_t d[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2_t f0 = fp8_pair_f32<0>(d[q]), f1 = fp8_pair_f32<1>(d[q]);
+      acc[4 * q + 0] = fmaf(f0.x, hf[r], acc[4 * q + 0]);
+      acc[4 * q + 1] = fmaf(f0.y, hf[r], acc[4 * q + 1]);
+      acc[4 * q + 2] = fmaf(f1.x, hf[r], acc[4 * q + 2]);
+      acc[4 * q + 3] = fmaf(f1.y, hf[r], acc[4 * q + 3]);
+    }
+  }
+}
+
 template <int FMT, int ROWS>
 __device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[ROWS], const float (&hf)[2 * ROWS],
                                              float (&acc)[16]) {
@@ -194,7 +234,11 @@ __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n,
 
 template <int FMT, int GUR>
 __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
-  constexpr int KROWS = fx_krows(GUR), MAX_KS = fx_max_ks(GUR);
+  constexpr int KB = fmt_kb(FMT);                  // K indices per stored byte
+  constexpr int KROWS = fx_krows(GUR);             // gate_up byte rows per unit
+  constexpr int MAX_KS = 2048 / KB / KROWS;        // gate_up K splits (H <= 2048)
+  constexpr int NH = KB * FX_DROWS;                // h values of a down unit
+  constexpr int NPL = KB * FX_D_ROWS;              // h values of a down lane
   __shared__ int s_ids[32];
   __shared__ int s_key[32];
   __shared__ float s_w[32];
@@ -311,21 +355,30 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const int rl = tid >> 4, ch = tid & 15;
     const size_t ld = 2 * (size_t)I;
     const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
-    const int r0 = ks * KROWS + GUR * rl;
-    const uint8_t* w = a.wgu + (size_t)e * (H / 2) * ld;
+    const int r0 = ks * KROWS + GUR * rl;                // byte row; K index KB r0
+    const uint8_t* w = a.wgu + (size_t)e * (H / KB) * ld;
     uint4 wvv[GUR];
     load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
     float sf[16];
-    scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((2 * r0) / a.group) * ld + col0, sf);
+    scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((KB * r0) / a.group) * ld + col0,
+             sf);
     uint32_t xr[GUR];
-    const float corr = load_x_rows<FMT, GUR>(a.x + (size_t)tok * H, r0, xr);
+    float corr = 0.0f;
+    if constexpr (FMT == FMT_FP8)  // x pairs of K indices r0 .. r0 + GUR - 1
+      load_x_rows<FMT_FP4, GUR / 2>(a.x + (size_t)tok * H, r0 / 2,
+                                    reinterpret_cast<uint32_t(&)[GUR / 2]>(xr));
+    else
+      corr = load_x_rows<FMT, GUR>(a.x + (size_t)tok * H, r0, xr);
     // all loads above are issued before the first use (the scheduler would otherwise sink
     // some of them to their uses, which serializes memory round trips)
     __builtin_amdgcn_sched_barrier(0);
     float accb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
-    rows_dot_x<FMT, GUR>(wvv, xr, accb);
+    if constexpr (FMT == FMT_FP8)
+      rows_dot_x_fp8<GUR>(wvv, xr, accb);
+    else
+      rows_dot_x<FMT, GUR>(wvv, xr, accb);
     // reduce the 16 row-lanes; thread i then owns partial column i (i < 128 gate, else up)
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = sf[c] * (accb[c] + corr);
@@ -350,7 +403,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   const int rl = tid >> 3, ch = tid & 7;
   const int col0 = 128 * mt + 16 * ch;
   const int R = c * FX_DROWS + FX_D_ROWS * rl;   // row in the concatenated slot list
-  const int rows_per_slot = I / 2;
+  const int rows_per_slot = I / KB;
   const bool active = R < S * rows_per_slot;
   const int sl = active ? R / rows_per_slot : tok * k;  // slot of the row
   const int j = sl - tok * k;                           // its rank within the token
@@ -360,7 +413,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // gate/up partial of this unit's range is published, so that the gate_up units, which are
   // on the critical path, have the memory bandwidth to themselves until then.
   if (a.hold_down) {
-    const int f0 = 2 * FX_DROWS * c;
+    const int f0 = NH * c;
     if (tid == 0 && f0 < S * I) {
       const int jj = f0 / I, n = f0 - jj * I;
       const float* p = gpart + ((size_t)((jj * NT + (n >> 7)) * KS + KS - 1)) * 256 + (n & 127);
@@ -376,14 +429,15 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   if (active) {
     const int e = s_ids[j];
     load_rows(a.wd + (size_t)e * rows_per_slot * H + (size_t)r0 * H + col0, H, wvv);
-    scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((2 * r0) / a.group) * H + col0, sf);
+    scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((KB * r0) / a.group) * H + col0,
+             sf);
   }
-  // gather h for this unit's rows: flat h index f = 2 R covers 2 FX_DROWS values from
-  // 2 FX_DROWS c on; thread t < FX_DROWS owns f = 2 FX_DROWS c + 2t, +1 (two columns of one
-  // slot); the KS partial gate and up pairs are polled together and summed in ascending ks
-  float* hl = s_red;  // 2 FX_DROWS floats, reused as the reduction buffer afterwards
-  if (tid < FX_DROWS) {
-    const int f = 2 * FX_DROWS * c + 2 * tid;
+  // gather h for this unit's rows: flat h index f = KB R covers the NH values from NH c on;
+  // thread t < NH / 2 owns f = NH c + 2t, +1 (two columns of one slot); the KS partial gate
+  // and up pairs are polled together and summed in ascending ks
+  float* hl = s_red;  // NH floats, reused as the reduction buffer afterwards
+  if (tid < NH / 2) {
+    const int f = NH * c + 2 * tid;
     float2 h2 = make_float2(0.0f, 0.0f);
     if (f < S * I) {
       const int jj = f / I, n = f - jj * I, nt = n >> 7, nc = n & 127;
@@ -430,10 +484,10 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
   if (active) {
-    float hf[2 * FX_D_ROWS];
+    float hf[2 * FX_D_ROWS];  // the lane's NPL h values
 #pragma unroll
-    for (int i = 0; i < FX_D_ROWS / 2; ++i) {
-      const float4 v = reinterpret_cast<const float4*>(hl)[(FX_D_ROWS / 2) * rl + i];
+    for (int i = 0; i < NPL / 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(hl)[(NPL / 4) * rl + i];
       hf[4 * i + 0] = v.x;
       hf[4 * i + 1] = v.y;
       hf[4 * i + 2] = v.z;
@@ -448,7 +502,10 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     float accb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) accb[q] = 0.0f;
-    rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
+    if constexpr (FMT == FMT_FP8)
+      rows_dot_f32_fp8<FX_D_ROWS>(wvv, reinterpret_cast<const float(&)[FX_D_ROWS]>(hf), accb);
+    else
+      rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
     const float wj = s_w[j];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = wj * (sf[q] * (accb[q] + corr));
@@ -498,67 +555,86 @@ bool fused_supported(int H, int I, int k) {
 }
 
 // T > 1: a token's down rows must fill whole chunks, so that no chunk spans two tokens
-bool fused_supported_t(int T, int H, int I, int k) {
+bool fused_supported_t(int T, int H, int I, int k, int fmt) {
   return fused_supported(H, I, k) && T >= 1 && T <= FX_MAX_T &&
-         (T == 1 || (k * (I / 2)) % FX_DROWS == 0);
+         (T == 1 || (k * (I / fmt_kb(fmt))) % FX_DROWS == 0);
 }
 
-// Workspace of the single-launch layer: one region per token count T (1 .. FX_MAX_T), each
-// with its call counter and its two copies of the exchange buffers.  Calls with different T
-// use different slots, so they must not share the buffers that are kept empty between calls.
-static size_t fused_region_bytes(int H, int I, int E, int k, int T) {
-  const int KS = H / 2 / fx_krows(fx_gu_rows(H, T)), NT = I / 128, n_mt = H / 128;
-  const int NC = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
-  size_t o = 256;                                         // call counter
-  o += 2 * (size_t)T * k * NT * KS * 256 * 4;             // gate/up partial rows
-  o += 2 * (size_t)n_mt * NC * 128 * 4;                   // output partial rows
-  if (fused_router_supported(E, T))                       // router partial rows
-    o += 2 * (size_t)router_splits(H) * T * E * 4;
-  return (o + 255) & ~(size_t)255;
+// gate_up rows per lane: FP8 always 16 (one byte per K index: H / 256 splits at most 8)
+static inline int fx_gur(int H, int T, int fmt) { return fmt == FMT_FP8 ? 16 : fx_gu_rows(H, T); }
+
+// Sizes of one call's exchange buffers (T tokens, format class of fmt)
+struct FxSizes {
+  int ks, n_chunks, n_mt;
+  size_t gpart, ypart, rpart, total;
+};
+static FxSizes fx_sizes(int H, int I, int E, int k, int T, int fmt) {
+  FxSizes z{};
+  const int kb = fmt_kb(fmt);
+  z.ks = H / kb / fx_krows(fx_gur(H, T, fmt));
+  z.n_mt = H / 128;
+  z.n_chunks = (T * k * (I / kb) + FX_DROWS - 1) / FX_DROWS;
+  z.gpart = 2 * (size_t)T * k * (I / 128) * z.ks * 256 * 4;   // gate/up partial rows
+  z.ypart = 2 * (size_t)z.n_mt * z.n_chunks * 128 * 4;        // output partial rows
+  z.rpart = fused_router_supported(E, T) ? 2 * (size_t)router_splits(H) * T * E * 4 : 0;
+  z.total = (256 + z.gpart + z.ypart + z.rpart + 255) & ~(size_t)255;  // + call counters
+  return z;
+}
+
+// Workspace of the single-launch layer: per token count T (1 .. FX_MAX_T) one region for the
+// 4-bit formats and one for FP8, each with its call counters and its two copies of the
+// exchange buffers.  Calls with a different T or format class use different slots, so they
+// never meet buffers that another layout left non-empty.
+static size_t fused_pair_bytes(int H, int I, int E, int k, int T) {
+  return fx_sizes(H, I, E, k, T, FMT_FP4).total + fx_sizes(H, I, E, k, T, FMT_FP8).total;
 }
 
 size_t fused_ws_bytes(int H, int I, int E, int k, int t_max) {
   size_t o = 0;
-  for (int T = 1; T <= t_max && T <= FX_MAX_T; ++T) o += fused_region_bytes(H, I, E, k, T);
+  for (int T = 1; T <= t_max && T <= FX_MAX_T; ++T) o += fused_pair_bytes(H, I, E, k, T);
   return o;
 }
 
+// f.fmt must be set
 void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, bool with_router) {
   char* p = static_cast<char*>(ws);
-  for (int t = 1; t < T; ++t) p += fused_region_bytes(H, I, E, k, t);
+  for (int t = 1; t < T; ++t) p += fused_pair_bytes(H, I, E, k, t);
+  if (f.fmt == FMT_FP8) p += fx_sizes(H, I, E, k, T, FMT_FP4).total;
+  const FxSizes z = fx_sizes(H, I, E, k, T, f.fmt);
+  const int kb = fmt_kb(f.fmt);
   f.T = T;
   f.rs = router_splits(H);
   f.n_r = with_router ? f.rs : 0;
-  f.ks = H / 2 / fx_krows(fx_gu_rows(H, T));
-  f.n_mt = H / 128;
-  f.n_chunks = (T * k * (I / 2) + FX_DROWS - 1) / FX_DROWS;
+  f.ks = z.ks;
+  f.n_mt = z.n_mt;
+  f.n_chunks = z.n_chunks;
   f.chunks_per_token = f.n_chunks / T;
   f.n_a = T * k * (I / 128) * f.ks;
   f.n_b = f.n_mt * f.n_chunks;
-  f.hold_down = (size_t)k * (H / 2) * (2 * (size_t)I) >= ((size_t)1 << 20);
+  f.hold_down = (size_t)k * (H / kb) * (2 * (size_t)I) >= ((size_t)1 << 20);
   f.calls = reinterpret_cast<unsigned int*>(p);
   f.rcalls = reinterpret_cast<unsigned int*>(p + 64);  // the router's own parity counter
-  size_t o = 256;
-  f.gpart = reinterpret_cast<float*>(p + o);
-  o += 2 * (size_t)T * k * (I / 128) * f.ks * 256 * 4;
-  f.ypart = reinterpret_cast<float*>(p + o);
-  o += 2 * (size_t)f.n_mt * f.n_chunks * 128 * 4;
-  f.rpart = fused_router_supported(E, T) ? reinterpret_cast<float*>(p + o) : nullptr;
+  f.gpart = reinterpret_cast<float*>(p + 256);
+  f.ypart = reinterpret_cast<float*>(p + 256 + z.gpart);
+  f.rpart = z.rpart ? reinterpret_cast<float*>(p + 256 + z.gpart + z.ypart) : nullptr;
 }
 
 hipError_t launch_fused_layer(const FusedArgs& f, hipStream_t st) {
   const int grid = f.n_r + f.n_a + f.n_b;
-  const bool big = fx_gu_rows(f.H, f.T) == 16;
-  if (f.fmt == FMT_FP4) {
+  const bool big = fx_gur(f.H, f.T, f.fmt) == 16;
+  const dim3 g(grid), b(FX_THREADS);
+  if (f.fmt == FMT_FP8) {
+    hipLaunchKernelGGL((fused_layer_kernel<FMT_FP8, 16>), g, b, 0, st, f);
+  } else if (f.fmt == FMT_FP4) {
     if (big)
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 16>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 16>), g, b, 0, st, f);
     else
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8>), g, b, 0, st, f);
   } else {
     if (big)
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 16>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 16>), g, b, 0, st, f);
     else
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8>), dim3(grid), dim3(FX_THREADS), 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8>), g, b, 0, st, f);
   }
   return hipGetLastError();
 }

@@ -82,7 +82,7 @@ struct FusedArgs {
 // multi-launch path: T = 5 30 vs 45 us, T = 8 46 vs 55 us, T = 12 65 vs 68 us, T = 16 84 vs 78 us)
 constexpr int FX_MAX_T = 8;
 bool fused_supported(int H, int I, int k);
-bool fused_supported_t(int T, int H, int I, int k);
+bool fused_supported_t(int T, int H, int I, int k, int fmt);
 bool fused_router_supported(int E, int T);
 // exchange regions for T = 1 .. t_max (one per token count)
 size_t fused_ws_bytes(int H, int I, int E, int k, int t_max);

@@ -291,13 +291,20 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
                                                       int group, float* __restrict__ out) {
   // one thread per 4 bytes of one byte row
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t nq = (size_t)(K / 2) * (N / 4);
+  const size_t nq = (size_t)(K / fmt_kb(FMT)) * (N / 4);
   if (idx >= nq) return;
   const int r = (int)(idx / (N / 4));
   const int n = (int)(idx % (N / 4)) * 4;
   const uint32_t d = *reinterpret_cast<const uint32_t*>(w + (size_t)r * N + n);
   float lo[4], hi[4];
-  if constexpr (FMT == FMT_FP4) {
+  if constexpr (FMT == FMT_FP8) {  // one code per byte: row r is K index r
+    const f32x2_t p0 = fp8_pair_f32<0>(d), p1 = fp8_pair_f32<1>(d);
+    const float v[4] = {p0.x, p0.y, p1.x, p1.y};
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      out[(size_t)r * N + n + b] = v[b] * bf16_to_f32(s[(size_t)(r / group) * N + n + b]);
+    return;
+  } else if constexpr (FMT == FMT_FP4) {
     const bf16x2_t p[4] = {fp4_pair_bf16<0>(d), fp4_pair_bf16<1>(d), fp4_pair_bf16<2>(d),
                            fp4_pair_bf16<3>(d)};
 #pragma unroll
@@ -358,9 +365,12 @@ hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, in
 
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st) {
-  const size_t nq = (size_t)(K / 2) * (N / 4);
+  const size_t nq = (size_t)(K / fmt_kb(fmt)) * (N / 4);
   const int grid = (int)((nq + 255) / 256);
-  if (fmt == FMT_FP4)
+  if (fmt == FMT_FP8)
+    hipLaunchKernelGGL(dequant_kernel<FMT_FP8>, dim3(grid), dim3(256), 0, st, w, s, K, N, group,
+                       out);
+  else if (fmt == FMT_FP4)
     hipLaunchKernelGGL(dequant_kernel<FMT_FP4>, dim3(grid), dim3(256), 0, st, w, s, K, N, group,
                        out);
   else

@@ -52,8 +52,11 @@ typedef enum dqg_status {
 } dqg_status;
 
 typedef enum dqg_format {
-  DQG_FMT_INT4 = 0,     /* value = nibble - 8            */
-  DQG_FMT_FP4_E2M1 = 1  /* value = E2M1(nibble)          */
+  DQG_FMT_INT4 = 0,     /* value = nibble - 8                                           */
+  DQG_FMT_FP4_E2M1 = 1, /* value = E2M1(nibble)                                         */
+  DQG_FMT_FP8_E4M3 = 2  /* value = E4M3(byte), one byte per weight: packed matrices are
+                           [K, N] instead of [K/2, N]; the MoE layer calls only, on their
+                           single launch (see moe_fp4_layer)                             */
 } dqg_format;
 
 /* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
@@ -143,6 +146,11 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
  * expert itself (an expert chosen by several tokens is read once per token).  Other calls
  * route inside the schedule of the multi-launch path.  ids_out (int32 [T, k]) and
  * weights_out (fp32 [T, k]) are optional outputs of the routing (NULL to skip).
+ * DQG_FMT_FP8_E4M3 (FireEcho page, "Quantization Formats": an 8-bit FP format; read as OCP
+ * E4M3) takes w_gate_up uint8 [E, H, 2I] and w_down uint8 [E, I, H], one code per byte, with
+ * the same scales; it runs on the single launch only (for T > 1, k * I a multiple of 256)
+ * and returns DQG_ERR_UNSUPPORTED where that does not apply (also with DQG_PATH_NO_FUSED,
+ * and always from moe_fp4_ffn).  E4M3 codes S.1111.111 (NaN) give unspecified results.
  */
 int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
                   const uint8_t* w_gate_up, const uint16_t* s_gate_up, const uint8_t* w_down,
@@ -219,8 +227,8 @@ int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
 
 /*
  * packed_dequant_f32 -- TEST AID: dequantize one packed matrix with the same in-register
- * decode the compute kernels use.  w uint8 [K/2, N], s bf16 [K/G, N] -> out fp32 [K, N],
- * out[k, n] = value(nibble) * s[k/G, n], exact.
+ * decode the compute kernels use.  w uint8 [K/2, N] (FP8: [K, N]), s bf16 [K/G, N] -> out
+ * fp32 [K, N], out[k, n] = value(code[k, n]) * s[k/G, n], exact.
  */
 int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,
                        int format, float* out, hipStream_t stream);

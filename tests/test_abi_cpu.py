@@ -107,6 +107,22 @@ def test_moe_layer_validation():
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
 
 
+def test_fp8_outside_the_single_launch_is_rejected_before_launch():
+    # moe_fp4_ffn never takes FP8
+    assert _moe(fmt=B.FMT_FP8_E4M3) == B.DQG_ERR_UNSUPPORTED
+    f = B.LIB.moe_fp4_layer
+    def layer(T, fmt):
+        return f(A, A, T, 256, 128, 8, 2, A, A, A, A, 32, fmt, 0, A, 0, 0, A, 1 << 30, None)
+    assert layer(16, B.FMT_FP8_E4M3) == B.DQG_ERR_UNSUPPORTED                   # T > 8
+    assert layer(1, B.FMT_FP8_E4M3 | B.PATH_NO_FUSED) == B.DQG_ERR_UNSUPPORTED
+    assert layer(1, 3) == B.DQG_ERR_UNSUPPORTED                                 # no format 3
+    g = B.LIB.moe_fp4_layer_from_hidden
+    assert g(A, A, 16, 256, 128, 8, 2, A, A, A, A, 32, B.FMT_FP8_E4M3, 0, A, 0, 0, 0, A,
+             1 << 30, None) == B.DQG_ERR_UNSUPPORTED
+    d = B.LIB.packed_dequant_f32
+    assert d(A, A, 64, 64, 32, 3, A, None) == B.DQG_ERR_UNSUPPORTED
+
+
 def test_router_validation():
     f = B.LIB.router_logits
     q = B.router_logits_workspace_bytes(1, 2048, 128)

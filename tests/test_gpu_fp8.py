@@ -1,0 +1,119 @@
+"""GPU parity: FP8 E4M3 weights (one code per byte) through the single-launch layer.
+
+The decode is compared bit for bit (every finite code), the layer per element against the
+float64 oracle with the method's tolerance (|gpu - oracle| <= 1e-2 rms + 1 bf16 ulp), the
+routing exactly."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bits16, check_bf16, dev, upload_layer
+from oracle import moe_oracle as O
+from workloads import synth as S
+
+pytestmark = pytest.mark.gpu
+
+
+def _b():
+    from dequant_gemv_amd import binding
+    return binding
+
+
+def test_fp8_dequant_bit_exact_every_finite_code():
+    B = _b()
+    rng = np.random.default_rng(0)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K, N, G = 256, 254, 32
+    codes = np.stack([np.roll(finite, r) for r in range(K)]).astype(np.uint8)     # [K, N]
+    Np = 256  # pad N to a multiple of 16 with zero codes
+    w = np.zeros((K, Np), np.uint8)
+    w[:, :N] = codes
+    s = S.f32_to_bf16_bits(rng.uniform(0.001, 4.0, size=(K // G, Np)))
+    got = B.packed_dequant_f32(dev(w), dev(s), G, B.FMT_FP8_E4M3).cpu().numpy()
+    want = O.dequant(w, s, G, O.FMT_FP8).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def _fp8_layer(T, seed, residual=False):
+    cfg = S.Q30_FP8.with_T(T)
+    lg = S.moe_layer_logits(cfg, seed)
+    ids, _ = O.topk_route(lg, cfg.k)
+    L = S.make_moe_layer(cfg, seed, experts=np.unique(ids))
+    D = upload_layer(L, np.unique(ids))
+    res = S.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((T, cfg.H))) \
+        if residual else None
+    return cfg, L, D, res
+
+
+@pytest.mark.parametrize("T,seed,residual", [(1, 0, False), (1, 1, True), (2, 0, False),
+                                             (4, 2, True), (8, 3, False)])
+def test_fp8_layer_parity(T, seed, residual):
+    B = _b()
+    cfg, L, D, res = _fp8_layer(T, seed, residual)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+    out = B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                          D["s_d"], cfg.group, cfg.fmt,
+                          residual=None if res is None else dev(res).view(torch.bfloat16),
+                          ids_out=ids, weights_out=w)
+    torch.cuda.synchronize()
+    want, oids, ow = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                                 cfg.fmt, residual_bits=res)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=4e-6, atol=1e-7)
+    check_bf16(bits16(out), want, what=f"fp8 T={T}")
+
+
+def test_fp8_layer_from_hidden():
+    """The router inside the single launch with FP8 experts."""
+    B = _b()
+    cfg = S.Q30_FP8
+    wr = S.make_router_weights(cfg.H, cfg.E, seed=4)
+    L0 = S.make_moe_layer(cfg, 4, experts=[])
+    ids, _ = O.topk_route(O.router_logits(L0.x, wr), cfg.k, dtype=np.float64)
+    L = S.make_moe_layer(cfg, 4, experts=np.unique(ids))
+    D = upload_layer(L, np.unique(ids))
+    gids = torch.empty((1, cfg.k), dtype=torch.int32, device="cuda")
+    out = B.moe_fp4_layer_from_hidden(dev(L.x), dev(wr), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                                      D["s_d"], cfg.group, cfg.fmt, ids_out=gids)
+    torch.cuda.synchronize()
+    want, oids, _, _ = O.moe_layer_from_hidden(L.x, wr, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d,
+                                               cfg.group, cfg.fmt)
+    assert np.array_equal(gids.cpu().numpy(), oids)
+    check_bf16(bits16(out), want, what="fp8 from hidden")
+
+
+def test_formats_alternate_on_one_workspace():
+    """FP4, FP8 and INT4 single-launch calls at T = 1 and 4 on one workspace (FP8 has its own
+    exchange regions): every call reproduces its first result bit for bit."""
+    B = _b()
+    cases = {}
+    for name, base in (("fp4", S.Q30), ("fp8", S.Q30_FP8),
+                       ("int4", S.replace(S.Q30, fmt=S.FMT_INT4))):
+        for T in (1, 4):
+            cfg = base.with_T(T)
+            lg = S.moe_layer_logits(cfg, 9)
+            ids, _ = O.topk_route(lg, cfg.k)
+            L = S.make_moe_layer(cfg, 9, experts=np.unique(ids))
+            cases[(name, T)] = (cfg, L, upload_layer(L, np.unique(ids)))
+    ws = B.moe_workspace(4, 2048, 768, 128, 8, "cuda")
+
+    def run(key):
+        cfg, L, D = cases[key]
+        return bits16(B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"],
+                                      D["w_d"], D["s_d"], cfg.group, cfg.fmt, workspace=ws))
+
+    order = [("fp4", 1), ("fp8", 1), ("fp8", 4), ("int4", 1), ("fp4", 4), ("fp8", 1),
+             ("int4", 4), ("fp4", 1), ("fp8", 4), ("fp8", 1), ("fp4", 4), ("int4", 1)]
+    first = {}
+    for key in order:
+        got = run(key)
+        if key in first:
+            assert np.array_equal(got, first[key]), key
+        else:
+            first[key] = got
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    cfg, L, _ = cases[("fp8", 4)]
+    want, _, _ = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                             cfg.fmt)
+    check_bf16(first[("fp8", 4)], want, what="fp8 T=4 on the shared workspace")
