@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per MoE layer at T=1 and achieved HBM GB/s vs peak (Qwen3-30B-A3B shape)"
 HBM_PEAK_GBPS = 8000.0
-FP4, INT4 = 1, 0
+FP4, INT4, FP8 = 1, 0, 2
 
 # Synthetic workloads (sizes of the 30B-A3B and 512-expert MoE layers, a tiny INT4 layer and
 # the dense INT4 GEMV).  `layers` distinct weight sets are rotated so that one timed pass
@@ -54,6 +54,10 @@ WORKLOADS = {
                                 scales=(0.002, 0.01), logits="router", layers=48),
     "q30_router_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                                 scales=(0.002, 0.01), logits="router", layers=48),
+    "q30_fp8_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
+                             scales=(0.002, 0.01), logits="normal", layers=48),
+    "q30_fp8_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
+                             scales=(0.002, 0.01), logits="normal+bias", layers=24),
     "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
                               scales=(0.005, 0.02), logits="normal", layers=48),
     "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),
@@ -71,9 +75,10 @@ KERNEL_SOURCES = {
 }
 
 
-def expert_bytes(H, I, G):
-    """Packed bytes + bf16 scales of one expert (gate_up and down)."""
-    return (H // 2) * (2 * I) + (H // G) * (2 * I) * 2 + (I // 2) * H + (I // G) * H * 2
+def expert_bytes(H, I, G, kb=2):
+    """Packed bytes + bf16 scales of one expert (gate_up and down); kb = K indices per byte
+    (2 for the 4-bit formats, 1 for FP8)."""
+    return (H // kb) * (2 * I) + (H // G) * (2 * I) * 2 + (I // kb) * H + (I // G) * H * 2
 
 
 def active_bytes(H, I, G, k):
@@ -111,6 +116,16 @@ def _logits(w, g, device):
     return lg
 
 
+def _codes(w, shape, g, device):
+    """Packed weight bytes: uniform over 0..255 (4-bit formats: every nibble uniform), or
+    for FP8 the E4M3 codes of N(0, 2) values (torch's float8_e4m3fn cast)."""
+    import torch
+    if w["fmt"] == FP8:
+        v = 2.0 * torch.randn(shape, device=device, generator=g)
+        return v.to(torch.float8_e4m3fn).view(torch.uint8)
+    return torch.randint(0, 256, shape, dtype=torch.uint8, device=device, generator=g)
+
+
 def build_moe_workload(w, seed: int = 0, device="cuda"):
     """Layer weight sets drawn on the device: packed bytes uniform over 0..255 (every
     nibble uniform), scales uniform in the workload's range rounded to bf16, x ~ N(0,1)
@@ -118,17 +133,16 @@ def build_moe_workload(w, seed: int = 0, device="cuda"):
     router weight W_r ~ N(0, 1/sqrt(H)) in bf16 [H, E] per layer instead of logits."""
     import torch
     T, E, H, I, G = w["T"], w["E"], w["H"], w["I"], w["group"]
+    kb = 1 if w["fmt"] == FP8 else 2
     lo, hi = w["scales"]
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     out = []
     for _ in range(w["layers"]):
         out.append(dict(
-            w_gu=torch.randint(0, 256, (E, H // 2, 2 * I), dtype=torch.uint8, device=device,
-                               generator=g),
+            w_gu=_codes(w, (E, H // kb, 2 * I), g, device),
             s_gu=_bf16_scales((E, H // G, 2 * I), lo, hi, g, device),
-            w_d=torch.randint(0, 256, (E, I // 2, H), dtype=torch.uint8, device=device,
-                              generator=g),
+            w_d=_codes(w, (E, I // kb, H), g, device),
             s_d=_bf16_scales((E, I // G, H), lo, hi, g, device),
             logits=None if w["logits"] == "router" else _logits(w, g, device),
             wr=(torch.randn((H, E), device=device, generator=g) / H ** 0.5).to(torch.bfloat16)
@@ -262,7 +276,7 @@ def distinct_experts(logits, k):
 def bench_moe(w, args, dev, stream, B):
     import torch
     T, E, H, I, k, G = (w[s] for s in ("T", "E", "H", "I", "k", "group"))
-    fmt = B.FMT_FP4_E2M1 if w["fmt"] == FP4 else B.FMT_INT4
+    fmt = {FP4: B.FMT_FP4_E2M1, INT4: B.FMT_INT4, FP8: B.FMT_FP8_E4M3}[w["fmt"]]
     flags = {"auto": 0, "unfused": B.PATH_NO_FUSED, "gemv": B.PATH_FORCE_GEMV | B.PATH_NO_FUSED,
              "mfma": B.PATH_FORCE_MFMA | B.PATH_NO_FUSED}[args.path]
     x, layers = build_moe_workload(w, device=dev)
@@ -317,7 +331,7 @@ def bench_moe(w, args, dev, stream, B):
     stream.synchronize()
     eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
 
-    per_expert = expert_bytes(H, I, G)
+    per_expert = expert_bytes(H, I, G, 1 if w["fmt"] == FP8 else 2)
     lgs = [L["logits"] if not router else x.float() @ L["wr"].float() for L in layers]
     n_active = [distinct_experts(lg, k) for lg in lgs]
     abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
@@ -326,7 +340,7 @@ def bench_moe(w, args, dev, stream, B):
     # the single-launch layer takes T <= 8 (for T > 1 a token's down rows must fill whole
     # 256-row chunks), E <= 512, H % 256 == 0, H <= 2048, I % 128 == 0
     fused = (args.path == "auto" and T <= 8 and E <= 512 and H % 256 == 0 and H <= 2048
-             and I % 128 == 0 and (T == 1 or (k * (I // 2)) % 256 == 0))
+             and I % 128 == 0 and (T == 1 or (k * (I // (1 if w["fmt"] == FP8 else 2))) % 256 == 0))
     gbps = abytes / (us_per_layer * 1e-6) / 1e9
     # the single-launch path runs the whole layer in one kernel, so its average duration
     # is the timed region (events on the replay stream) / launches; the multi-launch path
@@ -350,7 +364,7 @@ def bench_moe(w, args, dev, stream, B):
         roofline["router_in_launch"] = fused and E <= 128 and E % 8 == 0 and T <= 4
         roofline["router_call_then_layer_us"] = round(separate_us, 3)
     config = {"workload": args.workload, "T": T, "E": E, "H": H, "I": I, "k": k,
-              "format": "fp4_e2m1" if w["fmt"] == FP4 else "int4", "group": G,
+              "format": {FP4: "fp4_e2m1", INT4: "int4", FP8: "fp8_e4m3"}[w["fmt"]], "group": G,
               "layers_per_step": n_layers, "chained": chain, "path": args.path,
               "active_experts_per_layer_mean": round(sum(n_active) / n_layers, 2),
               "active_bytes_per_layer": round(abytes)}
