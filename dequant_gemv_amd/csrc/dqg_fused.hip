@@ -10,19 +10,23 @@
 // 128-byte lines and exchange data with as few round trips as possible.
 //
 // Slots s = t k + j (token t, rank j).  Every workgroup first routes its token itself (one
-// wavefront, threshold + compaction + rank selection; no other workgroup is waited for).
-// Workgroups (256 threads, 4 waves), every lane owning 16 columns x 8 byte rows:
+// wavefront, threshold + compaction + rank selection; no other workgroup is waited for) --
+// from the logits, or from the partial logits of the router units, which then come first in
+// the grid (the router GEMV x W_r, 128 rows of W_r each).  A byte row holds KB = 2 K indices
+// (4-bit formats) or 1 (FP8).
+// Workgroups (256 threads, 4 waves), every lane owning 16 columns x a few byte rows:
 //   gate_up units (s, nt, ks): slot s, h columns [128 nt, 128 nt + 128) -- 128 bytes of
 //     gate and 128 bytes of up per byte row (16 lanes) -- over 16 GUR byte rows from
-//     16 GUR ks on (16 row-lanes x GUR rows; GUR = 8 for one token, 16 for several).  Each
-//     publishes its partial gate/up row and exits; gate_up units never wait.  (A slot is one unit set: an expert chosen by
-//     two tokens is read twice, mostly from cache the second time.)
+//     16 GUR ks on (16 row-lanes x GUR rows; GUR = 8 for one token with 4-bit weights, 16
+//     otherwise).  Each publishes its partial gate/up row and exits; gate_up units never
+//     wait.  (A slot is one unit set: an expert chosen by two tokens is read twice, mostly
+//     from cache the second time.)
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
 //     rows); for T > 1 a token's rows fill whole chunks.  On layers with >= 1 MiB of gate_up
 //     weights per token, their weight loads wait for the first gate/up partial of their
 //     range (the gate_up loads, which are on the critical path, get the bandwidth first);
-//     then the threads gather the KS partial gate/up pairs of the unit's 512 h values
+//     then the threads gather the KS partial gate/up pairs of the unit's 256 KB h values
 //     (ascending ks), form h = SiLU(g)*u into LDS, and every lane scales its sum by its slot
 //     weight.  A token's chunks publish partial output rows, except its last chunk of each
 //     column tile, which gathers them in ascending c, adds its own and the residual, and

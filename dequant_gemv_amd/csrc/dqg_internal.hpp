@@ -52,7 +52,7 @@ struct GemvArgs {
   int* err;             // error word (bit 1: a wait gave up), may be null
 };
 
-// Single-launch layer for T <= 4 (routing + expert FFN + combine); see dqg_fused.hip.
+// Single-launch layer for T <= FX_MAX_T (routing + expert FFN + combine); see dqg_fused.hip.
 struct FusedArgs {
   const uint16_t* x;
   const float* logits;  // fp32 [T, E], or null when the router units compute them

@@ -1,6 +1,6 @@
 // HIP kernels for gfx950: top-k routing, the device-built expert schedule and the
 // dequantize test aid.  The expert kernels of the multi-launch MoE path and the dense GEMV
-// are in dqg_experts.hip, the single-launch T = 1 layer in dqg_fused.hip.  Host launchers at the
+// are in dqg_experts.hip, the single-launch layer in dqg_fused.hip; also the router GEMV.  Host launchers at the
 // bottom; the C ABI lives in dqg_api.cpp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
