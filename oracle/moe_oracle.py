@@ -22,6 +22,13 @@ What each function follows (page titles as printed at the head of each page):
   cache); as a weight format its element is read as OCP FP8 E4M3 (sign bit, 4 exponent bits
   with bias 7, 3 mantissa bits; exponent field 0 is subnormal; S.1111.111 is NaN and there
   is no infinity), one byte per weight, ``[E, K, N]`` with the same bf16 group scales.
+* INT2 cold experts -- the same table lists a scalar 2-bit INT2 format for the coldest
+  experts next to the 4-bit format of the hot ones (an engine that demotes experts by age).
+  The pages give no zero point or packing; read as: code n in 0..3 means n - 2, four codes
+  per byte with K index 4r + i in bits 2i..2i+1 of byte row r (low bits first, like the
+  nibbles), the same bf16 group scales.  A layer may mix formats per expert (a table of E
+  entries); every expert keeps the 4-bit slab ``[K/2, N]`` and an INT2 expert's ``[K/4, N]``
+  bytes fill the first K/4 rows of its slab.
 * INT4 values -- symmetric, ``nibble - 8``; the page's simplified snippet multiplies the
   raw nibble by the scale, which is not used (it is labelled a simplification).
 * group scales -- one bf16 scale per ``group`` consecutive K indices and per column.
@@ -53,6 +60,7 @@ import numpy as np
 FMT_INT4 = 0
 FMT_FP4 = 1
 FMT_FP8 = 2
+FMT_INT2 = 3
 
 
 # ------------------------------------------------------------------------------------
@@ -87,6 +95,11 @@ def e4m3_value(code: int) -> float:
     return math.copysign(mag, -1.0 if sign else 1.0)
 
 
+def int2_value(code: int) -> float:
+    """INT2: stored code n in 0..3 means n - 2."""
+    return float(code - 2)
+
+
 def int4_value(code: int) -> float:
     """Symmetric INT4: stored nibble n means n - 8."""
     return float(code - 8)
@@ -96,6 +109,8 @@ def decode_table(fmt: int) -> np.ndarray:
     """Value of every code: 16 entries (4-bit formats) or 256 (FP8; NaN codes give NaN)."""
     if fmt == FMT_FP8:
         return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    if fmt == FMT_INT2:
+        return np.array([int2_value(c) for c in range(4)], dtype=np.float64)
     if fmt not in (FMT_FP4, FMT_INT4):
         raise ValueError(fmt)
     fn = e2m1_value if fmt == FMT_FP4 else int4_value
@@ -103,8 +118,18 @@ def decode_table(fmt: int) -> np.ndarray:
 
 
 def codes_per_byte(fmt: int) -> int:
-    """K indices per stored byte: 2 for the 4-bit formats, 1 for FP8."""
-    return 1 if fmt == FMT_FP8 else 2
+    """K indices per stored byte: 2 for the 4-bit formats, 1 for FP8, 4 for INT2."""
+    return {FMT_FP8: 1, FMT_INT2: 4}.get(fmt, 2)
+
+
+def unpack_codes2(packed: np.ndarray) -> np.ndarray:
+    """INT2 bytes ``[K/4, N]`` -> codes ``[K, N]``: bits 2i..2i+1 of byte row r give K index
+    4r + i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((4 * p.shape[0], p.shape[1]), dtype=np.uint8)
+    for i in range(4):
+        codes[i::4, :] = (p >> (2 * i)) & 3
+    return codes
 
 
 def bf16_to_f64(bits) -> np.ndarray:
@@ -145,7 +170,12 @@ def dequant(packed: np.ndarray, scale_bits: np.ndarray, group: int, fmt: int,
     if cols is not None:
         packed = packed[:, cols]
         scale_bits = scale_bits[:, cols]
-    codes = np.asarray(packed, dtype=np.uint8) if fmt == FMT_FP8 else unpack_codes(packed)
+    if fmt == FMT_FP8:
+        codes = np.asarray(packed, dtype=np.uint8)
+    elif fmt == FMT_INT2:
+        codes = unpack_codes2(packed)
+    else:
+        codes = unpack_codes(packed)
     K = codes.shape[0]
     assert K % group == 0 and scale_bits.shape[0] == K // group
     vals = decode_table(fmt)[codes]
@@ -194,22 +224,34 @@ def silu(g: np.ndarray) -> np.ndarray:
 
 
 class ExpertCache:
-    """Dequantized experts of one layer, built on first use (the oracle never fuses)."""
+    """Dequantized experts of one layer, built on first use (the oracle never fuses).
+    ``expert_fmt`` (optional, [E]) gives each expert's format; an INT2 expert's codes are
+    the first K/4 byte rows of its slab."""
 
-    def __init__(self, w_gu, s_gu, w_d, s_d, group: int, fmt: int):
+    def __init__(self, w_gu, s_gu, w_d, s_d, group: int, fmt: int, expert_fmt=None):
         self.w_gu, self.s_gu, self.w_d, self.s_d = w_gu, s_gu, w_d, s_d
         self.group, self.fmt = group, fmt
+        self.expert_fmt = None if expert_fmt is None else np.asarray(expert_fmt)
         self._gu: Dict[int, np.ndarray] = {}
         self._d: Dict[int, np.ndarray] = {}
 
+    def _fmt(self, e: int) -> int:
+        return self.fmt if self.expert_fmt is None else int(self.expert_fmt[e])
+
+    def _deq(self, w, s, e: int) -> np.ndarray:
+        f = self._fmt(e)
+        if f == FMT_INT2:
+            w = w[: (s.shape[0] * self.group) // 4]
+        return dequant(w, s, self.group, f)
+
     def gate_up(self, e: int) -> np.ndarray:
         if e not in self._gu:
-            self._gu[e] = dequant(self.w_gu[e], self.s_gu[e], self.group, self.fmt)
+            self._gu[e] = self._deq(self.w_gu[e], self.s_gu[e], e)
         return self._gu[e]
 
     def down(self, e: int) -> np.ndarray:
         if e not in self._d:
-            self._d[e] = dequant(self.w_d[e], self.s_d[e], self.group, self.fmt)
+            self._d[e] = self._deq(self.w_d[e], self.s_d[e], e)
         return self._d[e]
 
 
@@ -223,14 +265,15 @@ def expert_ffn(x_row: np.ndarray, W_gu: np.ndarray, W_d: np.ndarray) -> np.ndarr
 
 
 def moe_ffn(x_bits, ids, weights, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
-            residual_bits=None, cache: Optional[ExpertCache] = None) -> np.ndarray:
+            residual_bits=None, cache: Optional[ExpertCache] = None,
+            expert_fmt=None) -> np.ndarray:
     """out[t] = residual[t] + sum_j weights[t, j] * FFN_{ids[t, j]}(x[t]), j ascending.
     Returns the unrounded float64 ``[T, H]``."""
     x = bf16_to_f64(x_bits)
     T, H = x.shape
     ids = np.asarray(ids)
     wts = np.asarray(weights, dtype=np.float64)
-    c = cache or ExpertCache(w_gu, s_gu, w_d, s_d, group, fmt)
+    c = cache or ExpertCache(w_gu, s_gu, w_d, s_d, group, fmt, expert_fmt)
     out = np.zeros((T, H), dtype=np.float64) if residual_bits is None else \
         bf16_to_f64(residual_bits).copy()
     for t in range(T):
@@ -243,11 +286,12 @@ def moe_ffn(x_bits, ids, weights, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
 
 
 def moe_layer(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
-              residual_bits=None, cache: Optional[ExpertCache] = None):
+              residual_bits=None, cache: Optional[ExpertCache] = None, expert_fmt=None):
     """Route, then the expert FFN and the weighted combine.
     Returns ``(out float64 [T, H], ids, weights)``."""
     ids, w = topk_route(logits, k)
-    out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache)
+    out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache,
+                  expert_fmt)
     return out, ids, w
 
 

@@ -50,7 +50,15 @@ def e4m3_fraction(code: int) -> Fraction:
 
 
 def dequant_exact(packed, scales, group: int, fmt: str):
-    """packed [K/2][N] bytes (fp8: [K][N]), scales [K/G][N] bf16 bits -> exact W [K][N]."""
+    """packed [K/2][N] bytes (fp8: [K][N]; int2: [K/4][N], or a 4-bit slab whose first
+    K/4 rows hold the codes), scales [K/G][N] bf16 bits -> exact W [K][N] (Fractions)."""
+    if fmt == "int2":
+        K = len(scales) * group
+        out = []
+        for k in range(K):
+            out.append([Fraction(((int(packed[k // 4][n]) >> (2 * (k % 4))) & 3) - 2) *
+                        bf16_fraction(scales[k // group][n]) for n in range(len(packed[0]))])
+        return out
     if fmt == "fp8":
         return [[e4m3_fraction(int(b)) * bf16_fraction(scales[k // group][n])
                  for n, b in enumerate(row)] for k, row in enumerate(packed)]
@@ -75,14 +83,16 @@ def topk_exact(row, k: int):
     return ids, [v / s for v in ex]
 
 
-def moe_exact(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: str,
+def moe_exact(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt,
               residual_bits=None):
-    """Returns (out [T][H] float64, ids [T][k], weights [T][k])."""
+    """fmt: one format name, or a list of E names (per-expert formats).
+    Returns (out [T][H] float64, ids [T][k], weights [T][k])."""
     T, H = len(x_bits), len(x_bits[0])
     E = len(w_gu)
     I = len(w_gu[0][0]) // 2
-    Wgu = [dequant_exact(w_gu[e], s_gu[e], group, fmt) for e in range(E)]
-    Wd = [dequant_exact(w_d[e], s_d[e], group, fmt) for e in range(E)]
+    fmts = fmt if isinstance(fmt, list) else [fmt] * E
+    Wgu = [dequant_exact(w_gu[e], s_gu[e], group, fmts[e]) for e in range(E)]
+    Wd = [dequant_exact(w_d[e], s_d[e], group, fmts[e]) for e in range(E)]
     out, all_ids, all_w = [], [], []
     for t in range(T):
         x = [bf16_fraction(v) for v in x_bits[t]]

@@ -322,6 +322,78 @@ def test_fp8_moe_matches_exact_bruteforce(seed):
 
 
 # --------------------------------------------------------------------------------------
+# INT2 cold experts and mixed per-expert formats
+# --------------------------------------------------------------------------------------
+def test_int2_hand_worked_bytes():
+    rows = []
+    for line in open(os.path.join(HERE, "golden", "int2_worked.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            b, *v = line.split()
+            rows.append((int(b, 16), [float(x) for x in v]))
+    packed = np.array([[b] for b, _ in rows], np.uint8)            # [R, 1]
+    K = 4 * len(rows)
+    W = O.dequant(packed, np.full((K // 4, 1), 0x3F80, np.uint16), 4, O.FMT_INT2)  # scale 1
+    assert W[:, 0].tolist() == [x for _, v in rows for x in v]
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_int2_dequant_matches_exact_bruteforce(seed):
+    rng = np.random.default_rng(600 + seed)
+    K, N, G = 64, 8, 32
+    packed = rng.integers(0, 256, size=(K // 4, N), dtype=np.uint8)
+    scales = S.f32_to_bf16_bits(rng.uniform(0.1, 1.0, size=(K // G, N)))
+    W = O.dequant(packed, scales, G, O.FMT_INT2)
+    ex = BF.dequant_exact(packed.tolist(), scales.tolist(), G, "int2")
+    assert all(W[kk, n] == float(ex[kk][n]) for kk in range(K) for n in range(N))
+
+
+def test_int2_expert_equals_int4_expert_with_shifted_codes():
+    """INT2 code n and INT4 nibble n + 6 both mean n - 2: a layer whose experts are INT2 gives
+    exactly the output of the same layer stored as INT4 (pins the 2-bit order and offset)."""
+    rng = np.random.default_rng(17)
+    T, E, k, G, H, I = 3, 4, 2, 32, 64, 32
+    x = S.f32_to_bf16_bits(rng.standard_normal((T, H)))
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    c_gu = rng.integers(0, 4, size=(E, H, 2 * I))
+    c_d = rng.integers(0, 4, size=(E, I, H))
+    s_gu = S.f32_to_bf16_bits(rng.uniform(0.05, 0.5, size=(E, H // G, 2 * I)))
+    s_d = S.f32_to_bf16_bits(rng.uniform(0.05, 0.5, size=(E, I // G, H)))
+
+    def pack2(c):  # [.., K, N] codes 0..3 -> 4-bit slab [.., K/2, N] with the first K/4 rows
+        K = c.shape[-2]
+        slab = np.zeros(c.shape[:-2] + (K // 2, c.shape[-1]), np.uint8)
+        for i in range(4):
+            slab[..., : K // 4, :] |= (c[..., i::4, :] << (2 * i)).astype(np.uint8)
+        return slab
+    int4 = lambda c: S.pack_nibbles((c + 6).astype(np.uint8))
+    o2, i2, _ = O.moe_layer(x, lg, k, pack2(c_gu), s_gu, pack2(c_d), s_d, G, O.FMT_FP4,
+                            expert_fmt=np.full(E, O.FMT_INT2))
+    o4, i4, _ = O.moe_layer(x, lg, k, np.stack([int4(c) for c in c_gu]), s_gu,
+                            np.stack([int4(c) for c in c_d]), s_d, G, O.FMT_INT4)
+    assert np.array_equal(i2, i4)
+    assert np.array_equal(o2, o4)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mixed_formats_match_exact_bruteforce(seed):
+    rng = np.random.default_rng(700 + seed)
+    T, E, k, G, H, I = int(rng.integers(1, 4)), 4, 2, 4, 16, 8
+    x, lg, w_gu, s_gu, w_d, s_d = _tiny_random(rng, T, E, H, I, G, "fp4")
+    efmt = np.array([O.FMT_FP4, O.FMT_INT2, O.FMT_INT2, O.FMT_FP4], np.uint8)
+    for e in (1, 2):  # INT2 experts: codes in the first K/4 rows, the rest of the slab zero
+        w_gu[e, H // 4:] = 0
+        w_d[e, I // 4:] = 0
+    out, ids, w = O.moe_layer(x, lg, k, w_gu, s_gu, w_d, s_d, G, O.FMT_FP4, expert_fmt=efmt)
+    names = ["fp4", "int2", "int2", "fp4"]
+    bout, bids, bw = BF.moe_exact(x.tolist(), lg.tolist(), k, w_gu.tolist(), s_gu.tolist(),
+                                  w_d.tolist(), s_d.tolist(), G, names)
+    assert ids.tolist() == bids
+    scale = max(1e-300, float(np.sqrt(np.mean(np.square(bout)))))
+    assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
+
+
+# --------------------------------------------------------------------------------------
 # router logits from the hidden state
 # --------------------------------------------------------------------------------------
 @pytest.mark.parametrize("seed", range(4))

@@ -29,6 +29,7 @@ import numpy as np
 FMT_INT4 = 0  # value = (nibble - 8) * scale
 FMT_FP4 = 1   # value = E2M1(nibble) * scale
 FMT_FP8 = 2   # value = E4M3(byte) * scale, one byte per weight
+FMT_INT2 = 3  # value = (code - 2) * scale, four codes per byte (per-expert cold format)
 
 
 # --------------------------------------------------------------------------------------
@@ -79,6 +80,7 @@ class MoEConfig:
     zipf_s: float = 1.1
     layers: int = 1
     residual: bool = False          # chained stack: x_{l+1} = bf16(x_l + MoE_l(x_l))
+    int2_frac: float = 0.0          # share of experts stored as INT2 (cold experts)
 
     def with_T(self, T: int) -> "MoEConfig":
         return replace(self, T=T)
@@ -115,6 +117,7 @@ Q30 = MoEConfig("q30", T=1, E=128, H=2048, I=768, k=8, fmt=FMT_FP4, group=32,
                 scale_lo=0.002, scale_hi=0.01)
 Q30_BATCH = replace(Q30, name="q30_batch", T=16, logits="normal+bias")
 Q30_FP8 = replace(Q30, name="q30_fp8", fmt=FMT_FP8)
+Q30_MIXED = replace(Q30, name="q30_mixed", int2_frac=0.5)
 W512 = MoEConfig("w512", T=1, E=512, H=2048, I=512, k=10, fmt=FMT_FP4, group=32,
                  scale_lo=0.002, scale_hi=0.01, logits="zipf", layers=48, residual=True)
 GEMV_N = (256, 8192, 34816)
@@ -139,6 +142,7 @@ class MoELayer:
     w_d: np.ndarray              # uint8  [E, I/2, H]
     s_d: np.ndarray              # uint16 [E, I/G, H]
     meta: dict = field(default_factory=dict)
+    expert_fmt: Optional[np.ndarray] = None  # uint8 [E] per-expert format (mixed layers)
 
 
 def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
@@ -190,16 +194,37 @@ def make_moe_layer(cfg: MoEConfig, seed: int = 0, layer: int = 0, with_x: bool =
     s_d = np.zeros((E, I // G, H), np.uint16)
     codes = fp8_codes if cfg.fmt == FMT_FP8 else \
         (lambda g, shape: g.integers(0, 256, size=shape, dtype=np.uint8))
+    efmt = expert_formats(cfg, seed, layer)
     want = None if experts is None else set(int(e) for e in np.asarray(experts).ravel())
     for e in range(E):
         sub = rng.spawn(1)[0]
         if want is not None and e not in want:
             continue
+        if efmt is not None and efmt[e] == FMT_INT2:  # codes in the first K/4 slab rows
+            w_gu[e, : H // 4] = codes(sub, (H // 4, 2 * I))
+            s_gu[e] = _scales(sub, (H // G, 2 * I), cfg.scale_lo, cfg.scale_hi)
+            w_d[e, : I // 4] = codes(sub, (I // 4, H))
+            s_d[e] = _scales(sub, (I // G, H), cfg.scale_lo, cfg.scale_hi)
+            continue
         w_gu[e] = codes(sub, (H // b, 2 * I))
         s_gu[e] = _scales(sub, (H // G, 2 * I), cfg.scale_lo, cfg.scale_hi)
         w_d[e] = codes(sub, (I // b, H))
         s_d[e] = _scales(sub, (I // G, H), cfg.scale_lo, cfg.scale_hi)
-    return MoELayer(cfg, seed, x, logits, w_gu, s_gu, w_d, s_d, meta={"rng_seed": s})
+    return MoELayer(cfg, seed, x, logits, w_gu, s_gu, w_d, s_d, meta={"rng_seed": s},
+                    expert_fmt=efmt)
+
+
+def expert_formats(cfg: MoEConfig, seed: int = 0, layer: int = 0) -> Optional[np.ndarray]:
+    """Per-expert formats of a mixed layer: round(int2_frac E) experts, drawn from their own
+    stream ``default_rng([seed, layer, 0x12])``, are INT2, the rest the layer's format; None
+    when the layer has no INT2 experts."""
+    if cfg.int2_frac <= 0:
+        return None
+    n = int(round(cfg.int2_frac * cfg.E))
+    cold = np.random.default_rng([seed, layer, 0x12]).choice(cfg.E, size=n, replace=False)
+    f = np.full(cfg.E, cfg.fmt, np.uint8)
+    f[cold] = FMT_INT2
+    return f
 
 
 # --------------------------------------------------------------------------------------
