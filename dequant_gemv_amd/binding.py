@@ -26,6 +26,7 @@ DQG_ERR_HIP = -5
 FMT_INT4 = 0
 FMT_FP4_E2M1 = 1
 FMT_FP8_E4M3 = 2
+FMT_INT2 = 3
 PATH_FORCE_GEMV = 0x100
 PATH_FORCE_MFMA = 0x200
 PATH_NO_FUSED = 0x400
@@ -47,6 +48,8 @@ SIGNATURES = {
     "router_logits": (_I, [_P, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "moe_fp4_layer_from_hidden": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P,
                                        _P, _P, _P, _P, _Z, _P]),
+    "moe_fp4_layer_mixed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
+                                 _P, _P, _P, _Z, _P]),
     "packed_gemv_int4_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
@@ -249,6 +252,34 @@ def moe_fp4_layer_from_hidden(x, w_router, k: int, w_gate_up, s_gate_up, w_down,
         _ptr(x), _ptr(w_router), T, H, I, E, k, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down),
         _ptr(s_down), group, fmt | flags, _ptr(residual), _ptr(out), _ptr(logits_out),
         _ptr(ids_out), _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+def moe_fp4_layer_mixed(x, logits, k: int, w_gate_up, s_gate_up, w_down, s_down,
+                        expert_formats, group: int, residual=None, out=None, ids_out=None,
+                        weights_out=None, workspace=None, flags: int = 0) -> torch.Tensor:
+    """FP4 layer whose experts marked FMT_INT2 in expert_formats (uint8 [E]) hold INT2 codes
+    in the first quarter of their slab."""
+    T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, FMT_FP4_E2M1)
+    _need(logits, "logits", 4, (T, E), x.device)
+    _need(expert_formats, "expert_formats", 1, (E,), x.device)
+    if residual is not None:
+        _need(residual, "residual", 2, (T, H), x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", 2, (T, H), x.device)
+    if ids_out is not None:
+        _need(ids_out, "ids_out", 4, (T, k), x.device)
+    if weights_out is not None:
+        _need(weights_out, "weights_out", 4, (T, k), x.device)
+    if workspace is None:
+        workspace = moe_workspace(T, H, I, E, k, x.device)
+    _need(workspace, "workspace", 1, None, x.device)
+    _check("moe_fp4_layer_mixed", LIB.moe_fp4_layer_mixed(
+        _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down),
+        _ptr(s_down), _ptr(expert_formats), group, FMT_FP4_E2M1 | flags, _ptr(residual),
+        _ptr(out), _ptr(ids_out), _ptr(weights_out), _ptr(workspace), workspace.numel(),
+        _stream(x)))
     return out
 
 

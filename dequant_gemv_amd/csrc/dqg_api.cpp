@@ -198,8 +198,10 @@ bool use_fused(int T, int H, int I, int E, int k, int format) {
 int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const uint16_t* wr,
               float* logits_out, const uint8_t* wgu, const uint16_t* sgu, const uint8_t* wd,
               const uint16_t* sd, int group, int format, const uint16_t* res, uint16_t* out,
-              int32_t* ids_out, float* w_out, void* ws, hipStream_t st) {
+              int32_t* ids_out, float* w_out, void* ws, hipStream_t st,
+              const uint8_t* efmt = nullptr) {
   dqg::FusedArgs f{};
+  f.efmt = efmt;
   f.x = x; f.logits = logits; f.H = p.H; f.I = p.I; f.E = p.E; f.k = p.k; f.group = group;
   f.wr = logits ? nullptr : wr;
   f.logits_out = logits ? nullptr : logits_out;
@@ -405,6 +407,27 @@ int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T
   a.ids = a.ids_w;
   a.wts = a.wts_w;
   return run_moe(a, p, lg, stream);
+}
+
+int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, int I, int E,
+                        int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                        const uint8_t* w_down, const uint16_t* s_down,
+                        const uint8_t* expert_formats, int group, int format,
+                        const uint16_t* residual, uint16_t* out, int32_t* ids_out,
+                        float* weights_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!logits || !expert_formats) return DQG_ERR_INVALID_ARG;
+  int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
+                            format, residual, out, workspace, workspace_bytes);
+  if (rc != DQG_OK) return rc;
+  if ((format & 0xFF) != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;  // FP4 hot experts
+  if (!use_fused(T, H, I, E, k, format)) return DQG_ERR_UNSUPPORTED;   // single launch only
+  if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
+    return DQG_ERR_MISALIGNED;
+  const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
+  return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
+                   format, residual, out, ids_out, weights_out, workspace, stream,
+                   expert_formats);
 }
 
 size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group) {

@@ -106,6 +106,76 @@ __device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[ROWS], const uint32
   }
 }
 
+// INT2 (cold experts of a mixed FP4 layer): byte row q holds K indices 4q .. 4q+3 of one
+// column in bits 0-1, 2-3, 4-5, 6-7; code c means c - 2.  t_m = (d >> 2m) & 0x03030303 puts
+// code m of the 4 columns of dword d in its 4 bytes.  For the bf16 dot the codes become
+// bf16 128 + c (bits 0x4300 | c) in pairs (one v_perm_b32 + or); the 130 sum(x) this adds
+// is removed once per lane (corr).
+template <int J>
+__device__ __forceinline__ uint32_t int2_bf16_pair(uint32_t ta, uint32_t tb) {
+  // byte J of ta -> bits 0..7, byte J of tb -> bits 16..23, zeros elsewhere
+  return __builtin_amdgcn_perm(tb, ta, (0x0Cu << 24) | ((4u + J) << 16) | (0x0Cu << 8) | J) |
+         0x43004300u;
+}
+
+// gate_up: ROWS 4-bit-row equivalents = ROWS / 2 INT2 byte rows; x pairs xr[2i], xr[2i+1]
+// cover K indices 4i .. 4i+3 of the lane's range
+template <int ROWS>
+__device__ __forceinline__ float rows_dot_x_int2(const uint4 (&wv)[ROWS / 2],
+                                                 const uint32_t (&xr)[ROWS], float (&acc)[16]) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 2; ++i) {
+    const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+    const bf16x2_t xa = __builtin_bit_cast(bf16x2_t, xr[2 * i]);
+    const bf16x2_t xb = __builtin_bit_cast(bf16x2_t, xr[2 * i + 1]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t t0 = d[q] & 0x03030303u, t1 = (d[q] >> 2) & 0x03030303u;
+      const uint32_t t2 = (d[q] >> 4) & 0x03030303u, t3 = (d[q] >> 6) & 0x03030303u;
+#define DQG_I2(J)                                                                              \
+  acc[4 * q + J] = dot2_bf16(__builtin_bit_cast(bf16x2_t, int2_bf16_pair<J>(t0, t1)), xa,    \
+                             acc[4 * q + J]);                                                  \
+  acc[4 * q + J] = dot2_bf16(__builtin_bit_cast(bf16x2_t, int2_bf16_pair<J>(t2, t3)), xb,    \
+                             acc[4 * q + J]);
+      DQG_I2(0) DQG_I2(1) DQG_I2(2) DQG_I2(3)
+#undef DQG_I2
+    }
+  }
+  // -130 sum(x) over the lane's K indices (bf16 -130 = 0xC302, exact)
+  float corr = 0.0f;
+  const bf16x2_t m130 = __builtin_bit_cast(bf16x2_t, 0xC302C302u);
+#pragma unroll
+  for (int p = 0; p < ROWS; ++p) corr = dot2_bf16(m130, __builtin_bit_cast(bf16x2_t, xr[p]), corr);
+  return corr;
+}
+
+// down: ROWS / 2 INT2 byte rows times the lane's 2 ROWS h values (K 4i + m <-> hf[4i + m]);
+// returns -2 sum(h) for the code offset
+template <int ROWS>
+__device__ __forceinline__ float rows_dot_f32_int2(const uint4 (&wv)[ROWS / 2],
+                                                   const float (&hf)[2 * ROWS], float (&acc)[16]) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 2; ++i) {
+    const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t t = (d[q] >> (2 * m)) & 0x03030303u;
+        const float h = hf[4 * i + m];
+        acc[4 * q + 0] = fmaf((float)(t & 0xFFu), h, acc[4 * q + 0]);
+        acc[4 * q + 1] = fmaf((float)((t >> 8) & 0xFFu), h, acc[4 * q + 1]);
+        acc[4 * q + 2] = fmaf((float)((t >> 16) & 0xFFu), h, acc[4 * q + 2]);
+        acc[4 * q + 3] = fmaf((float)(t >> 24), h, acc[4 * q + 3]);
+      }
+    }
+  }
+  float corr = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 2 * ROWS; ++i) corr += hf[i];
+  return -2.0f * corr;
+}
+
 // FP8 gate_up rows: rows 2i and 2i+1 meet the x pair xr[i]; their bytes are interleaved per
 // column (v_perm_b32) so that one conversion gives the bf16 pair (w[2i][c], w[2i+1][c]).
 template <int ROWS>
@@ -248,6 +318,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   __shared__ float s_w[32];
   __shared__ __align__(16) float s_red[FX_THREADS * 16];
   __shared__ __align__(16) long long s_route[64 * 8 + 68];
+  __shared__ unsigned char s_fmt[FMT == FMT_FP4 ? 512 : 1];  // per-expert formats (mixed)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
@@ -280,6 +351,17 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // tend to land on different SIMDs.  Only the down units need the weights; a gate_up unit
   // only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
+    if constexpr (FMT == FMT_FP4) {
+      // mixed layer: the expert formats into LDS (loads in flight with the routing's own)
+      if (a.efmt) {
+        unsigned char fv[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) fv[v] = (lane + 64 * v < a.E) ? a.efmt[lane + 64 * v] : 0;
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          if (lane + 64 * v < a.E) s_fmt[lane + 64 * v] = fv[v];
+      }
+    }
     float lg[2] = {0.0f, 0.0f};  // router mode: this lane's logits (elements lane, lane + 64)
     if (a.wr) {
       // gather the token's logits from the router units' partial rows (E <= 128), summed
@@ -361,8 +443,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
     const int r0 = ks * KROWS + GUR * rl;                // byte row; K index KB r0
     const uint8_t* w = a.wgu + (size_t)e * (H / KB) * ld;
+    bool i2 = false;  // an INT2 expert of a mixed layer: the same K range in half the rows
+    if constexpr (FMT == FMT_FP4) i2 = a.efmt != nullptr && s_fmt[e] == FMT_INT2;
     uint4 wvv[GUR];
-    load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
+    if (i2)
+      load_rows(w + (size_t)(r0 / 2) * ld + col0, ld, reinterpret_cast<uint4(&)[GUR / 2]>(wvv));
+    else
+      load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
     float sf[16];
     scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((KB * r0) / a.group) * ld + col0,
              sf);
@@ -379,10 +466,14 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     float accb[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = 0.0f;
-    if constexpr (FMT == FMT_FP8)
+    if constexpr (FMT == FMT_FP8) {
       rows_dot_x_fp8<GUR>(wvv, xr, accb);
-    else
-      rows_dot_x<FMT, GUR>(wvv, xr, accb);
+    } else {
+      if (i2)
+        corr = rows_dot_x_int2<GUR>(reinterpret_cast<const uint4(&)[GUR / 2]>(wvv), xr, accb);
+      else
+        rows_dot_x<FMT, GUR>(wvv, xr, accb);
+    }
     // reduce the 16 row-lanes; thread i then owns partial column i (i < 128 gate, else up)
 #pragma unroll
     for (int c = 0; c < 16; ++c) accb[c] = sf[c] * (accb[c] + corr);
@@ -430,9 +521,16 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   }
   uint4 wvv[FX_D_ROWS];
   float sf[16];
+  bool i2 = false;  // an INT2 expert of a mixed layer
   if (active) {
     const int e = s_ids[j];
-    load_rows(a.wd + (size_t)e * rows_per_slot * H + (size_t)r0 * H + col0, H, wvv);
+    if constexpr (FMT == FMT_FP4) i2 = a.efmt != nullptr && s_fmt[e] == FMT_INT2;
+    const uint8_t* wd = a.wd + (size_t)e * rows_per_slot * H;
+    if (i2)
+      load_rows(wd + (size_t)(r0 / 2) * H + col0, H,
+                reinterpret_cast<uint4(&)[FX_D_ROWS / 2]>(wvv));
+    else
+      load_rows(wd + (size_t)r0 * H + col0, H, wvv);
     scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((KB * r0) / a.group) * H + col0,
              sf);
   }
@@ -506,10 +604,15 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     float accb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) accb[q] = 0.0f;
-    if constexpr (FMT == FMT_FP8)
+    if constexpr (FMT == FMT_FP8) {
       rows_dot_f32_fp8<FX_D_ROWS>(wvv, reinterpret_cast<const float(&)[FX_D_ROWS]>(hf), accb);
-    else
-      rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
+    } else {
+      if (i2)
+        corr = rows_dot_f32_int2<FX_D_ROWS>(reinterpret_cast<const uint4(&)[FX_D_ROWS / 2]>(wvv),
+                                            hf, accb);
+      else
+        rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
+    }
     const float wj = s_w[j];
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = wj * (sf[q] * (accb[q] + corr));

@@ -54,9 +54,11 @@ typedef enum dqg_status {
 typedef enum dqg_format {
   DQG_FMT_INT4 = 0,     /* value = nibble - 8                                           */
   DQG_FMT_FP4_E2M1 = 1, /* value = E2M1(nibble)                                         */
-  DQG_FMT_FP8_E4M3 = 2  /* value = E4M3(byte), one byte per weight: packed matrices are
+  DQG_FMT_FP8_E4M3 = 2, /* value = E4M3(byte), one byte per weight: packed matrices are
                            [K, N] instead of [K/2, N]; the MoE layer calls only, on their
                            single launch (see moe_fp4_layer)                             */
+  DQG_FMT_INT2 = 3      /* value = code - 2, four codes per byte: only as an entry of the
+                           per-expert table of moe_fp4_layer_mixed                       */
 } dqg_format;
 
 /* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
@@ -157,6 +159,27 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
                   const uint16_t* s_down, int group, int format, const uint16_t* residual,
                   uint16_t* out, int32_t* ids_out, float* weights_out, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_fp4_layer_mixed -- moe_fp4_layer for a layer whose experts mix FP4 (hot) and INT2
+ * (cold) weights (FireEcho page, "Quantization Formats": FP4 for hot experts, a scalar 2-bit
+ * INT2 format for the coldest ones).
+ *   expert_formats  uint8 [E] on the device: DQG_FMT_INT2 marks an INT2 expert; any other
+ *                   value means FP4 (format must be DQG_FMT_FP4_E2M1)
+ *   w_gate_up, w_down  as for FP4, every expert at its FP4 slab offset; an INT2 expert's codes
+ *                   fill the first quarter-K rows of its slab: [H/4, 2I] and [I/4, H] bytes,
+ *                   K index 4r + i in bits 2i .. 2i+1 of byte row r (code c means c - 2); the
+ *                   scales keep their layout.  INT2 experts stream half the bytes.
+ * Runs on the single launch only (the conditions of moe_fp4_layer) and returns
+ * DQG_ERR_UNSUPPORTED otherwise.  Other arguments and rules as moe_fp4_layer.
+ */
+int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, int I, int E,
+                        int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
+                        const uint8_t* w_down, const uint16_t* s_down,
+                        const uint8_t* expert_formats, int group, int format,
+                        const uint16_t* residual, uint16_t* out, int32_t* ids_out,
+                        float* weights_out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
 
 /*
  * Bytes of device workspace router_logits needs (the router's fp32 partial rows, 4 bytes x

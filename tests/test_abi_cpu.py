@@ -25,7 +25,8 @@ def test_header_lists_expected_entry_points():
     for name in ("topk_route", "moe_fp4_ffn", "moe_fp4_layer", "packed_gemv_int4",
                  "packed_dequant_f32", "moe_fp4_ffn_workspace_bytes",
                  "packed_gemv_int4_workspace_bytes", "dqg_status_string", "dqg_abi_version",
-                 "router_logits", "router_logits_workspace_bytes", "moe_fp4_layer_from_hidden"):
+                 "router_logits", "router_logits_workspace_bytes", "moe_fp4_layer_from_hidden",
+                 "moe_fp4_layer_mixed"):
         assert name in fns
 
 
@@ -121,6 +122,18 @@ def test_fp8_outside_the_single_launch_is_rejected_before_launch():
              1 << 30, None) == B.DQG_ERR_UNSUPPORTED
     d = B.LIB.packed_dequant_f32
     assert d(A, A, 64, 64, 32, 3, A, None) == B.DQG_ERR_UNSUPPORTED
+
+
+def test_mixed_layer_validation():
+    f = B.LIB.moe_fp4_layer_mixed
+    def call(T=1, fmt=B.FMT_FP4_E2M1, tab=A, lg=A):
+        return f(A, lg, T, 256, 128, 8, 2, A, A, A, A, tab, 32, fmt, 0, A, 0, 0, A, 1 << 30, None)
+    assert call(tab=0) == B.DQG_ERR_INVALID_ARG
+    assert call(lg=0) == B.DQG_ERR_INVALID_ARG
+    assert call(fmt=B.FMT_INT4) == B.DQG_ERR_UNSUPPORTED          # FP4 base only
+    assert call(fmt=B.FMT_FP4_E2M1 | B.PATH_NO_FUSED) == B.DQG_ERR_UNSUPPORTED
+    assert call(T=16) == B.DQG_ERR_UNSUPPORTED                    # single launch only
+    assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
 
 
 def test_router_validation():

@@ -1,0 +1,98 @@
+"""GPU parity: layers whose experts mix FP4 (hot) and INT2 (cold) weights, through the
+single-launch layer (moe_fp4_layer_mixed), against the float64 oracle with the same
+per-expert formats (ids exact; output within |diff| <= 1e-2 rms + 1 bf16 ulp)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bits16, check_bf16, dev, upload_layer
+from oracle import moe_oracle as O
+from workloads import synth as S
+
+pytestmark = pytest.mark.gpu
+
+
+def _b():
+    from dequant_gemv_amd import binding
+    return binding
+
+
+def _mixed(cfg, seed):
+    lg = S.moe_layer_logits(cfg, seed)
+    ids, _ = O.topk_route(lg, cfg.k)
+    L = S.make_moe_layer(cfg, seed, experts=np.unique(ids))
+    return L, upload_layer(L, np.unique(ids))
+
+
+def _run(cfg, L, D, efmt, res=None, ws=None):
+    B = _b()
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    out = B.moe_fp4_layer_mixed(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                                D["s_d"], dev(efmt), cfg.group,
+                                residual=None if res is None else dev(res).view(torch.bfloat16),
+                                ids_out=ids, weights_out=w, workspace=ws)
+    torch.cuda.synchronize()
+    return bits16(out), ids.cpu().numpy(), w.cpu().numpy()
+
+
+CASES = [("q30_half_int2", S.Q30_MIXED, 1, 0), ("q30_half_int2", S.Q30_MIXED, 1, 1),
+         ("q30_half_int2", S.Q30_MIXED, 2, 0), ("q30_half_int2", S.Q30_MIXED, 4, 2),
+         ("q30_half_int2", S.Q30_MIXED, 8, 3), ("q30_all_int2", S.replace(S.Q30, int2_frac=1.0), 1, 0),
+         ("w512_quarter_int2", S.replace(S.W512, layers=1, int2_frac=0.25), 1, 0),
+         ("w512_quarter_int2", S.replace(S.W512, layers=1, int2_frac=0.25), 4, 1)]
+
+
+@pytest.mark.parametrize("name,cfg,T,seed", CASES, ids=[f"{c[0]}-T{c[2]}-s{c[3]}" for c in CASES])
+def test_mixed_layer_parity(name, cfg, T, seed):
+    cfg = cfg.with_T(T)
+    L, D = _mixed(cfg, seed)
+    assert L.expert_fmt is not None
+    res = S.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((T, cfg.H))) \
+        if seed % 2 else None
+    out, ids, w = _run(cfg, L, D, L.expert_fmt, res)
+    want, oids, ow = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                                 cfg.fmt, residual_bits=res, expert_fmt=L.expert_fmt)
+    assert np.array_equal(ids, oids)
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    n2 = int(np.sum(L.expert_fmt[np.unique(oids)] == O.FMT_INT2))
+    assert 0 < n2 or cfg.int2_frac == 0, "the routed experts should include INT2 ones"
+    check_bf16(out, want, what=f"{name} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_all_fp4_table_equals_the_fp4_layer(T):
+    """With no INT2 entry the mixed call runs exactly the FP4 arithmetic: bitwise equal to
+    moe_fp4_layer on the same inputs."""
+    B = _b()
+    cfg = S.Q30_BATCH.with_T(T)
+    L, D = _mixed(cfg, 21)
+    table = np.full(cfg.E, S.FMT_FP4, np.uint8)
+    got, _, _ = _run(cfg, L, D, table)
+    ref = B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                          D["s_d"], cfg.group, cfg.fmt)
+    torch.cuda.synchronize()
+    assert np.array_equal(got, bits16(ref))
+
+
+def test_mixed_and_plain_calls_share_a_workspace():
+    """Mixed and plain FP4 calls alternate on one workspace (same exchange regions): each call
+    reproduces its first result bit for bit."""
+    B = _b()
+    cfgm = S.Q30_MIXED
+    Lm, Dm = _mixed(cfgm, 5)
+    cfgp = S.Q30
+    Lp, Dp = _mixed(cfgp, 6)
+    ws = B.moe_workspace(1, 2048, 768, 128, 8, "cuda")
+
+    def plain():
+        o = B.moe_fp4_layer(dev(Lp.x), dev(Lp.logits), 8, Dp["w_gu"], Dp["s_gu"], Dp["w_d"],
+                            Dp["s_d"], 32, cfgp.fmt, workspace=ws)
+        return bits16(o)
+
+    first_m = _run(cfgm, Lm, Dm, Lm.expert_fmt, ws=ws)[0]
+    first_p = plain()
+    for _ in range(3):
+        assert np.array_equal(_run(cfgm, Lm, Dm, Lm.expert_fmt, ws=ws)[0], first_m)
+        assert np.array_equal(plain(), first_p)
+    assert int(ws[:4].view(torch.int32).item()) == 0
