@@ -58,6 +58,8 @@ WORKLOADS = {
                              scales=(0.002, 0.01), logits="normal", layers=48),
     "q30_fp8_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
                              scales=(0.002, 0.01), logits="normal+bias", layers=24),
+    "q30_mixed_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                               scales=(0.002, 0.01), logits="normal", layers=48, int2_frac=0.25),
     "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
                               scales=(0.005, 0.02), logits="normal", layers=48),
     "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),
@@ -126,6 +128,20 @@ def _codes(w, shape, g, device):
     return torch.randint(0, 256, shape, dtype=torch.uint8, device=device, generator=g)
 
 
+def _expert_formats(w, g, device):
+    """Mixed layers: a per-layer seeded random int2_frac share of the experts is INT2 (their
+    codes are the first quarter of the slab's random bytes, every byte a valid INT2 code)."""
+    import torch
+    frac = w.get("int2_frac", 0.0)
+    if frac <= 0:
+        return None
+    E = w["E"]
+    f = torch.full((E,), FP4, dtype=torch.uint8, device=device)
+    cold = torch.randperm(E, device=device, generator=g)[: int(round(frac * E))]
+    f[cold] = 3  # INT2
+    return f
+
+
 def build_moe_workload(w, seed: int = 0, device="cuda"):
     """Layer weight sets drawn on the device: packed bytes uniform over 0..255 (every
     nibble uniform), scales uniform in the workload's range rounded to bf16, x ~ N(0,1)
@@ -147,6 +163,7 @@ def build_moe_workload(w, seed: int = 0, device="cuda"):
             logits=None if w["logits"] == "router" else _logits(w, g, device),
             wr=(torch.randn((H, E), device=device, generator=g) / H ** 0.5).to(torch.bfloat16)
             if w["logits"] == "router" else None,
+            efmt=_expert_formats(w, g, device),
         ))
     x = torch.randn((T, H), device=device, generator=g).to(torch.bfloat16)
     return x, out
@@ -295,6 +312,11 @@ def bench_moe(w, args, dev, stream, B):
                                         L["s_d"], G, fmt, residual=xin if chain else None,
                                         out=xs[l + 1], workspace=ws, flags=flags)
             return
+        if L["efmt"] is not None:
+            B.moe_fp4_layer_mixed(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"],
+                                  L["efmt"], G, residual=xin if chain else None,
+                                  out=xs[l + 1], workspace=ws, flags=flags)
+            return
         B.moe_fp4_layer(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
                         residual=xin if chain else None, out=xs[l + 1], workspace=ws,
                         flags=flags)
@@ -335,6 +357,17 @@ def bench_moe(w, args, dev, stream, B):
     lgs = [L["logits"] if not router else x.float() @ L["wr"].float() for L in layers]
     n_active = [distinct_experts(lg, k) for lg in lgs]
     abytes = sum(n_active) * per_expert / n_layers  # mean active bytes per layer
+    n_int2 = 0.0
+    if layers[0]["efmt"] is not None:  # mixed: INT2 experts stream half the packed bytes
+        i2 = expert_bytes(H, I, G, 4)
+        tot = 0
+        for lg, L in zip(lgs, layers):
+            act = torch.unique(torch.topk(lg, k, dim=1).indices)
+            n2 = int((L["efmt"][act] == 3).sum())
+            n_int2 += n2
+            tot += (act.numel() - n2) * per_expert + n2 * i2
+        abytes = tot / n_layers
+        n_int2 /= n_layers
     if router:
         abytes += H * E * 2                         # the router weight
     # the single-launch layer takes T <= 8 (for T > 1 a token's down rows must fill whole
@@ -368,6 +401,9 @@ def bench_moe(w, args, dev, stream, B):
               "layers_per_step": n_layers, "chained": chain, "path": args.path,
               "active_experts_per_layer_mean": round(sum(n_active) / n_layers, 2),
               "active_bytes_per_layer": round(abytes)}
+    if layers[0]["efmt"] is not None:
+        config["int2_experts_share"] = w["int2_frac"]
+        config["int2_active_experts_per_layer_mean"] = round(n_int2, 2)
     return dict(value=round(us_per_layer, 3), unit="us/layer", ms_per_step=ms_per_step,
                 achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
 

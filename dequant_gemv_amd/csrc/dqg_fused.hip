@@ -351,15 +351,14 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // tend to land on different SIMDs.  Only the down units need the weights; a gate_up unit
   // only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
+    // mixed layer: the expert formats are loaded here and stored to LDS after the selection,
+    // so that their loads are in flight together with the routing's own
+    unsigned char fv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if constexpr (FMT == FMT_FP4) {
-      // mixed layer: the expert formats into LDS (loads in flight with the routing's own)
       if (a.efmt) {
-        unsigned char fv[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) fv[v] = (lane + 64 * v < a.E) ? a.efmt[lane + 64 * v] : 0;
 #pragma unroll
         for (int v = 0; v < 8; ++v)
-          if (lane + 64 * v < a.E) s_fmt[lane + 64 * v] = fv[v];
+          if (lane + 64 * v < a.E) fv[v] = a.efmt[lane + 64 * v];
       }
     }
     float lg[2] = {0.0f, 0.0f};  // router mode: this lane's logits (elements lane, lane + 64)
@@ -404,6 +403,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
         wave_topk_select<2>(row, a.E, k, lane, s_route, s_ids, s_key);
       else
         wave_topk_select<8>(row, a.E, k, lane, s_route, s_ids, s_key);
+    }
+    if constexpr (FMT == FMT_FP4) {
+      if (a.efmt) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          if (lane + 64 * v < a.E) s_fmt[lane + 64 * v] = fv[v];
+      }
     }
     if (bid >= a.n_a) {
       int sel_e;
