@@ -421,6 +421,8 @@ int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, in
                             format, residual, out, workspace, workspace_bytes);
   if (rc != DQG_OK) return rc;
   if ((format & 0xFF) != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;  // FP4 hot experts
+  if (E % 4) return DQG_ERR_UNSUPPORTED;                                // table read as words
+  if ((uintptr_t)expert_formats & 3u) return DQG_ERR_MISALIGNED;
   if (!use_fused(T, H, I, E, k, format)) return DQG_ERR_UNSUPPORTED;   // single launch only
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;

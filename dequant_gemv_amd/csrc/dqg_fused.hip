@@ -107,73 +107,73 @@ __device__ __forceinline__ void rows_dot_x(const uint4 (&wv)[ROWS], const uint32
 }
 
 // INT2 (cold experts of a mixed FP4 layer): byte row q holds K indices 4q .. 4q+3 of one
-// column in bits 0-1, 2-3, 4-5, 6-7; code c means c - 2.  t_m = (d >> 2m) & 0x03030303 puts
-// code m of the 4 columns of dword d in its 4 bytes.  For the bf16 dot the codes become
-// bf16 128 + c (bits 0x4300 | c) in pairs (one v_perm_b32 + or); the 130 sum(x) this adds
-// is removed once per lane (corr).
-template <int J>
-__device__ __forceinline__ uint32_t int2_bf16_pair(uint32_t ta, uint32_t tb) {
-  // byte J of ta -> bits 0..7, byte J of tb -> bits 16..23, zeros elsewhere
-  return __builtin_amdgcn_perm(tb, ta, (0x0Cu << 24) | ((4u + J) << 16) | (0x0Cu << 8) | J) |
-         0x43004300u;
-}
-
-// gate_up: ROWS 4-bit-row equivalents = ROWS / 2 INT2 byte rows; x pairs xr[2i], xr[2i+1]
-// cover K indices 4i .. 4i+3 of the lane's range
+// column in bits 0-1, 2-3, 4-5, 6-7; code c means c - 2.  d & 0x33333333 leaves in every
+// byte the codes of K 4q and 4q+2 in the low bits of its two nibbles, (d >> 2) & 0x33333333
+// those of 4q+1 and 4q+3; the FP4 (E2M1) conversion reads a nibble 0..3 as c / 2 exactly
+// (0, 0.5, 1, 1.5), so one and + one conversion give the pair (c_a / 2, c_b / 2).  The sum
+// is doubled and 2 sum(x) removed once per lane (returned as corr, both exact in fp32).
 template <int ROWS>
 __device__ __forceinline__ float rows_dot_x_int2(const uint4 (&wv)[ROWS / 2],
                                                  const uint32_t (&xr)[ROWS], float (&acc)[16]) {
 #pragma unroll
   for (int i = 0; i < ROWS / 2; ++i) {
     const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-    const bf16x2_t xa = __builtin_bit_cast(bf16x2_t, xr[2 * i]);
-    const bf16x2_t xb = __builtin_bit_cast(bf16x2_t, xr[2 * i + 1]);
+    // x pairs (x[4i], x[4i+2]) and (x[4i+1], x[4i+3]) of the lane's K range
+    const bf16x2_t x02 = __builtin_bit_cast(bf16x2_t,
+                                            __builtin_amdgcn_perm(xr[2 * i + 1], xr[2 * i], 0x05040100u));
+    const bf16x2_t x13 = __builtin_bit_cast(bf16x2_t,
+                                            __builtin_amdgcn_perm(xr[2 * i + 1], xr[2 * i], 0x07060302u));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t t0 = d[q] & 0x03030303u, t1 = (d[q] >> 2) & 0x03030303u;
-      const uint32_t t2 = (d[q] >> 4) & 0x03030303u, t3 = (d[q] >> 6) & 0x03030303u;
-#define DQG_I2(J)                                                                              \
-  acc[4 * q + J] = dot2_bf16(__builtin_bit_cast(bf16x2_t, int2_bf16_pair<J>(t0, t1)), xa,    \
-                             acc[4 * q + J]);                                                  \
-  acc[4 * q + J] = dot2_bf16(__builtin_bit_cast(bf16x2_t, int2_bf16_pair<J>(t2, t3)), xb,    \
-                             acc[4 * q + J]);
-      DQG_I2(0) DQG_I2(1) DQG_I2(2) DQG_I2(3)
-#undef DQG_I2
+      const uint32_t m0 = d[q] & 0x33333333u, m1 = (d[q] >> 2) & 0x33333333u;
+      acc[4 * q + 0] = dot2_bf16(fp4_pair_bf16<0>(m0), x02, acc[4 * q + 0]);
+      acc[4 * q + 1] = dot2_bf16(fp4_pair_bf16<1>(m0), x02, acc[4 * q + 1]);
+      acc[4 * q + 2] = dot2_bf16(fp4_pair_bf16<2>(m0), x02, acc[4 * q + 2]);
+      acc[4 * q + 3] = dot2_bf16(fp4_pair_bf16<3>(m0), x02, acc[4 * q + 3]);
+      acc[4 * q + 0] = dot2_bf16(fp4_pair_bf16<0>(m1), x13, acc[4 * q + 0]);
+      acc[4 * q + 1] = dot2_bf16(fp4_pair_bf16<1>(m1), x13, acc[4 * q + 1]);
+      acc[4 * q + 2] = dot2_bf16(fp4_pair_bf16<2>(m1), x13, acc[4 * q + 2]);
+      acc[4 * q + 3] = dot2_bf16(fp4_pair_bf16<3>(m1), x13, acc[4 * q + 3]);
     }
   }
-  // -130 sum(x) over the lane's K indices (bf16 -130 = 0xC302, exact)
-  float corr = 0.0f;
-  const bf16x2_t m130 = __builtin_bit_cast(bf16x2_t, 0xC302C302u);
 #pragma unroll
-  for (int p = 0; p < ROWS; ++p) corr = dot2_bf16(m130, __builtin_bit_cast(bf16x2_t, xr[p]), corr);
-  return corr;
+  for (int c = 0; c < 16; ++c) acc[c] *= 2.0f;
+  float sx = 0.0f;
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+  for (int p = 0; p < ROWS; ++p) sx = dot2_bf16(one, __builtin_bit_cast(bf16x2_t, xr[p]), sx);
+  return -2.0f * sx;
 }
 
 // down: ROWS / 2 INT2 byte rows times the lane's 2 ROWS h values (K 4i + m <-> hf[4i + m]);
-// returns -2 sum(h) for the code offset
+// same decode in f32; returns -2 sum(h) for the code offset
 template <int ROWS>
 __device__ __forceinline__ float rows_dot_f32_int2(const uint4 (&wv)[ROWS / 2],
                                                    const float (&hf)[2 * ROWS], float (&acc)[16]) {
 #pragma unroll
   for (int i = 0; i < ROWS / 2; ++i) {
     const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+    const float h0 = hf[4 * i], h1 = hf[4 * i + 1], h2 = hf[4 * i + 2], h3 = hf[4 * i + 3];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const uint32_t m0 = d[q] & 0x33333333u, m1 = (d[q] >> 2) & 0x33333333u;
+      f32x2_t a[4], b[4];
+      a[0] = fp4_pair_f32<0>(m0); a[1] = fp4_pair_f32<1>(m0);
+      a[2] = fp4_pair_f32<2>(m0); a[3] = fp4_pair_f32<3>(m0);
+      b[0] = fp4_pair_f32<0>(m1); b[1] = fp4_pair_f32<1>(m1);
+      b[2] = fp4_pair_f32<2>(m1); b[3] = fp4_pair_f32<3>(m1);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t t = (d[q] >> (2 * m)) & 0x03030303u;
-        const float h = hf[4 * i + m];
-        acc[4 * q + 0] = fmaf((float)(t & 0xFFu), h, acc[4 * q + 0]);
-        acc[4 * q + 1] = fmaf((float)((t >> 8) & 0xFFu), h, acc[4 * q + 1]);
-        acc[4 * q + 2] = fmaf((float)((t >> 16) & 0xFFu), h, acc[4 * q + 2]);
-        acc[4 * q + 3] = fmaf((float)(t >> 24), h, acc[4 * q + 3]);
-      }
+      for (int J = 0; J < 4; ++J)
+        acc[4 * q + J] = fmaf(b[J].y, h3, fmaf(a[J].y, h2, fmaf(b[J].x, h1,
+                              fmaf(a[J].x, h0, acc[4 * q + J]))));
     }
   }
-  float corr = 0.0f;
+  float sh = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 2 * ROWS; ++i) corr += hf[i];
-  return -2.0f * corr;
+  for (int c = 0; c < 16; ++c) acc[c] *= 2.0f;
+#pragma unroll
+  for (int i = 0; i < 2 * ROWS; ++i) sh += hf[i];
+  return -2.0f * sh;
 }
 
 // FP8 gate_up rows: rows 2i and 2i+1 meet the x pair xr[i]; their bytes are interleaved per
@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   __shared__ float s_w[32];
   __shared__ __align__(16) float s_red[FX_THREADS * 16];
   __shared__ __align__(16) long long s_route[64 * 8 + 68];
-  __shared__ unsigned char s_fmt[FMT == FMT_FP4 ? 512 : 1];  // per-expert formats (mixed)
+  __shared__ __align__(4) unsigned char s_fmt[FMT == FMT_FP4 ? 512 : 4];  // per-expert formats
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
@@ -351,14 +351,15 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // tend to land on different SIMDs.  Only the down units need the weights; a gate_up unit
   // only needs its slot's id. ----
   if (wv == (int)(blockIdx.x & 3)) {
-    // mixed layer: the expert formats are loaded here and stored to LDS after the selection,
-    // so that their loads are in flight together with the routing's own
-    unsigned char fv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // mixed layer: the expert formats (4 per lane-word, E % 4 == 0) are loaded here and
+    // stored to LDS after the selection, so that their loads are in flight together with the
+    // routing's own
+    uint32_t fw[2] = {0u, 0u};
     if constexpr (FMT == FMT_FP4) {
       if (a.efmt) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-          if (lane + 64 * v < a.E) fv[v] = a.efmt[lane + 64 * v];
+        const uint32_t* ef = reinterpret_cast<const uint32_t*>(a.efmt);
+        if (4 * lane < a.E) fw[0] = ef[lane];
+        if (4 * (lane + 64) < a.E) fw[1] = ef[lane + 64];
       }
     }
     float lg[2] = {0.0f, 0.0f};  // router mode: this lane's logits (elements lane, lane + 64)
@@ -406,9 +407,9 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     if constexpr (FMT == FMT_FP4) {
       if (a.efmt) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-          if (lane + 64 * v < a.E) s_fmt[lane + 64 * v] = fv[v];
+        uint32_t* sf32 = reinterpret_cast<uint32_t*>(s_fmt);
+        if (4 * lane < a.E) sf32[lane] = fw[0];
+        if (4 * (lane + 64) < a.E) sf32[lane + 64] = fw[1];
       }
     }
     if (bid >= a.n_a) {

@@ -164,8 +164,8 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
  * moe_fp4_layer_mixed -- moe_fp4_layer for a layer whose experts mix FP4 (hot) and INT2
  * (cold) weights (FireEcho page, "Quantization Formats": FP4 for hot experts, a scalar 2-bit
  * INT2 format for the coldest ones).
- *   expert_formats  uint8 [E] on the device: DQG_FMT_INT2 marks an INT2 expert; any other
- *                   value means FP4 (format must be DQG_FMT_FP4_E2M1)
+ *   expert_formats  uint8 [E] on the device, 4-byte aligned, E % 4 == 0: DQG_FMT_INT2 marks
+ *                   an INT2 expert; any other value means FP4 (format must be DQG_FMT_FP4_E2M1)
  *   w_gate_up, w_down  as for FP4, every expert at its FP4 slab offset; an INT2 expert's codes
  *                   fill the first quarter-K rows of its slab: [H/4, 2I] and [I/4, H] bytes,
  *                   K index 4r + i in bits 2i .. 2i+1 of byte row r (code c means c - 2); the

@@ -134,6 +134,7 @@ def test_mixed_layer_validation():
     assert call(fmt=B.FMT_FP4_E2M1 | B.PATH_NO_FUSED) == B.DQG_ERR_UNSUPPORTED
     assert call(T=16) == B.DQG_ERR_UNSUPPORTED                    # single launch only
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
+    assert call(tab=A + 1) == B.DQG_ERR_MISALIGNED                # table read as words
 
 
 def test_router_validation():
