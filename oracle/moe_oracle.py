@@ -29,6 +29,12 @@ What each function follows (page titles as printed at the head of each page):
   nibbles), the same bf16 group scales.  A layer may mix formats per expert (a table of E
   entries); every expert keeps the 4-bit slab ``[K/2, N]`` and an INT2 expert's ``[K/4, N]``
   bytes fill the first K/4 rows of its slab.
+* FE-XC codebook experts -- the same table lists FE-XC, a 2-bit codebook format "2x8" for
+  cold experts.  Read as additive quantization with two codebooks: a group of 8 consecutive
+  K indices of one column is C1[c1] + C2[c2], two bf16 vectors of length 8 picked by two
+  8-bit codes, times the bf16 group scale; codes ``[K/8, 2, N]`` (codebook m of group g in
+  byte row 2g + m) fill the first K/4 rows of the slab; each expert matrix has its own pair
+  of codebooks ``[2, 256, 8]``.
 * INT4 values -- symmetric, ``nibble - 8``; the page's simplified snippet multiplies the
   raw nibble by the scale, which is not used (it is labelled a simplification).
 * group scales -- one bf16 scale per ``group`` consecutive K indices and per column.
@@ -61,6 +67,7 @@ FMT_INT4 = 0
 FMT_FP4 = 1
 FMT_FP8 = 2
 FMT_INT2 = 3
+FMT_FEXC = 4
 
 
 # ------------------------------------------------------------------------------------
@@ -223,14 +230,31 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
+def dequant_fexc(codes: np.ndarray, codebooks_bits: np.ndarray, scale_bits: np.ndarray,
+                 group: int) -> np.ndarray:
+    """FE-XC: codes ``[K/8, 2, N]`` (or the slab rows holding them), codebooks bf16
+    ``[2, 256, 8]``, scales ``[K/G, N]`` -> float64 ``[K, N]``:
+    ``W[8g + i, n] = (C[0][c0(g, n)][i] + C[1][c1(g, n)][i]) * scale[(8g + i) // group, n]``."""
+    K = scale_bits.shape[0] * group
+    N = scale_bits.shape[1]
+    c = np.asarray(codes, dtype=np.uint8)[: K // 4].reshape(K // 8, 2, N).astype(np.int64)
+    C = bf16_to_f64(codebooks_bits)                      # [2, 256, 8]
+    W = C[0][c[:, 0, :]] + C[1][c[:, 1, :]]              # [K/8, N, 8]
+    W = W.transpose(0, 2, 1).reshape(K, N)
+    return W * np.repeat(bf16_to_f64(scale_bits), group, axis=0)
+
+
 class ExpertCache:
     """Dequantized experts of one layer, built on first use (the oracle never fuses).
-    ``expert_fmt`` (optional, [E]) gives each expert's format; an INT2 expert's codes are
-    the first K/4 byte rows of its slab."""
+    ``expert_fmt`` (optional, [E]) gives each expert's format; an INT2 or FE-XC expert's codes
+    are the first K/4 byte rows of its slab; ``codebooks`` (bf16 ``[E, 2, 2, 256, 8]``: gate_up
+    then down) serve the FE-XC experts."""
 
-    def __init__(self, w_gu, s_gu, w_d, s_d, group: int, fmt: int, expert_fmt=None):
+    def __init__(self, w_gu, s_gu, w_d, s_d, group: int, fmt: int, expert_fmt=None,
+                 codebooks=None):
         self.w_gu, self.s_gu, self.w_d, self.s_d = w_gu, s_gu, w_d, s_d
         self.group, self.fmt = group, fmt
+        self.codebooks = codebooks
         self.expert_fmt = None if expert_fmt is None else np.asarray(expert_fmt)
         self._gu: Dict[int, np.ndarray] = {}
         self._d: Dict[int, np.ndarray] = {}
@@ -238,20 +262,22 @@ class ExpertCache:
     def _fmt(self, e: int) -> int:
         return self.fmt if self.expert_fmt is None else int(self.expert_fmt[e])
 
-    def _deq(self, w, s, e: int) -> np.ndarray:
+    def _deq(self, w, s, e: int, mat: int) -> np.ndarray:
         f = self._fmt(e)
+        if f == FMT_FEXC:
+            return dequant_fexc(w, self.codebooks[e][mat], s, self.group)
         if f == FMT_INT2:
             w = w[: (s.shape[0] * self.group) // 4]
         return dequant(w, s, self.group, f)
 
     def gate_up(self, e: int) -> np.ndarray:
         if e not in self._gu:
-            self._gu[e] = self._deq(self.w_gu[e], self.s_gu[e], e)
+            self._gu[e] = self._deq(self.w_gu[e], self.s_gu[e], e, 0)
         return self._gu[e]
 
     def down(self, e: int) -> np.ndarray:
         if e not in self._d:
-            self._d[e] = self._deq(self.w_d[e], self.s_d[e], e)
+            self._d[e] = self._deq(self.w_d[e], self.s_d[e], e, 1)
         return self._d[e]
 
 
@@ -266,14 +292,14 @@ def expert_ffn(x_row: np.ndarray, W_gu: np.ndarray, W_d: np.ndarray) -> np.ndarr
 
 def moe_ffn(x_bits, ids, weights, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
             residual_bits=None, cache: Optional[ExpertCache] = None,
-            expert_fmt=None) -> np.ndarray:
+            expert_fmt=None, codebooks=None) -> np.ndarray:
     """out[t] = residual[t] + sum_j weights[t, j] * FFN_{ids[t, j]}(x[t]), j ascending.
     Returns the unrounded float64 ``[T, H]``."""
     x = bf16_to_f64(x_bits)
     T, H = x.shape
     ids = np.asarray(ids)
     wts = np.asarray(weights, dtype=np.float64)
-    c = cache or ExpertCache(w_gu, s_gu, w_d, s_d, group, fmt, expert_fmt)
+    c = cache or ExpertCache(w_gu, s_gu, w_d, s_d, group, fmt, expert_fmt, codebooks)
     out = np.zeros((T, H), dtype=np.float64) if residual_bits is None else \
         bf16_to_f64(residual_bits).copy()
     for t in range(T):
@@ -286,12 +312,13 @@ def moe_ffn(x_bits, ids, weights, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
 
 
 def moe_layer(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt: int,
-              residual_bits=None, cache: Optional[ExpertCache] = None, expert_fmt=None):
+              residual_bits=None, cache: Optional[ExpertCache] = None, expert_fmt=None,
+              codebooks=None):
     """Route, then the expert FFN and the weighted combine.
     Returns ``(out float64 [T, H], ids, weights)``."""
     ids, w = topk_route(logits, k)
     out = moe_ffn(x_bits, ids, w, w_gu, s_gu, w_d, s_d, group, fmt, residual_bits, cache,
-                  expert_fmt)
+                  expert_fmt, codebooks)
     return out, ids, w
 
 

@@ -49,6 +49,22 @@ def e4m3_fraction(code: int) -> Fraction:
     return -mag if s else mag
 
 
+def fexc_exact(codes, codebooks, scales, group: int):
+    """FE-XC: byte row 2g + m of ``codes`` is codebook m's code of group g (8 K indices);
+    W[8g + i][n] = (C[0][c0][i] + C[1][c1][i]) * scale[(8g + i) // group][n], exactly."""
+    K, N = len(scales) * group, len(scales[0])
+    out = []
+    for kk in range(K):
+        g, i = kk // 8, kk % 8
+        row = []
+        for n in range(N):
+            c0, c1 = int(codes[2 * g][n]), int(codes[2 * g + 1][n])
+            v = bf16_fraction(codebooks[0][c0][i]) + bf16_fraction(codebooks[1][c1][i])
+            row.append(v * bf16_fraction(scales[kk // group][n]))
+        out.append(row)
+    return out
+
+
 def dequant_exact(packed, scales, group: int, fmt: str):
     """packed [K/2][N] bytes (fp8: [K][N]; int2: [K/4][N], or a 4-bit slab whose first
     K/4 rows hold the codes), scales [K/G][N] bf16 bits -> exact W [K][N] (Fractions)."""
@@ -84,15 +100,19 @@ def topk_exact(row, k: int):
 
 
 def moe_exact(x_bits, logits, k: int, w_gu, s_gu, w_d, s_d, group: int, fmt,
-              residual_bits=None):
+              residual_bits=None, codebooks=None):
     """fmt: one format name, or a list of E names (per-expert formats).
     Returns (out [T][H] float64, ids [T][k], weights [T][k])."""
     T, H = len(x_bits), len(x_bits[0])
     E = len(w_gu)
     I = len(w_gu[0][0]) // 2
     fmts = fmt if isinstance(fmt, list) else [fmt] * E
-    Wgu = [dequant_exact(w_gu[e], s_gu[e], group, fmts[e]) for e in range(E)]
-    Wd = [dequant_exact(w_d[e], s_d[e], group, fmts[e]) for e in range(E)]
+    def deq(w, s, e, mat):
+        if fmts[e] == "fexc":
+            return fexc_exact(w, codebooks[e][mat], s, group)
+        return dequant_exact(w, s, group, fmts[e])
+    Wgu = [deq(w_gu[e], s_gu[e], e, 0) for e in range(E)]
+    Wd = [deq(w_d[e], s_d[e], e, 1) for e in range(E)]
     out, all_ids, all_w = [], [], []
     for t in range(T):
         x = [bf16_fraction(v) for v in x_bits[t]]

@@ -393,6 +393,43 @@ def test_mixed_formats_match_exact_bruteforce(seed):
     assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
 
 
+def test_fexc_closed_form_codebooks():
+    """C0[c][i] = c / 16 and C1[c][i] = i / 64 (exact bf16) give W[8g + i, n] =
+    c0(g, n) / 16 + i / 64 at scale 1: pins the group axis (K), the plane order and the
+    element index."""
+    rng = np.random.default_rng(31)
+    K, N, G = 64, 8, 32
+    codes = rng.integers(0, 256, size=(K // 8, 2, N), dtype=np.uint8)
+    c = np.arange(256, dtype=np.float64)
+    cb = np.stack([np.repeat((c / 16)[:, None], 8, axis=1),
+                   np.repeat((np.arange(8) / 64)[None, :], 256, axis=0)])
+    W = O.dequant_fexc(codes.reshape(K // 4, N), S.f32_to_bf16_bits(cb),
+                       np.full((K // G, N), 0x3F80, np.uint16), G)
+    want = np.array([[codes[kk // 8, 0, n] / 16 + (kk % 8) / 64 for n in range(N)]
+                     for kk in range(K)])
+    assert np.array_equal(W, want)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_mixed_fp4_int2_fexc_match_exact_bruteforce(seed):
+    rng = np.random.default_rng(800 + seed)
+    T, E, k, G, H, I = 2, 3, 2, 8, 16, 16
+    x, lg, w_gu, s_gu, w_d, s_d = _tiny_random(rng, T, E, H, I, G, "fp4")
+    efmt = np.array([O.FMT_FP4, O.FMT_INT2, O.FMT_FEXC], np.uint8)
+    for e in (1, 2):
+        w_gu[e, H // 4:] = 0
+        w_d[e, I // 4:] = 0
+    cb = S.f32_to_bf16_bits(rng.standard_normal((E, 2, 2, 256, 8)))
+    out, ids, w = O.moe_layer(x, lg, k, w_gu, s_gu, w_d, s_d, G, O.FMT_FP4, expert_fmt=efmt,
+                              codebooks=cb)
+    bout, bids, bw = BF.moe_exact(x.tolist(), lg.tolist(), k, w_gu.tolist(), s_gu.tolist(),
+                                  w_d.tolist(), s_d.tolist(), G, ["fp4", "int2", "fexc"],
+                                  codebooks=cb.tolist())
+    assert ids.tolist() == bids
+    scale = max(1e-300, float(np.sqrt(np.mean(np.square(bout)))))
+    assert np.max(np.abs(out - np.array(bout))) <= 1e-12 * scale + 1e-300
+
+
 # --------------------------------------------------------------------------------------
 # router logits from the hidden state
 # --------------------------------------------------------------------------------------

@@ -30,6 +30,7 @@ FMT_INT4 = 0  # value = (nibble - 8) * scale
 FMT_FP4 = 1   # value = E2M1(nibble) * scale
 FMT_FP8 = 2   # value = E4M3(byte) * scale, one byte per weight
 FMT_INT2 = 3  # value = (code - 2) * scale, four codes per byte (per-expert cold format)
+FMT_FEXC = 4  # value = (C1[c1] + C2[c2])[i] * scale, 2 codes per 8 weights (codebook format)
 
 
 # --------------------------------------------------------------------------------------
@@ -81,6 +82,7 @@ class MoEConfig:
     layers: int = 1
     residual: bool = False          # chained stack: x_{l+1} = bf16(x_l + MoE_l(x_l))
     int2_frac: float = 0.0          # share of experts stored as INT2 (cold experts)
+    fexc_frac: float = 0.0          # share of experts stored as FE-XC codebook codes
 
     def with_T(self, T: int) -> "MoEConfig":
         return replace(self, T=T)
@@ -118,6 +120,7 @@ Q30 = MoEConfig("q30", T=1, E=128, H=2048, I=768, k=8, fmt=FMT_FP4, group=32,
 Q30_BATCH = replace(Q30, name="q30_batch", T=16, logits="normal+bias")
 Q30_FP8 = replace(Q30, name="q30_fp8", fmt=FMT_FP8)
 Q30_MIXED = replace(Q30, name="q30_mixed", int2_frac=0.5)
+Q30_CODEBOOK = replace(Q30, name="q30_codebook", int2_frac=0.25, fexc_frac=0.25)
 W512 = MoEConfig("w512", T=1, E=512, H=2048, I=512, k=10, fmt=FMT_FP4, group=32,
                  scale_lo=0.002, scale_hi=0.01, logits="zipf", layers=48, residual=True)
 GEMV_N = (256, 8192, 34816)
@@ -143,6 +146,7 @@ class MoELayer:
     s_d: np.ndarray              # uint16 [E, I/G, H]
     meta: dict = field(default_factory=dict)
     expert_fmt: Optional[np.ndarray] = None  # uint8 [E] per-expert format (mixed layers)
+    codebooks: Optional[np.ndarray] = None   # uint16 bf16 [E, 2, 2, 256, 8] (FE-XC experts)
 
 
 def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
@@ -200,7 +204,7 @@ def make_moe_layer(cfg: MoEConfig, seed: int = 0, layer: int = 0, with_x: bool =
         sub = rng.spawn(1)[0]
         if want is not None and e not in want:
             continue
-        if efmt is not None and efmt[e] == FMT_INT2:  # codes in the first K/4 slab rows
+        if efmt is not None and efmt[e] in (FMT_INT2, FMT_FEXC):  # codes: first K/4 rows
             w_gu[e, : H // 4] = codes(sub, (H // 4, 2 * I))
             s_gu[e] = _scales(sub, (H // G, 2 * I), cfg.scale_lo, cfg.scale_hi)
             w_d[e, : I // 4] = codes(sub, (I // 4, H))
@@ -211,19 +215,31 @@ def make_moe_layer(cfg: MoEConfig, seed: int = 0, layer: int = 0, with_x: bool =
         w_d[e] = codes(sub, (I // b, H))
         s_d[e] = _scales(sub, (I // G, H), cfg.scale_lo, cfg.scale_hi)
     return MoELayer(cfg, seed, x, logits, w_gu, s_gu, w_d, s_d, meta={"rng_seed": s},
-                    expert_fmt=efmt)
+                    expert_fmt=efmt, codebooks=make_codebooks(cfg, seed, layer))
+
+
+def make_codebooks(cfg: MoEConfig, seed: int = 0, layer: int = 0) -> Optional[np.ndarray]:
+    """FE-XC codebooks of every expert (gate_up and down, two codebooks each, 256 entries of
+    8): bf16 N(0, 2), from their own stream ``default_rng([seed, layer, 0xC0])``; None when
+    the layer has no FE-XC experts."""
+    if cfg.fexc_frac <= 0:
+        return None
+    rng = np.random.default_rng([seed, layer, 0xC0])
+    return f32_to_bf16_bits(2.0 * rng.standard_normal((cfg.E, 2, 2, 256, 8)))
 
 
 def expert_formats(cfg: MoEConfig, seed: int = 0, layer: int = 0) -> Optional[np.ndarray]:
     """Per-expert formats of a mixed layer: round(int2_frac E) experts, drawn from their own
     stream ``default_rng([seed, layer, 0x12])``, are INT2, the rest the layer's format; None
     when the layer has no INT2 experts."""
-    if cfg.int2_frac <= 0:
+    if cfg.int2_frac <= 0 and cfg.fexc_frac <= 0:
         return None
-    n = int(round(cfg.int2_frac * cfg.E))
-    cold = np.random.default_rng([seed, layer, 0x12]).choice(cfg.E, size=n, replace=False)
+    n2 = int(round(cfg.int2_frac * cfg.E))
+    nx = int(round(cfg.fexc_frac * cfg.E))
+    cold = np.random.default_rng([seed, layer, 0x12]).permutation(cfg.E)
     f = np.full(cfg.E, cfg.fmt, np.uint8)
-    f[cold] = FMT_INT2
+    f[cold[:n2]] = FMT_INT2
+    f[cold[n2:n2 + nx]] = FMT_FEXC
     return f
 
 
