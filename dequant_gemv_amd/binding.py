@@ -27,6 +27,7 @@ FMT_INT4 = 0
 FMT_FP4_E2M1 = 1
 FMT_FP8_E4M3 = 2
 FMT_INT2 = 3
+FMT_FEXC = 4
 PATH_FORCE_GEMV = 0x100
 PATH_FORCE_MFMA = 0x200
 PATH_NO_FUSED = 0x400
@@ -48,8 +49,8 @@ SIGNATURES = {
     "router_logits": (_I, [_P, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "moe_fp4_layer_from_hidden": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P,
                                        _P, _P, _P, _P, _Z, _P]),
-    "moe_fp4_layer_mixed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
-                                 _P, _P, _P, _Z, _P]),
+    "moe_fp4_layer_mixed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _P,
+                                 _P, _P, _P, _P, _Z, _P]),
     "packed_gemv_int4_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
@@ -256,13 +257,16 @@ def moe_fp4_layer_from_hidden(x, w_router, k: int, w_gate_up, s_gate_up, w_down,
 
 
 def moe_fp4_layer_mixed(x, logits, k: int, w_gate_up, s_gate_up, w_down, s_down,
-                        expert_formats, group: int, residual=None, out=None, ids_out=None,
-                        weights_out=None, workspace=None, flags: int = 0) -> torch.Tensor:
-    """FP4 layer whose experts marked FMT_INT2 in expert_formats (uint8 [E]) hold INT2 codes
-    in the first quarter of their slab."""
+                        expert_formats, group: int, codebooks=None, residual=None, out=None,
+                        ids_out=None, weights_out=None, workspace=None,
+                        flags: int = 0) -> torch.Tensor:
+    """FP4 layer whose experts marked FMT_INT2 / FMT_FEXC in expert_formats (uint8 [E]) hold
+    INT2 or FE-XC codes in the first quarter of their slab (codebooks bf16 [E, 2, 2, 256, 8])."""
     T, H, I, E = _moe_shapes(x, w_gate_up, s_gate_up, w_down, s_down, group, FMT_FP4_E2M1)
     _need(logits, "logits", 4, (T, E), x.device)
     _need(expert_formats, "expert_formats", 1, (E,), x.device)
+    if codebooks is not None:
+        _need(codebooks, "codebooks", 2, (E, 2, 2, 256, 8), x.device)
     if residual is not None:
         _need(residual, "residual", 2, (T, H), x.device)
     if out is None:
@@ -277,7 +281,8 @@ def moe_fp4_layer_mixed(x, logits, k: int, w_gate_up, s_gate_up, w_down, s_down,
     _need(workspace, "workspace", 1, None, x.device)
     _check("moe_fp4_layer_mixed", LIB.moe_fp4_layer_mixed(
         _ptr(x), _ptr(logits), T, H, I, E, k, _ptr(w_gate_up), _ptr(s_gate_up), _ptr(w_down),
-        _ptr(s_down), _ptr(expert_formats), group, FMT_FP4_E2M1 | flags, _ptr(residual),
+        _ptr(s_down), _ptr(expert_formats), _ptr(codebooks), group, FMT_FP4_E2M1 | flags,
+        _ptr(residual),
         _ptr(out), _ptr(ids_out), _ptr(weights_out), _ptr(workspace), workspace.numel(),
         _stream(x)))
     return out

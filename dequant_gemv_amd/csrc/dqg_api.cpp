@@ -199,9 +199,10 @@ int run_fused(const MoePlan& p, const uint16_t* x, const float* logits, const ui
               float* logits_out, const uint8_t* wgu, const uint16_t* sgu, const uint8_t* wd,
               const uint16_t* sd, int group, int format, const uint16_t* res, uint16_t* out,
               int32_t* ids_out, float* w_out, void* ws, hipStream_t st,
-              const uint8_t* efmt = nullptr) {
+              const uint8_t* efmt = nullptr, const uint16_t* cb = nullptr) {
   dqg::FusedArgs f{};
   f.efmt = efmt;
+  f.cb = cb;
   f.x = x; f.logits = logits; f.H = p.H; f.I = p.I; f.E = p.E; f.k = p.k; f.group = group;
   f.wr = logits ? nullptr : wr;
   f.logits_out = logits ? nullptr : logits_out;
@@ -412,8 +413,8 @@ int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T
 int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, int I, int E,
                         int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
                         const uint8_t* w_down, const uint16_t* s_down,
-                        const uint8_t* expert_formats, int group, int format,
-                        const uint16_t* residual, uint16_t* out, int32_t* ids_out,
+                        const uint8_t* expert_formats, const uint16_t* codebooks, int group,
+                        int format, const uint16_t* residual, uint16_t* out, int32_t* ids_out,
                         float* weights_out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   if (!logits || !expert_formats) return DQG_ERR_INVALID_ARG;
@@ -423,13 +424,16 @@ int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, in
   if ((format & 0xFF) != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;  // FP4 hot experts
   if (E % 4) return DQG_ERR_UNSUPPORTED;                                // table read as words
   if ((uintptr_t)expert_formats & 3u) return DQG_ERR_MISALIGNED;
+  // FE-XC: a down unit's rows span at most two slots, whose codebooks it stages
+  if (codebooks && I / 2 < 256) return DQG_ERR_UNSUPPORTED;
+  if (codebooks && !aligned16(codebooks)) return DQG_ERR_MISALIGNED;
   if (!use_fused(T, H, I, E, k, format)) return DQG_ERR_UNSUPPORTED;   // single launch only
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
                    format, residual, out, ids_out, weights_out, workspace, stream,
-                   expert_formats);
+                   expert_formats, codebooks);
 }
 
 size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group) {

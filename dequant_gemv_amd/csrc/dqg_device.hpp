@@ -33,7 +33,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum { FMT_INT4 = 0, FMT_FP4 = 1, FMT_FP8 = 2, FMT_INT2 = 3 };
+enum { FMT_INT4 = 0, FMT_FP4 = 1, FMT_FP8 = 2, FMT_INT2 = 3, FMT_FEXC = 4 };
 enum { X_BF16 = 0, X_F16 = 1, X_F32 = 2 };
 
 constexpr int BLK_ROWS = 16;  // byte rows per block (32 K indices)

@@ -176,6 +176,74 @@ __device__ __forceinline__ float rows_dot_f32_int2(const uint4 (&wv)[ROWS / 2],
   return -2.0f * sh;
 }
 
+// FE-XC (codebook experts of a mixed FP4 layer): code row 2g + m holds codebook m's 8-bit
+// code of group g (8 consecutive K indices) for 16 columns; the group's weights are
+// C[0][c0] + C[1][c1], 8 bf16 each (one uint4 of the LDS copy `cb`, [2][256] vectors).
+// gate_up: ROWS 4-bit-row equivalents = ROWS / 4 groups; x pairs xr[4g + p] hold K 8g + 2p
+// and 8g + 2p + 1 of the lane's range, which meet the vectors' pairs in v_dot2_f32_bf16.
+__device__ __forceinline__ uint32_t byte_of(const uint4& w, int j) {
+  const uint32_t d = (j < 4) ? w.x : (j < 8) ? w.y : (j < 12) ? w.z : w.w;
+  return (d >> (8 * (j & 3))) & 0xFFu;
+}
+template <int ROWS>
+__device__ __forceinline__ void rows_dot_x_fexc(const uint4 (&wv)[ROWS / 2],
+                                                const uint32_t (&xr)[ROWS], const uint4* cb,
+                                                float (&acc)[16]) {
+#pragma unroll
+  for (int g = 0; g < ROWS / 4; ++g) {
+    bf16x2_t xp[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) xp[p] = __builtin_bit_cast(bf16x2_t, xr[4 * g + p]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 v0 = cb[byte_of(wv[2 * g], j)], v1 = cb[256 + byte_of(wv[2 * g + 1], j)];
+      float s = acc[j];
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v0.x), xp[0], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v0.y), xp[1], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v0.z), xp[2], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v0.w), xp[3], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v1.x), xp[0], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v1.y), xp[1], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v1.z), xp[2], s);
+      s = dot2_bf16(__builtin_bit_cast(bf16x2_t, v1.w), xp[3], s);
+      acc[j] = s;
+    }
+  }
+}
+
+// down: the lane's 2 ROWS fp32 h values split into bf16 hi + lo pairs (hi = the top 16 bits,
+// lo = the exact remainder rounded to bf16: about 16 significant bits of h in all)
+template <int ROWS>
+__device__ __forceinline__ void rows_dot_f32_fexc(const uint4 (&wv)[ROWS / 2],
+                                                  const float (&hf)[2 * ROWS], const uint4* cb,
+                                                  float (&acc)[16]) {
+#pragma unroll
+  for (int g = 0; g < ROWS / 4; ++g) {
+    bf16x2_t hh[4], hl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = hf[8 * g + 2 * p], b = hf[8 * g + 2 * p + 1];
+      const uint32_t ah = __float_as_uint(a) & 0xFFFF0000u, bh = __float_as_uint(b) & 0xFFFF0000u;
+      hh[p] = __builtin_bit_cast(bf16x2_t, (ah >> 16) | bh);
+      const uint32_t al = f32_to_bf16(a - __uint_as_float(ah));
+      const uint32_t bl = f32_to_bf16(b - __uint_as_float(bh));
+      hl[p] = __builtin_bit_cast(bf16x2_t, al | (bl << 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 v0 = cb[byte_of(wv[2 * g], j)], v1 = cb[256 + byte_of(wv[2 * g + 1], j)];
+      const uint32_t vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float s = acc[j];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        s = dot2_bf16(__builtin_bit_cast(bf16x2_t, vv[q]), hh[q & 3], s);
+        s = dot2_bf16(__builtin_bit_cast(bf16x2_t, vv[q]), hl[q & 3], s);
+      }
+      acc[j] = s;
+    }
+  }
+}
+
 // FP8 gate_up rows: rows 2i and 2i+1 meet the x pair xr[i]; their bytes are interleaved per
 // column (v_perm_b32) so that one conversion gives the bf16 pair (w[2i][c], w[2i+1][c]).
 template <int ROWS>
@@ -319,6 +387,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   __shared__ __align__(16) float s_red[FX_THREADS * 16];
   __shared__ __align__(16) long long s_route[64 * 8 + 68];
   __shared__ __align__(4) unsigned char s_fmt[FMT == FMT_FP4 ? 512 : 4];  // per-expert formats
+  __shared__ uint4 s_cb[FMT == FMT_FP4 ? 2 * 512 : 1];  // FE-XC codebooks: 2 sets of [2][256]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
@@ -450,8 +519,15 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const int col0 = (ch < 8) ? (128 * nt + 16 * ch) : (I + 128 * nt + 16 * (ch - 8));
     const int r0 = ks * KROWS + GUR * rl;                // byte row; K index KB r0
     const uint8_t* w = a.wgu + (size_t)e * (H / KB) * ld;
-    bool i2 = false;  // an INT2 expert of a mixed layer: the same K range in half the rows
-    if constexpr (FMT == FMT_FP4) i2 = a.efmt != nullptr && s_fmt[e] == FMT_INT2;
+    bool i2 = false;  // an INT2 or FE-XC expert of a mixed layer: the K range in half the rows
+    bool fx = false;  // FE-XC (codebooks staged in LDS)
+    if constexpr (FMT == FMT_FP4) {
+      if (a.efmt != nullptr) {
+        const int f = s_fmt[e];
+        fx = f == FMT_FEXC && a.cb != nullptr;
+        i2 = f == FMT_INT2 || fx;
+      }
+    }
     uint4 wvv[GUR];
     if (i2)
       load_rows(w + (size_t)(r0 / 2) * ld + col0, ld, reinterpret_cast<uint4(&)[GUR / 2]>(wvv));
@@ -476,10 +552,18 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     if constexpr (FMT == FMT_FP8) {
       rows_dot_x_fp8<GUR>(wvv, xr, accb);
     } else {
-      if (i2)
+      if (fx) {  // the expert's gate_up codebooks, loaded after its codes are in flight
+        const uint4* src = reinterpret_cast<const uint4*>(a.cb) + (size_t)e * 1024;
+        const uint4 v0 = src[tid], v1 = src[tid + 256];
+        s_cb[tid] = v0;
+        s_cb[tid + 256] = v1;
+        __syncthreads();
+        rows_dot_x_fexc<GUR>(reinterpret_cast<const uint4(&)[GUR / 2]>(wvv), xr, s_cb, accb);
+      } else if (i2) {
         corr = rows_dot_x_int2<GUR>(reinterpret_cast<const uint4(&)[GUR / 2]>(wvv), xr, accb);
-      else
+      } else {
         rows_dot_x<FMT, GUR>(wvv, xr, accb);
+      }
     }
     // reduce the 16 row-lanes; thread i then owns partial column i (i < 128 gate, else up)
 #pragma unroll
@@ -528,10 +612,36 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   }
   uint4 wvv[FX_D_ROWS];
   float sf[16];
-  bool i2 = false;  // an INT2 expert of a mixed layer
+  bool i2 = false;  // an INT2 or FE-XC expert of a mixed layer
+  bool fx = false;  // FE-XC: codebook set `cset` (the chunk's first or second slot)
+  int cset = 0;
+  // FE-XC codebooks of the chunk's first two slots (a chunk spans at most two when
+  // I / 2 >= 256, which the host requires with codebooks), staged by the whole workgroup
+  // (loaded after the h gather, so that they hold no registers across it)
+  int stage_e[2] = {-1, -1};
+  const int sl_a = (c * FX_DROWS) / rows_per_slot;
+  if constexpr (FMT == FMT_FP4) {
+    if (a.efmt != nullptr && a.cb != nullptr) {
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const int slz = sl_a + z;
+        if (slz < S && slz * rows_per_slot < (c + 1) * FX_DROWS) {
+          const int ez = s_ids[slz - tok * k];
+          if (s_fmt[ez] == FMT_FEXC) stage_e[z] = ez;
+        }
+      }
+    }
+  }
   if (active) {
     const int e = s_ids[j];
-    if constexpr (FMT == FMT_FP4) i2 = a.efmt != nullptr && s_fmt[e] == FMT_INT2;
+    if constexpr (FMT == FMT_FP4) {
+      if (a.efmt != nullptr) {
+        const int f = s_fmt[e];
+        fx = f == FMT_FEXC && a.cb != nullptr;
+        i2 = f == FMT_INT2 || fx;
+        cset = sl - sl_a;
+      }
+    }
     const uint8_t* wd = a.wd + (size_t)e * rows_per_slot * H;
     if (i2)
       load_rows(wd + (size_t)(r0 / 2) * H + col0, H,
@@ -588,6 +698,24 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     reinterpret_cast<float2*>(hl)[tid] = h2;
   }
+  if constexpr (FMT == FMT_FP4) {
+    if (stage_e[0] >= 0 || stage_e[1] >= 0) {
+      uint4 v[4];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.cb) +
+                           (size_t)(stage_e[z] >= 0 ? stage_e[z] : 0) * 1024 + 512;
+        v[2 * z] = stage_e[z] >= 0 ? src[tid] : make_uint4(0, 0, 0, 0);
+        v[2 * z + 1] = stage_e[z] >= 0 ? src[tid + 256] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int z = 0; z < 2; ++z)
+        if (stage_e[z] >= 0) {
+          s_cb[512 * z + tid] = v[2 * z];
+          s_cb[512 * z + tid + 256] = v[2 * z + 1];
+        }
+    }
+  }
   __syncthreads();
   float acc[16];
 #pragma unroll
@@ -614,7 +742,10 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     if constexpr (FMT == FMT_FP8) {
       rows_dot_f32_fp8<FX_D_ROWS>(wvv, reinterpret_cast<const float(&)[FX_D_ROWS]>(hf), accb);
     } else {
-      if (i2)
+      if (fx)
+        rows_dot_f32_fexc<FX_D_ROWS>(reinterpret_cast<const uint4(&)[FX_D_ROWS / 2]>(wvv), hf,
+                                     s_cb + 512 * cset, accb);
+      else if (i2)
         corr = rows_dot_f32_int2<FX_D_ROWS>(reinterpret_cast<const uint4(&)[FX_D_ROWS / 2]>(wvv),
                                             hf, accb);
       else

@@ -59,6 +59,7 @@ struct FusedArgs {
   const uint16_t* wr;   // router weight bf16 [H, E] (router units), or null
   float* logits_out;    // optional fp32 [T, E] copy of the router's logits (may be null)
   const uint8_t* efmt;  // per-expert formats [E] of a mixed FP4 layer (FMT_INT2 entries), or null
+  const uint16_t* cb;   // FE-XC codebooks bf16 [E][2 (gate_up, down)][2][256][8], or null
   float* rpart;         // [2][rs][T][E] router partial rows, two copies
   int n_r, rs;          // router units (the first n_r workgroups) and row splits
   int H, I, E, k, group, fmt;

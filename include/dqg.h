@@ -57,8 +57,9 @@ typedef enum dqg_format {
   DQG_FMT_FP8_E4M3 = 2, /* value = E4M3(byte), one byte per weight: packed matrices are
                            [K, N] instead of [K/2, N]; the MoE layer calls only, on their
                            single launch (see moe_fp4_layer)                             */
-  DQG_FMT_INT2 = 3      /* value = code - 2, four codes per byte: only as an entry of the
+  DQG_FMT_INT2 = 3,     /* value = code - 2, four codes per byte: only as an entry of the
                            per-expert table of moe_fp4_layer_mixed                       */
+  DQG_FMT_FEXC = 4      /* FE-XC 2x8 codebook codes: only as an entry of that table       */
 } dqg_format;
 
 /* Path flags, OR-ed into the `format` argument of the MoE calls (testing aid; the
@@ -161,11 +162,19 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
                   size_t workspace_bytes, hipStream_t stream);
 
 /*
- * moe_fp4_layer_mixed -- moe_fp4_layer for a layer whose experts mix FP4 (hot) and INT2
- * (cold) weights (FireEcho page, "Quantization Formats": FP4 for hot experts, a scalar 2-bit
- * INT2 format for the coldest ones).
+ * moe_fp4_layer_mixed -- moe_fp4_layer for a layer whose experts mix FP4 (hot), FE-XC and
+ * INT2 (cold) weights (FireEcho page, "Quantization Formats": FP4 for hot experts, the 2-bit
+ * FE-XC codebook format and a scalar 2-bit INT2 format for the cold ones).
  *   expert_formats  uint8 [E] on the device, 4-byte aligned, E % 4 == 0: DQG_FMT_INT2 marks
- *                   an INT2 expert; any other value means FP4 (format must be DQG_FMT_FP4_E2M1)
+ *                   an INT2 expert, DQG_FMT_FEXC an FE-XC expert; any other value means FP4
+ *                   (format must be DQG_FMT_FP4_E2M1)
+ *   codebooks       bf16 [E, 2, 2, 256, 8] (16-byte aligned) or NULL: per expert, for gate_up
+ *                   then down, two codebooks of 256 vectors of 8; needs I >= 512 (a down unit's
+ *                   256 rows then span at most two experts).  An FE-XC expert's codes fill the
+ *                   first quarter-K rows of its slab as [K/8, 2, N] bytes (codebook m's code of
+ *                   the group of K indices 8g .. 8g+7 in byte row 2g + m); its weights are
+ *                   (C[0][c0] + C[1][c1])[i] * scale.  Without codebooks an FE-XC entry reads
+ *                   its slab as FP4.
  *   w_gate_up, w_down  as for FP4, every expert at its FP4 slab offset; an INT2 expert's codes
  *                   fill the first quarter-K rows of its slab: [H/4, 2I] and [I/4, H] bytes,
  *                   K index 4r + i in bits 2i .. 2i+1 of byte row r (code c means c - 2); the
@@ -176,8 +185,8 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
 int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, int I, int E,
                         int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
                         const uint8_t* w_down, const uint16_t* s_down,
-                        const uint8_t* expert_formats, int group, int format,
-                        const uint16_t* residual, uint16_t* out, int32_t* ids_out,
+                        const uint8_t* expert_formats, const uint16_t* codebooks, int group,
+                        int format, const uint16_t* residual, uint16_t* out, int32_t* ids_out,
                         float* weights_out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 

@@ -126,8 +126,8 @@ def test_fp8_outside_the_single_launch_is_rejected_before_launch():
 
 def test_mixed_layer_validation():
     f = B.LIB.moe_fp4_layer_mixed
-    def call(T=1, fmt=B.FMT_FP4_E2M1, tab=A, lg=A):
-        return f(A, lg, T, 256, 128, 8, 2, A, A, A, A, tab, 32, fmt, 0, A, 0, 0, A, 1 << 30, None)
+    def call(T=1, fmt=B.FMT_FP4_E2M1, tab=A, lg=A, cb=0, I=128):
+        return f(A, lg, T, 256, I, 8, 2, A, A, A, A, tab, cb, 32, fmt, 0, A, 0, 0, A, 1 << 30, None)
     assert call(tab=0) == B.DQG_ERR_INVALID_ARG
     assert call(lg=0) == B.DQG_ERR_INVALID_ARG
     assert call(fmt=B.FMT_INT4) == B.DQG_ERR_UNSUPPORTED          # FP4 base only
@@ -135,6 +135,9 @@ def test_mixed_layer_validation():
     assert call(T=16) == B.DQG_ERR_UNSUPPORTED                    # single launch only
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
     assert call(tab=A + 1) == B.DQG_ERR_MISALIGNED                # table read as words
+    assert call(cb=A) == B.DQG_ERR_UNSUPPORTED                    # FE-XC needs I >= 512
+    assert call(cb=A, I=512, T=16) == B.DQG_ERR_UNSUPPORTED       # single launch only
+    assert call(cb=A + 8, I=512) == B.DQG_ERR_MISALIGNED
 
 
 def test_router_validation():

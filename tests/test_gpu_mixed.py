@@ -1,4 +1,4 @@
-"""GPU parity: layers whose experts mix FP4 (hot) and INT2 (cold) weights, through the
+"""GPU parity: layers whose experts mix FP4 (hot), FE-XC and INT2 (cold) weights, through the
 single-launch layer (moe_fp4_layer_mixed), against the float64 oracle with the same
 per-expert formats (ids exact; output within |diff| <= 1e-2 rms + 1 bf16 ulp)."""
 import numpy as np
@@ -28,8 +28,9 @@ def _run(cfg, L, D, efmt, res=None, ws=None):
     B = _b()
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    cb = None if L.codebooks is None else dev(L.codebooks)
     out = B.moe_fp4_layer_mixed(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
-                                D["s_d"], dev(efmt), cfg.group,
+                                D["s_d"], dev(efmt), cfg.group, codebooks=cb,
                                 residual=None if res is None else dev(res).view(torch.bfloat16),
                                 ids_out=ids, weights_out=w, workspace=ws)
     torch.cuda.synchronize()
@@ -40,7 +41,11 @@ CASES = [("q30_half_int2", S.Q30_MIXED, 1, 0), ("q30_half_int2", S.Q30_MIXED, 1,
          ("q30_half_int2", S.Q30_MIXED, 2, 0), ("q30_half_int2", S.Q30_MIXED, 4, 2),
          ("q30_half_int2", S.Q30_MIXED, 8, 3), ("q30_all_int2", S.replace(S.Q30, int2_frac=1.0), 1, 0),
          ("w512_quarter_int2", S.replace(S.W512, layers=1, int2_frac=0.25), 1, 0),
-         ("w512_quarter_int2", S.replace(S.W512, layers=1, int2_frac=0.25), 4, 1)]
+         ("w512_quarter_int2", S.replace(S.W512, layers=1, int2_frac=0.25), 4, 1),
+         ("q30_codebook", S.Q30_CODEBOOK, 1, 0), ("q30_codebook", S.Q30_CODEBOOK, 1, 1),
+         ("q30_codebook", S.Q30_CODEBOOK, 2, 2), ("q30_codebook", S.Q30_CODEBOOK, 4, 3),
+         ("q30_codebook", S.Q30_CODEBOOK, 8, 4), ("q30_all_fexc", S.replace(S.Q30, fexc_frac=1.0), 1, 0),
+         ("w512_codebook", S.replace(S.W512, layers=1, int2_frac=0.2, fexc_frac=0.3), 1, 2)]
 
 
 @pytest.mark.parametrize("name,cfg,T,seed", CASES, ids=[f"{c[0]}-T{c[2]}-s{c[3]}" for c in CASES])
@@ -52,11 +57,13 @@ def test_mixed_layer_parity(name, cfg, T, seed):
         if seed % 2 else None
     out, ids, w = _run(cfg, L, D, L.expert_fmt, res)
     want, oids, ow = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
-                                 cfg.fmt, residual_bits=res, expert_fmt=L.expert_fmt)
+                                 cfg.fmt, residual_bits=res, expert_fmt=L.expert_fmt,
+                                 codebooks=L.codebooks)
     assert np.array_equal(ids, oids)
     np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
-    n2 = int(np.sum(L.expert_fmt[np.unique(oids)] == O.FMT_INT2))
-    assert 0 < n2 or cfg.int2_frac == 0, "the routed experts should include INT2 ones"
+    routed = L.expert_fmt[np.unique(oids)]
+    assert cfg.int2_frac == 0 or np.any(routed == O.FMT_INT2), "no INT2 expert routed"
+    assert cfg.fexc_frac == 0 or np.any(routed == O.FMT_FEXC), "no FE-XC expert routed"
     check_bf16(out, want, what=f"{name} T={T}")
 
 
