@@ -60,6 +60,9 @@ WORKLOADS = {
                              scales=(0.002, 0.01), logits="normal+bias", layers=24),
     "q30_mixed_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                                scales=(0.002, 0.01), logits="normal", layers=48, int2_frac=0.25),
+    "q30_codebook_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32,
+                                  fmt=FP4, scales=(0.002, 0.01), logits="normal", layers=48,
+                                  int2_frac=0.25, fexc_frac=0.25),
     "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
                               scales=(0.005, 0.02), logits="normal", layers=48),
     "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),
@@ -129,16 +132,19 @@ def _codes(w, shape, g, device):
 
 
 def _expert_formats(w, g, device):
-    """Mixed layers: a per-layer seeded random int2_frac share of the experts is INT2 (their
-    codes are the first quarter of the slab's random bytes, every byte a valid INT2 code)."""
+    """Mixed layers: per-layer seeded random int2_frac and fexc_frac shares of the experts are
+    INT2 and FE-XC (their codes are the first quarter of the slab's random bytes, every byte a
+    valid INT2 or FE-XC code)."""
     import torch
-    frac = w.get("int2_frac", 0.0)
-    if frac <= 0:
+    f2, fx = w.get("int2_frac", 0.0), w.get("fexc_frac", 0.0)
+    if f2 <= 0 and fx <= 0:
         return None
     E = w["E"]
     f = torch.full((E,), FP4, dtype=torch.uint8, device=device)
-    cold = torch.randperm(E, device=device, generator=g)[: int(round(frac * E))]
-    f[cold] = 3  # INT2
+    cold = torch.randperm(E, device=device, generator=g)
+    n2, nx = int(round(f2 * E)), int(round(fx * E))
+    f[cold[:n2]] = 3           # INT2
+    f[cold[n2:n2 + nx]] = 4    # FE-XC
     return f
 
 
@@ -164,6 +170,8 @@ def build_moe_workload(w, seed: int = 0, device="cuda"):
             wr=(torch.randn((H, E), device=device, generator=g) / H ** 0.5).to(torch.bfloat16)
             if w["logits"] == "router" else None,
             efmt=_expert_formats(w, g, device),
+            cb=(2.0 * torch.randn((E, 2, 2, 256, 8), device=device, generator=g)).to(torch.bfloat16)
+            if w.get("fexc_frac", 0.0) > 0 else None,
         ))
     x = torch.randn((T, H), device=device, generator=g).to(torch.bfloat16)
     return x, out
@@ -314,7 +322,7 @@ def bench_moe(w, args, dev, stream, B):
             return
         if L["efmt"] is not None:
             B.moe_fp4_layer_mixed(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"],
-                                  L["efmt"], G, residual=xin if chain else None,
+                                  L["efmt"], G, codebooks=L["cb"], residual=xin if chain else None,
                                   out=xs[l + 1], workspace=ws, flags=flags)
             return
         B.moe_fp4_layer(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
@@ -363,9 +371,11 @@ def bench_moe(w, args, dev, stream, B):
         tot = 0
         for lg, L in zip(lgs, layers):
             act = torch.unique(torch.topk(lg, k, dim=1).indices)
-            n2 = int((L["efmt"][act] == 3).sum())
+            n2 = int((L["efmt"][act] >= 3).sum())   # INT2 and FE-XC: 2 bits per weight
             n_int2 += n2
             tot += (act.numel() - n2) * per_expert + n2 * i2
+            if L["cb"] is not None:                   # codebooks of the routed FE-XC experts
+                tot += int((L["efmt"][act] == 4).sum()) * 2 * 2 * 256 * 8 * 2
         abytes = tot / n_layers
         n_int2 /= n_layers
     if router:
@@ -402,8 +412,9 @@ def bench_moe(w, args, dev, stream, B):
               "active_experts_per_layer_mean": round(sum(n_active) / n_layers, 2),
               "active_bytes_per_layer": round(abytes)}
     if layers[0]["efmt"] is not None:
-        config["int2_experts_share"] = w["int2_frac"]
-        config["int2_active_experts_per_layer_mean"] = round(n_int2, 2)
+        config["int2_experts_share"] = w.get("int2_frac", 0.0)
+        config["fexc_experts_share"] = w.get("fexc_frac", 0.0)
+        config["two_bit_active_experts_per_layer_mean"] = round(n_int2, 2)
     return dict(value=round(us_per_layer, 3), unit="us/layer", ms_per_step=ms_per_step,
                 achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
 

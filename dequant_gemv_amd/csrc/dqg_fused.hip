@@ -185,6 +185,13 @@ __device__ __forceinline__ uint32_t byte_of(const uint4& w, int j) {
   const uint32_t d = (j < 4) ? w.x : (j < 8) ? w.y : (j < 12) ? w.z : w.w;
   return (d >> (8 * (j & 3))) & 0xFFu;
 }
+// 16 bytes per lane from global memory straight into LDS, through no registers: the wave's
+// lanes land in consecutive 16-byte slots from dst_wave, which must be the same in every lane
+__device__ __forceinline__ void copy_to_lds16(const uint4* src, uint4* dst_wave) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src),
+                                   (__attribute__((address_space(3))) void*)dst_wave, 16, 0, 0);
+}
+
 template <int ROWS>
 __device__ __forceinline__ void rows_dot_x_fexc(const uint4 (&wv)[ROWS / 2],
                                                 const uint32_t (&xr)[ROWS], const uint4* cb,
@@ -528,6 +535,14 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
         i2 = f == FMT_INT2 || fx;
       }
     }
+    if constexpr (FMT == FMT_FP4) {
+      if (fx) {  // the expert's gate_up codebooks, copied into LDS ahead of its codes
+        const uint4* src = reinterpret_cast<const uint4*>(a.cb) + (size_t)e * 1024;
+        const int wb = 64 * __builtin_amdgcn_readfirstlane(tid >> 6);
+        copy_to_lds16(src + tid, s_cb + wb);
+        copy_to_lds16(src + 256 + tid, s_cb + 256 + wb);
+      }
+    }
     uint4 wvv[GUR];
     if (i2)
       load_rows(w + (size_t)(r0 / 2) * ld + col0, ld, reinterpret_cast<uint4(&)[GUR / 2]>(wvv));
@@ -552,11 +567,8 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     if constexpr (FMT == FMT_FP8) {
       rows_dot_x_fp8<GUR>(wvv, xr, accb);
     } else {
-      if (fx) {  // the expert's gate_up codebooks, loaded after its codes are in flight
-        const uint4* src = reinterpret_cast<const uint4*>(a.cb) + (size_t)e * 1024;
-        const uint4 v0 = src[tid], v1 = src[tid + 256];
-        s_cb[tid] = v0;
-        s_cb[tid + 256] = v1;
+      if (fx) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's codebook copies have landed
         __syncthreads();
         rows_dot_x_fexc<GUR>(reinterpret_cast<const uint4(&)[GUR / 2]>(wvv), xr, s_cb, accb);
       } else if (i2) {
@@ -616,8 +628,8 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   bool fx = false;  // FE-XC: codebook set `cset` (the chunk's first or second slot)
   int cset = 0;
   // FE-XC codebooks of the chunk's first two slots (a chunk spans at most two when
-  // I / 2 >= 256, which the host requires with codebooks), staged by the whole workgroup
-  // (loaded after the h gather, so that they hold no registers across it)
+  // I / 2 >= 256, which the host requires with codebooks), copied into LDS by the whole
+  // workgroup once the weight loads are issued, so that they land during the h gather
   int stage_e[2] = {-1, -1};
   const int sl_a = (c * FX_DROWS) / rows_per_slot;
   if constexpr (FMT == FMT_FP4) {
@@ -650,6 +662,19 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
       load_rows(wd + (size_t)r0 * H + col0, H, wvv);
     scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((KB * r0) / a.group) * H + col0,
              sf);
+  }
+  const bool staged = stage_e[0] >= 0 || stage_e[1] >= 0;  // uniform
+  if constexpr (FMT == FMT_FP4) {
+    if (staged) {
+      const int wb = 64 * __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+      for (int z = 0; z < 2; ++z)
+        if (stage_e[z] >= 0) {
+          const uint4* src = reinterpret_cast<const uint4*>(a.cb) + (size_t)stage_e[z] * 1024 + 512;
+          copy_to_lds16(src + tid, s_cb + 512 * z + wb);
+          copy_to_lds16(src + 256 + tid, s_cb + 512 * z + 256 + wb);
+        }
+    }
   }
   // gather h for this unit's rows: flat h index f = KB R covers the NH values from NH c on;
   // thread t < NH / 2 owns f = NH c + 2t, +1 (two columns of one slot); the KS partial gate
@@ -698,24 +723,8 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     reinterpret_cast<float2*>(hl)[tid] = h2;
   }
-  if constexpr (FMT == FMT_FP4) {
-    if (stage_e[0] >= 0 || stage_e[1] >= 0) {
-      uint4 v[4];
-#pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.cb) +
-                           (size_t)(stage_e[z] >= 0 ? stage_e[z] : 0) * 1024 + 512;
-        v[2 * z] = stage_e[z] >= 0 ? src[tid] : make_uint4(0, 0, 0, 0);
-        v[2 * z + 1] = stage_e[z] >= 0 ? src[tid + 256] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int z = 0; z < 2; ++z)
-        if (stage_e[z] >= 0) {
-          s_cb[512 * z + tid] = v[2 * z];
-          s_cb[512 * z + tid + 256] = v[2 * z + 1];
-        }
-    }
-  }
+  if constexpr (FMT == FMT_FP4)
+    if (staged) __builtin_amdgcn_s_waitcnt(0);  // this wave's codebook copies have landed
   __syncthreads();
   float acc[16];
 #pragma unroll
