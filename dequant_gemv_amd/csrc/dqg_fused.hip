@@ -23,7 +23,7 @@
 //     from cache the second time.)
 //   down units (mt, c): output columns [128 mt, 128 mt + 128) (8 lanes) over byte rows
 //     [256 c, 256 c + 256) of the concatenated per-slot down matrices (32 row-lanes x 8
-//     rows); for T > 1 a token's rows fill whole chunks.  On layers with >= 1 MiB of gate_up
+//     rows); for T > 1 a token's rows fill whole chunks.  On layers with >= 16 MiB of gate_up
 //     weights per token, their weight loads wait for the first gate/up partial of their
 //     range (the gate_up loads, which are on the critical path, get the bandwidth first);
 //     then the threads gather the KS partial gate/up pairs of the unit's 256 KB h values
@@ -323,15 +323,37 @@ __device__ __forceinline__ void rows_dot_f32(const uint4 (&wv)[ROWS], const floa
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void load_rows(const uint8_t* wp, size_t ld, uint4 (&wv)[ROWS]) {
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
+// With one token the k experts are distinct and their weights and scales are read once per
+// call: non-temporal loads (`nt`, uniform), so that streaming them does not evict from L2 the
+// exchange rows and the code that the end of the chain runs.  With several tokens an expert
+// chosen twice is streamed once per slot and its repeats are meant to hit L2: plain loads.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_nt t = __builtin_nontemporal_load(static_cast<const u32x4_nt*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-__device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16]) {
-  const uint4 s0 = *reinterpret_cast<const uint4*>(sp);
-  const uint4 s1 = *reinterpret_cast<const uint4*>(sp + 8);
+template <int ROWS>
+__device__ __forceinline__ void load_rows(const uint8_t* wp, size_t ld, uint4 (&wv)[ROWS],
+                                          bool nt) {
+  if (nt) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) wv[r] = ld_stream16(wp + (size_t)r * ld);
+  } else {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) wv[r] = *reinterpret_cast<const uint4*>(wp + (size_t)r * ld);
+  }
+}
+
+__device__ __forceinline__ void scales16(const uint16_t* sp, float (&sf)[16], bool nt) {
+  uint4 s0, s1;
+  if (nt) {
+    s0 = ld_stream16(sp);
+    s1 = ld_stream16(sp + 8);
+  } else {
+    s0 = *reinterpret_cast<const uint4*>(sp);
+    s1 = *reinterpret_cast<const uint4*>(sp + 8);
+  }
   const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -363,18 +385,20 @@ __device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t
   return corr;
 }
 
-// Poll n (<= FX_GATHER) published floats p[i * stride] until none is the empty pattern; all
-// loads of one round are in flight together.  Returns false on timeout.
-constexpr int FX_GATHER = 32;
+// Poll n (1 <= n <= FX_GATHER) published floats p[i * stride] until none is the empty
+// pattern; all loads of one round are in flight together.  Every round issues FX_GATHER
+// loads (those past n repeat the last one), so that the code has no branches: the units that
+// run it do so once per launch, at the end of the layer's dependency chain, from an
+// instruction cache that the weight stream has left cold, and code size is time there.
+// Returns false on timeout.
+constexpr int FX_GATHER = 16;
 __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n, float* v) {
   for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
     bool ready = true;
 #pragma unroll
-    for (int i = 0; i < FX_GATHER; ++i)
-      if (i < n) v[i] = ld_sc1(p, (size_t)i * stride);
+    for (int i = 0; i < FX_GATHER; ++i) v[i] = ld_sc1(p, (size_t)(i < n ? i : n - 1) * stride);
 #pragma unroll
-    for (int i = 0; i < FX_GATHER; ++i)
-      if (i < n) ready = ready && (__float_as_uint(v[i]) != 0u);
+    for (int i = 0; i < FX_GATHER; ++i) ready = ready && (__float_as_uint(v[i]) != 0u);
     if (ready) return true;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -397,6 +421,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   __shared__ uint4 s_cb[FMT == FMT_FP4 ? 2 * 512 : 1];  // FE-XC codebooks: 2 sets of [2][256]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, k = a.k;
+  const bool nt = a.T == 1;  // weights streamed once: non-temporal loads
   const int NT = I / 128, KS = a.ks, NC = a.n_chunks;
   const size_t rsz = (size_t)a.rs * a.T * a.E;       // one copy of the router partial rows
 
@@ -545,12 +570,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     uint4 wvv[GUR];
     if (i2)
-      load_rows(w + (size_t)(r0 / 2) * ld + col0, ld, reinterpret_cast<uint4(&)[GUR / 2]>(wvv));
+      load_rows(w + (size_t)(r0 / 2) * ld + col0, ld, reinterpret_cast<uint4(&)[GUR / 2]>(wvv),
+                nt);
     else
-      load_rows(w + (size_t)r0 * ld + col0, ld, wvv);
+      load_rows(w + (size_t)r0 * ld + col0, ld, wvv, nt);
     float sf[16];
     scales16(a.sgu + (size_t)e * (H / a.group) * ld + (size_t)((KB * r0) / a.group) * ld + col0,
-             sf);
+             sf, nt);
     uint32_t xr[GUR];
     float corr = 0.0f;
     if constexpr (FMT == FMT_FP8)  // x pairs of K indices r0 .. r0 + GUR - 1
@@ -657,11 +683,11 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const uint8_t* wd = a.wd + (size_t)e * rows_per_slot * H;
     if (i2)
       load_rows(wd + (size_t)(r0 / 2) * H + col0, H,
-                reinterpret_cast<uint4(&)[FX_D_ROWS / 2]>(wvv));
+                reinterpret_cast<uint4(&)[FX_D_ROWS / 2]>(wvv), nt);
     else
-      load_rows(wd + (size_t)r0 * H + col0, H, wvv);
+      load_rows(wd + (size_t)r0 * H + col0, H, wvv, nt);
     scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((KB * r0) / a.group) * H + col0,
-             sf);
+             sf, nt);
   }
   const bool staged = stage_e[0] >= 0 || stage_e[1] >= 0;  // uniform
   if constexpr (FMT == FMT_FP4) {
@@ -691,19 +717,20 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
       bool ok = false;
       for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
         f32x2_t gv[MAX_KS], uv[MAX_KS];
+        // every round reloads the partials (the compiler must not keep an earlier round's
+        // values) and issues MAX_KS loads of each (those past KS repeat the last: no branches)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int q = 0; q < MAX_KS; ++q) {
-          if (q < KS) {
-            gv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024, 0, CPOL_SC1);
-            uv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + q * 1024 + 512, 0, CPOL_SC1);
-          }
+          const int qq = q < KS ? q : KS - 1;
+          gv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + qq * 1024, 0, CPOL_SC1);
+          uv[q] = __builtin_amdgcn_raw_buffer_load_b64(gr, base + qq * 1024 + 512, 0, CPOL_SC1);
         }
         bool ready = true;
 #pragma unroll
         for (int q = 0; q < MAX_KS; ++q)
-          if (q < KS)
-            ready = ready && __float_as_uint(gv[q].x) && __float_as_uint(gv[q].y) &&
-                    __float_as_uint(uv[q].x) && __float_as_uint(uv[q].y);
+          ready = ready && __float_as_uint(gv[q].x) && __float_as_uint(gv[q].y) &&
+                  __float_as_uint(uv[q].x) && __float_as_uint(uv[q].y);
         if (ready) {
           g2 = gv[0];
           u2 = uv[0];
@@ -719,7 +746,9 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
         __builtin_amdgcn_s_sleep(4);
       }
       if (!ok) atomicOr(a.err, 2);
-      h2 = make_float2(g2.x / (1.0f + expf(-g2.x)) * u2.x, g2.y / (1.0f + expf(-g2.y)) * u2.y);
+      // __expf (v_exp_f32 on x log2(e)): a short sequence on the chain's cold tail
+      h2 = make_float2(g2.x / (1.0f + __expf(-g2.x)) * u2.x,
+                       g2.y / (1.0f + __expf(-g2.y)) * u2.y);
     }
     reinterpret_cast<float2*>(hl)[tid] = h2;
   }
@@ -865,7 +894,7 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, boo
   f.chunks_per_token = f.n_chunks / T;
   f.n_a = T * k * (I / 128) * f.ks;
   f.n_b = f.n_mt * f.n_chunks;
-  f.hold_down = (size_t)k * (H / kb) * (2 * (size_t)I) >= ((size_t)1 << 20);
+  f.hold_down = (size_t)k * (H / kb) * (2 * (size_t)I) >= ((size_t)1 << 24);
   f.calls = reinterpret_cast<unsigned int*>(p);
   f.rcalls = reinterpret_cast<unsigned int*>(p + 64);  // the router's own parity counter
   f.gpart = reinterpret_cast<float*>(p + 256);
