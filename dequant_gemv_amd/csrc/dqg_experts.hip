@@ -38,6 +38,9 @@ constexpr int EX_LDS = 8192;      // floats of LDS: the operand window, then the
 constexpr int EX_MAX_SPLIT = 64;  // K splits of gate_up, at most
 constexpr int EX_MAX_SPLIT_GEMV = 64;  // K splits of the GEMV, at most
 constexpr int EX_CPOL_SC1 = 16;   // cache policy: agent-coherent access
+// cache policy: non-temporal (the dense GEMV reads each weight once per call; streaming them
+// leaves L2 to the partial rows and the code of the split finishers)
+constexpr int EX_STREAM = 2;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -89,19 +92,21 @@ __device__ __forceinline__ bool ready4(float4 v) {
          (__float_as_uint(v.z) != 0u) & (__float_as_uint(v.w) != 0u);
 }
 // Waits until the n (<= 16) floats at byte offsets off[i] are all published (bounded:
-// returns false when the wait gives up), then clears them.
+// returns false when the wait gives up), then clears them.  Every one of the 16 offsets
+// must name a published value of this wait: callers fill those past n with repeats of
+// earlier ones, so that the loads, checks and clears run without branches (this runs once,
+// cold, at the end of a dependency chain, where code size is time).
 __device__ __forceinline__ bool take16(__amdgpu_buffer_rsrc_t r, const int (&off)[16], int n,
                                        float (&v)[16]) {
   bool ok = false;
   for (unsigned spin = 0; spin < EX_SPIN_LIMIT; ++spin) {
+    asm volatile("" ::: "memory");  // every round reloads the values
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (i < n) v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off[i], 0,
-                                                                             EX_CPOL_SC1));
+      v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off[i], 0, EX_CPOL_SC1));
     bool all = true;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < n) all = all && (__float_as_uint(v[i]) != 0u);
+    for (int i = 0; i < 16; ++i) all = all && (__float_as_uint(v[i]) != 0u);
     if (all) {
       ok = true;
       break;
@@ -109,8 +114,7 @@ __device__ __forceinline__ bool take16(__amdgpu_buffer_rsrc_t r, const int (&off
     __builtin_amdgcn_s_sleep(8);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (i < n) __builtin_amdgcn_raw_buffer_store_b32(0u, r, off[i], 0, EX_CPOL_SC1);
+  for (int i = 0; i < 16; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, r, off[i], 0, EX_CPOL_SC1);
   return ok;
 }
 
@@ -154,16 +158,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t view_rsrc(const void* p, size_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
+template <int WAUX>
 __device__ __forceinline__ void load_wblock(const ExpertView& v, int blk, int kg, int col,
                                             bool ok, WBlock& o) {
   const int wo = ok ? (16 * blk + 4 * kg) * v.ld + col : EX_OOB;
   const int so = ok ? (((32 * blk) / v.group) * v.ld + col) * 2 : EX_OOB;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(v.w, wo, j * v.ld, 0);
+    const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(v.w, wo, j * v.ld, WAUX);
     o.w[j] = make_uint2(d.x, d.y);
   }
-  const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.s, so, 0, 0);
+  const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(v.s, so, 0, WAUX);
   o.s = make_uint4(d.x, d.y, d.z, d.w);
 }
 
@@ -305,15 +310,16 @@ struct Acc<BODY_MFMA, MT> {
 };
 
 // The lane's weights of one group: RBW blocks (b = g0 + off + step * r); blocks past b1
-// (and columns past the tile) load as zero.
-template <int RBW>
+// (and columns past the tile) load as zero.  WAUX: the loads' cache policy (EX_STREAM for
+// weights that are read once per call).
+template <int RBW, int WAUX = 0>
 __device__ __forceinline__ void load_group(const ExpertView& v, int g0, int off, int step,
                                            int b1, int kg, int col, bool col_ok,
                                            WBlock (&wb)[RBW]) {
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     const int b = g0 + off + step * r;
-    load_wblock(v, b, kg, col, col_ok && b < b1, wb[r]);
+    load_wblock<WAUX>(v, b, kg, col, col_ok && b < b1, wb[r]);
   }
 }
 
@@ -450,7 +456,7 @@ __device__ __forceinline__ void compute_group(const WBlock (&wb)[RBW], const uin
 // workgroup streams a few batches (many workgroups keep the bytes in flight; fewer splits
 // keep the partial traffic low).
 // Leaves the LDS free (a barrier follows the last batch).
-template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP>
+template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP, int WAUX = 0>
 __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool col_ok,
                                               const OpSrc& src, const int* s_slot, int nch,
                                               int b0, int b1, int off, float* lds,
@@ -470,7 +476,7 @@ __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool
       for (int i = 0; i < 8; ++i) acc.v[m][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   for (int bb = b0; bb < b1; bb += GB) {
-    if (bb != b0) load_group<RBW>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
+    if (bb != b0) load_group<RBW, WAUX>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
     Window<FMT, GB, NTOK> wnd;
     wnd.load(src, s_slot, nch, bb, b1);
     if (bb != b0) __syncthreads();  // the previous batch is done with the window
@@ -483,25 +489,23 @@ __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool
 
 // One pass of a phase: dispatch the token count (VALU: 1, 2, 4 or 8 rows; MFMA: MT tiles)
 // to a compile-time width.
-template <int FMT, int VT, int RBW, int STEP>
+template <int FMT, int VT, int RBW, int STEP, int WAUX = 0>
 __device__ __forceinline__ void stream_valu(const ExpertView& v, int col, bool col_ok,
                                             const OpSrc& src, const int* s_slot, int nch, int b0,
                                             int b1, int off, float* lds, WBlock (&wa)[RBW],
                                             Acc<BODY_VALU, VT>& acc) {
   if (VT <= 1 || nch <= 1)
-    stream_expert<FMT, BODY_VALU, VT, 1, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0, b1,
-                                                    off, lds, wa, acc);
+    stream_expert<FMT, BODY_VALU, VT, 1, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
+                                                          b1, off, lds, wa, acc);
   else if (VT <= 2 || nch <= 2)
-    stream_expert<FMT, BODY_VALU, VT, (VT < 2 ? VT : 2), RBW, STEP>(v, col, col_ok, src, s_slot,
-                                                                   nch, b0, b1, off, lds, wa,
-                                                                   acc);
+    stream_expert<FMT, BODY_VALU, VT, (VT < 2 ? VT : 2), RBW, STEP, WAUX>(
+        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc);
   else if (VT <= 4 || nch <= 4)
-    stream_expert<FMT, BODY_VALU, VT, (VT < 4 ? VT : 4), RBW, STEP>(v, col, col_ok, src, s_slot,
-                                                                   nch, b0, b1, off, lds, wa,
-                                                                   acc);
+    stream_expert<FMT, BODY_VALU, VT, (VT < 4 ? VT : 4), RBW, STEP, WAUX>(
+        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc);
   else
-    stream_expert<FMT, BODY_VALU, VT, VT, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0, b1,
-                                                     off, lds, wa, acc);
+    stream_expert<FMT, BODY_VALU, VT, VT, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
+                                                           b1, off, lds, wa, acc);
 }
 
 // 16-bit h operand pair (bf16 for FP4, fp16 for INT4) of SiLU(g) * u, two columns
@@ -892,12 +896,12 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
   for (int c0 = 0; c0 < T; c0 += CH) {
     const int nch = min(CH, T - c0);
     WBlock wa[2];  // the first group's weights load while the token list is set up
-    load_group<2>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
+    load_group<2, EX_STREAM>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
     if (tid < nch) s_slot[tid] = c0 + tid;
     __syncthreads();
     if constexpr (MT > 0) {
       Acc<BODY_MFMA, MT> acc;
-      stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1,
+      stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 4, EX_STREAM>(v, col, col_ok, src, s_slot, nch, b0, b1,
                                                        wv, lds, wa, acc);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -921,7 +925,8 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
       }
     } else {
       Acc<BODY_VALU, VT> acc;
-      stream_valu<FMT, VT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1, wv, lds, wa, acc);
+      stream_valu<FMT, VT, 2, 4, EX_STREAM>(v, col, col_ok, src, s_slot, nch, b0, b1, wv, lds, wa,
+                                       acc);
 #pragma unroll
       for (int hh = 0; hh < (VT + 3) / 4; ++hh) {
         if (4 * hh >= nch) break;
