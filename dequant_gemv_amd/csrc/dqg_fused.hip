@@ -471,14 +471,17 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
       const int par = (int)((__builtin_amdgcn_readfirstlane(c0) >> 20) & 1u);
       const float* rp = a.rpart + par * rsz + (size_t)tok * a.E;
       const size_t st = (size_t)a.T * a.E;
-      const bool in0 = lane < a.E, in1 = lane + 64 < a.E;
+      // branch-free rounds: splits past rs repeat the last one and lanes past E read
+      // element E - 1 (their values are polled but never summed into a kept logit)
+      const int e0 = min(lane, a.E - 1), e1 = min(lane + 64, a.E - 1);
       bool ok = false;
       for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
         float v0[16], v1[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          v0[q] = (q < a.rs && in0) ? ld_sc1(rp, q * st + lane) : 1.0f;
-          v1[q] = (q < a.rs && in1) ? ld_sc1(rp, q * st + lane + 64) : 1.0f;
+          const size_t qo = (size_t)(q < a.rs ? q : a.rs - 1) * st;
+          v0[q] = ld_sc1(rp, qo + e0);
+          v1[q] = ld_sc1(rp, qo + e1);
         }
         bool ready = true;
 #pragma unroll
