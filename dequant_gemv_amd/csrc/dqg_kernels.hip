@@ -114,6 +114,39 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
     long long* scratch = reinterpret_cast<long long*>(sm + sched_int_words(E)) +
                          (size_t)wv * sched_scratch_entries(E);
     const int stride = RW ? RW : SCHED_THREADS / 64;
+    if (E <= 128) {
+      // the logits of the wave's next 4 tokens are loaded together, then selected one after
+      // another (rows shift through registers): one memory round trip per 4 tokens
+      int* sel = reinterpret_cast<int*>(scratch + 64 * 2 + 4);
+      for (int t0 = wv; t0 < T && wv < RW; t0 += 4 * stride) {
+        int key[4][2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float* row = logits + (size_t)min(t0 + r * stride, T - 1) * E;
+#pragma unroll
+          for (int v = 0; v < 2; ++v) key[r][v] = logit_key(row[min(lane + 64 * v, E - 1)]);
+        }
+#pragma unroll 1
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + r * stride;
+          if (t >= T) break;
+          int e;
+          float w;
+          wave_topk_select_keys<2>(key[0], E, k, lane, scratch, sel, sel + 64);
+          wave_topk_weights(sel, sel + 64, k, lane, &e, &w);
+          if (lane < k) {
+            a.ids_w[(size_t)t * k + lane] = e;
+            a.wts_w[(size_t)t * k + lane] = w;
+            if (in_lds) lids[t * k + lane] = e;
+          }
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            key[q][0] = key[q + 1][0];
+            key[q][1] = key[q + 1][1];
+          }
+        }
+      }
+    } else
     for (int t = wv; t < T && (RW == 0 || wv < RW); t += stride) {
       int e;
       float w;
