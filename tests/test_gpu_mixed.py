@@ -67,19 +67,27 @@ def test_mixed_layer_parity(name, cfg, T, seed):
     check_bf16(out, want, what=f"{name} T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 4])
-def test_all_fp4_table_equals_the_fp4_layer(T):
+@pytest.mark.parametrize("name,base,T", [("q30", S.Q30_BATCH, 1), ("q30", S.Q30_BATCH, 4),
+                                         ("w512", S.replace(S.W512, layers=1), 1),
+                                         ("w512", S.replace(S.W512, layers=1), 8)])
+def test_all_fp4_table_equals_the_fp4_layer(name, base, T):
     """With no INT2 entry the mixed call runs exactly the FP4 arithmetic: bitwise equal to
-    moe_fp4_layer on the same inputs."""
+    moe_fp4_layer on the same inputs (ids and weights too).  The two calls run different
+    instances of the kernel: the mixed one with the format-table paths, the plain one with
+    them compiled out."""
     B = _b()
-    cfg = S.Q30_BATCH.with_T(T)
+    cfg = base.with_T(T)
     L, D = _mixed(cfg, 21)
     table = np.full(cfg.E, S.FMT_FP4, np.uint8)
-    got, _, _ = _run(cfg, L, D, table)
+    got, gids, gw = _run(cfg, L, D, table)
+    ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
     ref = B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
-                          D["s_d"], cfg.group, cfg.fmt)
+                          D["s_d"], cfg.group, cfg.fmt, ids_out=ids, weights_out=w)
     torch.cuda.synchronize()
     assert np.array_equal(got, bits16(ref))
+    assert np.array_equal(gids, ids.cpu().numpy())
+    assert np.array_equal(gw.view(np.uint32), w.cpu().numpy().view(np.uint32))
 
 
 def test_mixed_and_plain_calls_share_a_workspace():
