@@ -41,7 +41,8 @@
 // on every gate_up unit of the token); producers clear their slots of copy 1-p, which the
 // previous call used and the next call will use.  Each token count T has its own counter
 // and buffers in the workspace, so that calls with different T never leave data in each
-// other's slots.  The router's partial rows follow the same scheme with a counter of their
+// other's slots (likewise each format class: the 4-bit formats and FP8).  The router's
+// partial rows follow the same scheme with a counter of their
 // own that only calls with router units advance, so that calls without them (which leave
 // those rows alone) cannot put a later router call on a copy that still holds old rows.
 // A unit only waits on units with lower block ids, so in-order dispatch
@@ -56,7 +57,6 @@
 namespace dqg {
 
 constexpr int FX_THREADS = 256;
-constexpr int FX_RL = 64;          // row-lanes per workgroup (4 lanes per byte row)
 constexpr unsigned FX_SPIN_LIMIT = 1u << 20;
 constexpr int CPOL_SC1 = 16;       // cache-policy operand: agent-coherent access
 
