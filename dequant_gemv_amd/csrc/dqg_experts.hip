@@ -872,7 +872,8 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
   };
 
   if (s == S) {  // finisher: sum the S split partials in split order
-    wg_wait_published(pr, (((S - 1) * Tc + 0) * N + m0c) * 4);
+    // every thread polls its own partials directly (a one-lane wait on the last split before
+    // the gather would add a round trip to the end of the call: 10.4 -> 9.9 us at N = 8192)
     for (int it = tid; it < T * 128; it += EX_THREADS) {
       const int t = it >> 7, c = it & 127;
       if (c >= ncols) continue;
