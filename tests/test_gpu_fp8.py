@@ -117,3 +117,22 @@ def test_formats_alternate_on_one_workspace():
     want, _, _ = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
                              cfg.fmt)
     check_bf16(first[("fp8", 4)], want, what="fp8 T=4 on the shared workspace")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_fp8_layer_w512_shape(T):
+    """FP8 weights at the 512-expert shape (k = 10, I = 512, skewed routing), T = 1 and 8."""
+    B = _b()
+    cfg = S.replace(S.W512, layers=1, fmt=S.FMT_FP8).with_T(T)
+    lg = S.moe_layer_logits(cfg, 5)
+    ids, _ = O.topk_route(lg, cfg.k)
+    L = S.make_moe_layer(cfg, 5, experts=np.unique(ids))
+    D = upload_layer(L, np.unique(ids))
+    gids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    out = B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"],
+                          D["s_d"], cfg.group, cfg.fmt, ids_out=gids)
+    torch.cuda.synchronize()
+    want, oids, _ = O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group,
+                                cfg.fmt)
+    assert np.array_equal(gids.cpu().numpy(), oids)
+    check_bf16(bits16(out), want, what=f"fp8 w512 T={T}")

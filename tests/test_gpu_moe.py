@@ -462,3 +462,16 @@ def test_fused_layer_int4_q30_shape(T):
     want, oids, ow = _oracle_layer(cfg, L)
     assert np.array_equal(ids, oids)
     check_bf16(out, want, what=f"int4 q30 T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_fused_layer_int4_w512_shape(T):
+    """INT4 weights through the single-launch layer at the 512-expert shape (k = 10, I = 512:
+    the wider routing selection and a chunk that spans slots), T = 1 and 8."""
+    cfg = S.replace(S.W512, layers=1, fmt=S.FMT_INT4).with_T(T)
+    L, D = _layer(cfg, seed=70 + T)
+    out, ids, w = _run_layer(cfg, L, D)
+    want, oids, ow = _oracle_layer(cfg, L)
+    assert np.array_equal(ids, oids)
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    check_bf16(out, want, what=f"int4 w512 T={T}")
