@@ -53,6 +53,7 @@ SIGNATURES = {
                                  _P, _P, _P, _P, _Z, _P]),
     "packed_gemv_int4_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
+    "packed_gemv_int4_noalloc": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
@@ -311,6 +312,25 @@ def packed_gemv_int4(x, w, s, group: int, y=None, workspace=None) -> torch.Tenso
     _check("packed_gemv_int4", LIB.packed_gemv_int4(
         _ptr(x), T, K, N, _ptr(w), _ptr(s), group, _ptr(y), _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream(x)))
+    return y
+
+
+def packed_gemv_int4_noalloc(x, w, s, group: int, y=None, status=None) -> torch.Tensor:
+    """The allocation-free GEMV entry point: split partials in the library's device array.
+    ``y`` (bf16 [T, N]) and ``status`` (int32, one element) are optional device tensors; when
+    ``y`` is None it is allocated here with torch (the C call itself allocates nothing)."""
+    T, K = x.shape
+    N = w.shape[1]
+    _need(x, "x", 2)
+    _need(w, "w", 1, (K // 2, N), x.device)
+    _need(s, "s", 2, (K // group, N), x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", 2, (T, N), x.device)
+    if status is not None:
+        _need(status, "status", 4, (1,), x.device)
+    _check("packed_gemv_int4_noalloc", LIB.packed_gemv_int4_noalloc(
+        _ptr(x), T, K, N, _ptr(w), _ptr(s), group, _ptr(y), _ptr(status), _stream(x)))
     return y
 
 

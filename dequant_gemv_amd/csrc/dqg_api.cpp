@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/dqg.h"
 #include "dqg_internal.hpp"
@@ -273,6 +274,35 @@ bool gemv_sizes_ok(int T, int K, int N, int group) {
   return true;
 }
 
+// ---- allocation-free GEMV: library-owned split-partial scratch -----------------------------
+// [error word, 256 bytes][split partials], one copy per GPU (a device global: it is zero-filled
+// when the code object loads, and every completed call leaves its partials zero again).
+constexpr size_t kScratchPartialBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void** out);
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[256 + kScratchPartialBytes];
+
+namespace {
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DQG_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DQG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DQG_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return DQG_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -460,6 +490,36 @@ int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
   if (gp.S > 1) {
     g.err = static_cast<int*>(workspace);
     g.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
+  }
+  return dqg::launch_gemv_ex(g, gp.mt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+}
+
+int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8_t* w,
+                             const uint16_t* s, int group, uint16_t* y, int* status,
+                             hipStream_t stream) {
+  if (!x || !w || !s || !y) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (!gemv_sizes_ok(T, K, N, group)) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return DQG_ERR_MISALIGNED;
+  if ((uintptr_t)status & 3u) return DQG_ERR_MISALIGNED;
+  // the layout of a workspace sized exactly for T tokens; its partials must fit the scratch
+  const GemvPlan gp = plan_gemv(T, K, N);
+  if (gp.S > 1 && gp.total > 256 + kScratchPartialBytes) return DQG_ERR_WORKSPACE;
+  if (stream) {  // the scratch address below is the current device's: the stream must be on it
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return DQG_ERR_HIP;
+    if (sdev != cur) return DQG_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc != DQG_OK) return rc;
+  GemvArgs g{};
+  g.x = x; g.T = T; g.K = K; g.N = N; g.group = group; g.w = w; g.s = s; g.y = y; g.S = gp.S;
+  g.t_cap = gp.t_cap;
+  if (gp.S > 1) {
+    g.err = status ? status : static_cast<int*>(ws);
+    g.part = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
   }
   return dqg::launch_gemv_ex(g, gp.mt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }

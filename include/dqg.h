@@ -8,7 +8,8 @@
  * the host, so they can be captured into a hipGraph.  The caller keeps every buffer
  * alive until the stream work has completed.  The library owns no device memory and
  * keeps no state between calls (reentrant), except that concurrent calls must not
- * share one workspace.
+ * share one workspace -- and except the one allocation-free entry point,
+ * packed_gemv_int4_noalloc, whose scratch array the library holds per GPU.
  *
  * Argument checks happen on the host before any launch; a failed check returns a
  * negative status and launches nothing.  A launch failure is reported as DQG_ERR_HIP
@@ -256,6 +257,24 @@ size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
 int packed_gemv_int4(const uint16_t* x, int T, int K, int N, const uint8_t* w,
                      const uint16_t* s, int group, uint16_t* y, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * packed_gemv_int4_noalloc -- packed_gemv_int4 for callers that cannot allocate device memory
+ * or pass a workspace (code under hipGraph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, arithmetic, kernels and results as packed_gemv_int4 with a
+ * workspace sized for T (bitwise identical outputs), except that the K-split partials live in
+ * a library-owned device array of 16 MiB + 256 bytes per GPU, held until the process ends.
+ * The call allocates nothing.  status: NULL, or a device int32 into which a call ORs bit 1
+ * when a wait between workgroups gave up (the output is then not valid; the caller clears
+ * it).  Calls whose partials (K splits x T x N x 4 bytes) exceed 16 MiB return
+ * DQG_ERR_WORKSPACE before any launch.  Calls that may overlap on one GPU (different
+ * streams, or another thread) race on that array and must not; stream must belong to the
+ * current device.  Every completed call leaves the array's partials zero; after a status bit
+ * 1 that no longer holds for the rest of the process.
+ */
+int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8_t* w,
+                             const uint16_t* s, int group, uint16_t* y, int* status,
+                             hipStream_t stream);
 
 /*
  * packed_dequant_f32 -- TEST AID: dequantize one packed matrix with the same in-register

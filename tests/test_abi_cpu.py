@@ -208,3 +208,15 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         B.topk_route(torch.zeros(1, 8), 2)
+
+
+def test_noalloc_gemv_host_checks():
+    """The allocation-free GEMV validates on the host before it touches the device: bad
+    arguments, and partials beyond its 16 MiB scratch (T = 16, N = 65536: 6 K splits x 16 x
+    65536 x 4 bytes = 25 MB) return an error and launch nothing."""
+    f = B.LIB.packed_gemv_int4_noalloc
+    assert f(0, 1, 5120, 8192, A, A, 128, A, None, None) == B.DQG_ERR_INVALID_ARG
+    assert f(A, 1, 5120, 100, A, A, 128, A, None, None) == B.DQG_ERR_UNSUPPORTED
+    assert f(MIS, 1, 5120, 8192, A, A, 128, A, None, None) == B.DQG_ERR_MISALIGNED
+    assert f(A, 1, 5120, 8192, A, A, 128, A, A + 2, None) == B.DQG_ERR_MISALIGNED
+    assert f(A, 16, 5120, 65536, A, A, 128, A, None, None) == B.DQG_ERR_WORKSPACE
