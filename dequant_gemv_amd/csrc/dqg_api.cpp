@@ -74,6 +74,16 @@ int moe_split_max(int nblk, int per_wg, int cap, long long tk_cap, long long row
   return (int)std::max(1LL, std::min<long long>(std::min((nblk + per_wg - 1) / per_wg, cap), fit));
 }
 
+// Bytes of a split-partial region: splits x tk_cap x row_bytes with the uncapped number of
+// splits, but never more than 2^31 (the capped count keeps offsets below that anyway).  The
+// bound grows with t_cap, so the workspace total is monotonic in the capacity and the layout
+// a workspace gets depends only on its size (the capped count alone would shrink the region,
+// and the total with it, each time the cap drops by one split).
+size_t split_region_bytes(int nblk, int per_wg, int cap, long long tk_cap, long long row_bytes) {
+  const long long uncapped = std::min((nblk + per_wg - 1) / per_wg, cap);
+  return (size_t)std::min<long long>(uncapped * tk_cap * row_bytes, 1LL << 31);
+}
+
 void moe_layout(MoePlan& p, int t_cap) {
   const int H = p.H, I = p.I, k = p.k;
   const long long tkc = (long long)t_cap * k;
@@ -93,8 +103,8 @@ void moe_layout(MoePlan& p, int t_cap) {
   p.o_ids = o;     o = up256(o + sizeof(int) * tkc);
   p.o_wts = o;     o = up256(o + sizeof(float) * tkc);
   p.o_h = o;       o = up256(o + sizeof(uint16_t) * (size_t)tkc * I);
-  p.o_pgu = o;     o = up256(o + sizeof(float) * (size_t)p.sgu_max * tkc * 2 * I);
-  p.o_pdn = o;     o = up256(o + sizeof(float) * (size_t)p.sdn_max * tkc * H);
+  p.o_pgu = o;     o = up256(o + split_region_bytes(H / 32, 4, dqg::ex_max_split(), tkc, 8LL * I));
+  p.o_pdn = o;     o = up256(o + split_region_bytes(I / 32, 8, kMaxSplitDown, tkc, 4LL * H));
   p.o_rtp = o;     o = up256(o + sizeof(float) * (size_t)dqg::router_splits(H) * t_cap * p.E);
   p.o_rtl = o;     o = up256(o + sizeof(float) * (size_t)t_cap * p.E);
   p.total = o;

@@ -98,10 +98,12 @@ int topk_route(const float* logits, int T, int E, int k, int32_t* ids, float* we
  * [0, E) was seen -- the slot then contributes zero; bit 1: a wait between workgroups gave
  * up -- the output of that call is not valid), the device-built expert schedule, and
  * exchange buffers that must hold zeros between calls.  Zero-fill a workspace once before
- * its first use; every completed call leaves it ready for the next.  Its layout depends
- * only on (H, I, E, k) and its size, so one workspace serves calls with any T up to the T
- * it was sized for.  Calls that may run at the same time must not share a workspace.  Only
- * the caller clears the error word.
+ * its first use; every completed call leaves it ready for the next -- except a call that set
+ * bit 1: a late producer may then leave a published value behind, so zero-fill the whole
+ * workspace again before reusing it.  Its layout depends only on (H, I, E, k) and its size
+ * (the size grows with T), so one workspace serves calls with any T up to the T it was sized
+ * for.  Calls that may run at the same time must not share a workspace.  Only the caller
+ * clears the error word.
  */
 size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
 
@@ -134,7 +136,9 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
  * E <= 4096, T*k <= 65536.  out may not alias x or residual.  With DQG_FMT_INT4 the
  * activations must satisfy |x| < 65504 (INT4 tiles multiply in fp16, accumulate in fp32;
- * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).
+ * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below), and on the
+ * multi-launch path (T > 8, or DQG_PATH_NO_FUSED) h = SiLU(g) * u enters the down
+ * projection as fp16, so |h| must stay below 65504 too (larger values become inf).
  */
 int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int32_t* ids,
                 const float* weights, const uint8_t* w_gate_up, const uint16_t* s_gate_up,
@@ -250,7 +254,9 @@ size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
  * across workgroups: pass a workspace of at least that many bytes, zero-filled before its
  * first use; every completed call leaves it zero-filled again, and one workspace serves
  * calls with any T up to the T it was sized for.  Its first int32 is an error word (bit 1:
- * a wait between workgroups gave up).  With a NULL workspace the call runs without the K
+ * a wait between workgroups gave up; the output is then not valid and a late producer may
+ * leave a partial behind: zero-fill the workspace again before reusing it).  With a NULL
+ * workspace the call runs without the K
  * split (correct, fewer workgroups).  Deterministic.  Calls that may run at the same time
  * must not share a workspace.
  */

@@ -155,3 +155,37 @@ def gemv_exact(x_bits, packed, scales, group: int, fmt: str = "int4"):
         x = [bf16_fraction(v) for v in xr]
         out.append([float(sum(x[k] * W[k][n] for k in range(K))) for n in range(N)])
     return out
+
+
+def bf16_rne_bits(v: float) -> int:
+    """Round a float to the nearest bf16 (ties to even), exactly via Fractions, and return
+    its 16-bit pattern.  Normal and subnormal ranges; no overflow handling (tiny tests)."""
+    q = Fraction(v)
+    if q == 0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                      # now 2^e <= a < 2^(e+1)
+    e = max(e, -126)                # subnormals share the smallest normal's step
+    step = Fraction(2) ** (e - 7)   # 7 stored mantissa bits
+    m = round(a / step)             # Fraction.__round__: nearest, ties to even
+    r = m * step
+    f = struct.unpack("<I", struct.pack("<f", float(r)))[0]   # r is exactly an fp32 value
+    assert f & 0xFFFF == 0
+    return sign | (f >> 16)
+
+
+def moe_stack_exact(x_bits, layers, k: int, group: int, fmt: str):
+    """The chained stack x_{l+1} = bf16(x_l + MoE_l(x_l)) through moe_exact, with the exact
+    bf16 rounding above between layers.  ``layers``: objects with logits, w_gu, s_gu, w_d,
+    s_d.  Returns (bits of the last layer's input, float64 output of the last layer)."""
+    x = [[int(v) for v in row] for row in x_bits]
+    out, last_in = None, None
+    for L in layers:
+        out, _, _ = moe_exact(x, L.logits, k, L.w_gu, L.s_gu, L.w_d, L.s_d, group, fmt,
+                              residual_bits=x)
+        last_in = x
+        x = [[bf16_rne_bits(v) for v in row] for row in out]
+    return last_in, out

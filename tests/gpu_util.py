@@ -66,7 +66,7 @@ def upload_layer(L, experts=None):
 
 
 def check_chain(gpu_bits: np.ndarray, oracle: np.ndarray, n_layers: int, rel: float = 1e-2,
-                what: str = ""):
+                what: str = "", elementwise: bool = True):
     """Tolerance for an L-layer residual chain x_{l+1} = bf16(x_l + MoE_l(x_l)) run
     independently on both sides.  Each side rounds every layer's output to bf16, and one
     rounding decision that falls differently (values within fp32 noise of a bf16
@@ -81,8 +81,37 @@ def check_chain(gpu_bits: np.ndarray, oracle: np.ndarray, n_layers: int, rel: fl
     rms_err = float(np.sqrt(np.mean(np.square(err))))
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     assert rms_err <= rel * rms, f"{what}: rms error {rms_err!r} > {rel} * rms {rms!r}"
+    if not elementwise:
+        return rms_err / rms
     bound = rel * rms + n_layers * ulp_bf16(np.maximum(np.abs(o), np.abs(g)))
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond {n_layers} ulps + "
                            f"{rel} * rms; worst {err.max()!r}")
     return rms_err / rms
+
+
+GUARD = 4096      # canary bytes on each side of a guarded buffer (keeps 256-byte alignment)
+CANARY = 0xA5
+
+
+def guarded(shape, dtype, zero: bool = False):
+    """A device buffer of ``shape``/``dtype`` inside canary bands of GUARD bytes on each
+    side.  Returns ``(view, check)``; ``check()`` asserts that no kernel wrote outside the
+    view.  ``zero`` zero-fills the view (workspaces)."""
+    n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    base = torch.full((GUARD + n + GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+    view = base[GUARD:GUARD + n].view(dtype).view(shape)
+    if zero:
+        view.zero_()
+
+    def check():
+        torch.cuda.synchronize()
+        lo, hi = base[:GUARD], base[GUARD + n:]
+        assert bool((lo == CANARY).all()) and bool((hi == CANARY).all()), \
+            "a kernel wrote outside its buffer (canary band changed)"
+    return view, check
+
+
+def guarded_workspace(nbytes: int):
+    """A zero-filled workspace of nbytes (uint8) inside canary bands."""
+    return guarded((nbytes,), torch.uint8, zero=True)

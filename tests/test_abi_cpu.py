@@ -220,3 +220,15 @@ def test_noalloc_gemv_host_checks():
     assert f(MIS, 1, 5120, 8192, A, A, 128, A, None, None) == B.DQG_ERR_MISALIGNED
     assert f(A, 1, 5120, 8192, A, A, 128, A, A + 2, None) == B.DQG_ERR_MISALIGNED
     assert f(A, 16, 5120, 65536, A, A, 128, A, None, None) == B.DQG_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("H,I,E,k", [(2048, 768, 128, 8), (2048, 512, 512, 10), (256, 128, 8, 2)])
+def test_moe_workspace_size_is_monotonic_in_T(H, I, E, k):
+    """The workspace layout is chosen as the largest token capacity whose size fits, so the
+    size must never shrink as T grows (otherwise one workspace would get different layouts
+    for different T and leave data where another layout expects zeros)."""
+    prev = 0
+    for T in list(range(1, 65)) + list(range(65, 65536 // k + 1, 37)) + [65536 // k]:
+        n = B.moe_fp4_ffn_workspace_bytes(T, H, I, E, k)
+        assert n >= prev, (T, n, prev)
+        prev = n

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import bits16, check_bf16, check_chain, dev, upload_layer
+from gpu_util import bits16, check_bf16, check_chain, dev, guarded, guarded_workspace, upload_layer
 from oracle import moe_oracle as O
 from workloads import synth as S
 
@@ -54,8 +54,22 @@ CASES = [
 
 @pytest.mark.parametrize("name,cfg,seed", CASES, ids=[f"{c[0]}-s{c[2]}" for c in CASES])
 def test_moe_layer_parity(name, cfg, seed):
+    """Every config: ids bit-exact, weights to fp32 rounding, outputs within the method's
+    tolerance; the output and workspace sit inside canary bands that must stay untouched."""
+    B = _b()
     L, D = _layer(cfg, seed)
-    out, ids, w = _run_layer(cfg, L, D)
+    out_t, chk_out = guarded((cfg.T, cfg.H), torch.bfloat16)
+    ws, chk_ws = guarded_workspace(B.moe_fp4_ffn_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E,
+                                                                  cfg.k))
+    ids_t = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w_t = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    B.moe_fp4_layer(dev(L.x), dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
+                    cfg.group, cfg.fmt, out=out_t, ids_out=ids_t, weights_out=w_t, workspace=ws)
+    torch.cuda.synchronize()
+    chk_out()
+    chk_ws()
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    out, ids, w = bits16(out_t), ids_t.cpu().numpy(), w_t.cpu().numpy()
     want, oids, ow = _oracle_layer(cfg, L)
     assert np.array_equal(ids, oids), "expert selection must match bit-exactly"
     np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
@@ -168,6 +182,7 @@ def test_moe_deterministic_and_layer_equals_ffn(T):
         check_bf16(bits16(o3), _oracle_layer(cfg, L)[0], what="ffn T=1")
 
 
+@pytest.mark.error_word_expected
 def test_moe_invalid_ids_contribute_zero_and_set_error_word():
     cfg = S.TINY.with_T(3)
     L, D = _layer(cfg, seed=7)
@@ -254,34 +269,45 @@ def test_graph_replay_with_changing_inputs():
         check_bf16(got, _oracle_layer(cfg, L2)[0], what=f"replay {rep}")
 
 
-def _stack(T, n_layers):
+@pytest.mark.parametrize("T", [1, 8])
+def test_w512_stack_teacher_forced_48_layers(T):
+    """48 independently seeded E=512 layers chained as x_{l+1} = bf16(x_l + MoE_l(x_l)).
+    Every layer is checked element by element against the oracle on the GPU's own input of
+    that layer (read back from the device), at the method's tolerance; separately, the
+    oracle's own 48-layer chain is run alongside and the GPU's final state is compared with
+    it in rms norm only, since one bf16 rounding that falls differently moves later layers
+    and no per-element bound composes over 48 roundings."""
+    B = _b()
     cfg = S.replace(S.W512, T=T)
-    layers, devs = [], []
+    n_layers = 48
+    ws = B.moe_workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
+    xin = None
+    x_oracle = None
+    worst = 0.0
     for l in range(n_layers):
         lg = S.moe_layer_logits(cfg, 0, l)
         ids, _ = O.topk_route(lg, cfg.k)
         L = S.make_moe_layer(cfg, 0, l, with_x=(l == 0), experts=np.unique(ids))
-        layers.append(L)
-        devs.append(upload_layer(L, np.unique(ids)))
-    return cfg, layers, devs
-
-
-@pytest.mark.parametrize("T,n_layers", [(1, 48), (8, 12)])
-def test_w512_stack_chained_residual(T, n_layers):
-    """48 independently seeded E=512 layers chained as x_{l+1} = bf16(x_l + MoE_l(x_l))."""
-    B = _b()
-    cfg, layers, devs = _stack(T, n_layers)
-    ws = B.moe_workspace(T, cfg.H, cfg.I, cfg.E, cfg.k, "cuda")
-    bufs = [dev(layers[0].x).view(torch.bfloat16),
-            torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")]
-    for l, (L, D) in enumerate(zip(layers, devs)):
-        xin, xout = bufs[l % 2], bufs[(l + 1) % 2]
+        D = upload_layer(L, np.unique(ids))
+        if l == 0:
+            xin = dev(L.x).view(torch.bfloat16)
+            x_oracle = L.x
+        xout = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
         B.moe_fp4_layer(xin, dev(L.logits), cfg.k, D["w_gu"], D["s_gu"], D["w_d"], D["s_d"],
                         cfg.group, cfg.fmt, residual=xin, out=xout, workspace=ws)
-    torch.cuda.synchronize()
-    got = bits16(bufs[n_layers % 2])
-    _, want = O.moe_stack(layers[0].x, layers, cfg.k, cfg.group, cfg.fmt)
-    check_chain(got, want, n_layers, what=f"stack T={T}")
+        torch.cuda.synchronize()
+        x_bits = bits16(xin)
+        want, _, _ = O.moe_layer(x_bits, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d,
+                                 cfg.group, cfg.fmt, residual_bits=x_bits)
+        worst = max(worst, check_bf16(bits16(xout), want, what=f"stack T={T} layer {l}"))
+        chain, _, _ = O.moe_layer(x_oracle, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d,
+                                  cfg.group, cfg.fmt, residual_bits=x_oracle)
+        x_oracle = O.bf16_round_to_bits(chain)
+        xin = xout
+        del D, L
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    # end to end: the norm bound only (the per-element bar is the per-layer check above)
+    check_chain(bits16(xin), chain, n_layers, what=f"stack T={T} end to end", elementwise=False)
 
 
 # ---- multi-launch expert kernels: vector-ALU and matrix-core bodies -------------------------

@@ -569,6 +569,35 @@ def test_stack_chains_through_bf16_residual():
     assert not np.array_equal(last_in, x0)
 
 
+@pytest.mark.parametrize("fmt", [O.FMT_FP4, O.FMT_INT4])
+def test_stack_matches_exact_rational_chain(fmt):
+    """moe_stack against an exact-rational 3-layer chain: brute-force layers (Fraction gate,
+    up and down sums, float64 SiLU and combine) joined by an exact bf16 round-to-nearest-even
+    written from the format's definition.  The bf16 inputs of every layer must agree
+    bit for bit, the last output to float64 rounding."""
+    cfg = S.replace(S.W512, E=4, H=64, I=32, k=2, T=2, layers=3, fmt=fmt)
+    layers = [S.make_moe_layer(cfg, seed=0, layer=l) for l in range(3)]
+    name = "fp4" if fmt == O.FMT_FP4 else "int4"
+    x0 = layers[0].x
+    b_in, b_out = BF.moe_stack_exact(x0.tolist(), layers, cfg.k, cfg.group, name)
+    o_in, o_out = O.moe_stack(x0, layers, cfg.k, cfg.group, fmt)
+    assert np.array_equal(np.asarray(b_in, np.uint16), o_in)
+    assert not np.array_equal(o_in, x0)                      # the chain moved
+    np.testing.assert_allclose(o_out, np.asarray(b_out), rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_rne_bits_against_hand_values():
+    """The brute-force rounding on values whose bf16 neighbours are known by hand."""
+    assert BF.bf16_rne_bits(1.0) == 0x3F80
+    assert BF.bf16_rne_bits(1.0 + 2 ** -8) == 0x3F80           # tie -> even (mantissa 0)
+    assert BF.bf16_rne_bits(1.0 + 3 * 2 ** -8) == 0x3F82       # tie -> even (mantissa 2)
+    assert BF.bf16_rne_bits(1.0 + 2 ** -8 + 2 ** -20) == 0x3F81
+    assert BF.bf16_rne_bits(-2.0) == 0xC000
+    assert BF.bf16_rne_bits(255.5) == 0x4380                   # 255.5 -> 256 (carry)
+    assert BF.bf16_rne_bits(-0.0) == 0x8000
+    assert BF.bf16_rne_bits(2.0 ** -130) == 0x0008             # subnormal: 2^-130 = 8 * 2^-133
+
+
 # --------------------------------------------------------------------------------------
 # dense GEMV
 # --------------------------------------------------------------------------------------
