@@ -200,28 +200,105 @@ def build_gemv_workload(w, seed: int = 0, device="cuda"):
     return x, sets
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The float64 oracle on the same layer shape, single-threaded BLAS, for a bounded
-    number of layers (about `budget_s` seconds).  Returns µs per layer."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_layer(L, k):
+    """Host copy of one timed layer's logits and of its routed experts' slabs only (dicts
+    keyed by expert id: the oracle looks experts up by id)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    import torch
     from oracle import moe_oracle as O
-    from workloads import synth as S
-    cfg = S.Q30
-    layers, t_total, n = 0, 0.0, 0
+    lg = L["logits"].cpu().numpy()
+    ids, _ = O.topk_route(lg, k)
+    sl = {}
+    for name in ("w_gu", "s_gu", "w_d", "s_d"):
+        t = L[name] if L[name].dtype == torch.uint8 else L[name].view(torch.int16)
+        sl[name] = {int(e): t[int(e)].cpu().numpy() for e in np.unique(ids)}
+        if L[name].dtype != torch.uint8:
+            sl[name] = {e: a.view(np.uint16) for e, a in sl[name].items()}
+    return lg, sl
+
+
+def oracle_layer_out(x_bits, lg, sl, k, group, fmt, residual_bits=None):
+    from oracle import moe_oracle as O
+    out, _, _ = O.moe_layer(x_bits, lg, k, sl["w_gu"], sl["s_gu"], sl["w_d"], sl["s_d"], group,
+                            fmt, residual_bits=residual_bits)
+    return out
+
+
+def within_method_tolerance(gpu_bits, want):
+    """|gpu - oracle| <= 1e-2 rms(oracle) + 1 bf16 ulp of the oracle value, per element."""
+    import numpy as np
+    g = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rms = float(np.sqrt(np.mean(np.square(want))))
+    a = np.abs(want)
+    ulp = np.where(a > 0, 2.0 ** (np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -126) - 7),
+                   2.0 ** -133)
+    err = np.abs(g - want)
+    return bool(np.all(err <= 1e-2 * rms + ulp)), float(np.max(err / (1e-2 * rms + ulp)))
+
+
+def cpu_baseline(timed, x_bits, k, group, fmt, budget_s: float = 10.0):
+    """The float64 oracle on layers the GPU timed (their routed experts copied to the
+    host), after checking the GPU's outputs of those layers against it.  Two legs: one
+    thread with one BLAS thread (median µs per layer), then one worker thread per core of
+    this process's CPU set (at most 16), each running whole layers with one BLAS thread
+    (µs per layer = wall time / layers).  numpy releases the GIL inside its array loops, so
+    the threads run side by side; threads rather than processes keep every CPU worker
+    inside this one process.  `timed` lists (logits, slabs, gpu_out_bits) per layer."""
+    import concurrent.futures as cf
+    import statistics
+    from threadpoolctl import threadpool_limits
+    worst = 0.0
+    for lg, sl, gpu_bits in timed[:4]:  # parity first
+        ok, ratio = within_method_tolerance(gpu_bits, oracle_layer_out(x_bits, lg, sl, k, group,
+                                                                          fmt))
+        if not ok:
+            raise SystemExit(f"cpu_baseline: GPU output of a timed layer is outside the "
+                             f"tolerance (worst ratio {ratio:.3f})")
+        worst = max(worst, ratio)
+    times, t_one = [], 0.0
     with threadpool_limits(limits=1):
-        seed = 0
-        while t_total < budget_s and n < 512:
-            ids_needed = O.topk_route(S.moe_layer_logits(cfg, seed), cfg.k)[0]
-            L = S.make_moe_layer(cfg, seed, experts=np.unique(ids_needed))
+        while t_one < budget_s / 2 and len(times) < 4 * len(timed):
+            lg, sl, _ = timed[len(times) % len(timed)]
             t0 = time.perf_counter()
-            O.moe_layer(L.x, L.logits, cfg.k, L.w_gu, L.s_gu, L.w_d, L.s_d, cfg.group, cfg.fmt)
-            t_total += time.perf_counter() - t0
-            n += 1
-            seed += 1
-    return {"value": t_total / n * 1e6, "unit": "us/layer", "cores": 1, "kind": "oracle",
-            "sample": f"{n} Q30 T=1 layers (route + 8 experts + combine), float64 numpy, "
-                      f"one BLAS thread, {t_total:.1f} s total"}
+            oracle_layer_out(x_bits, lg, sl, k, group, fmt)
+            dt = time.perf_counter() - t0
+            times.append(dt)
+            t_one += dt
+    one_us = statistics.median(times) * 1e6
+    ncpu = min(len(os.sched_getaffinity(0)), 16)
+    # all cores: as many layers as one core did in its leg, times the core count, so that
+    # the leg also takes about budget_s / 2 at perfect scaling
+
+    def one_layer(i):
+        lg, sl, _ = timed[i % len(timed)]
+        oracle_layer_out(x_bits, lg, sl, k, group, fmt)
+
+    n_all = max(ncpu, int(len(times) * ncpu))
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(max_workers=ncpu) as ex:
+        list(ex.map(one_layer, range(ncpu)))            # threads started
+        t0 = time.perf_counter()
+        list(ex.map(one_layer, range(n_all)))
+        t_all = time.perf_counter() - t0
+    return {"value": round(t_all / n_all * 1e6, 1), "unit": "us/layer", "cores": ncpu,
+            "kind": "oracle",
+            "sample": f"{n_all} GPU-timed layers (route + routed experts + combine, float64 "
+                      f"numpy) on {ncpu} worker threads, {t_all:.1f} s wall; "
+                      f"value = wall time / layers",
+            "single_thread": {"value": round(one_us, 1), "unit": "us/layer", "cores": 1,
+                              "sample": f"median of {len(times)} layers, {t_one:.1f} s"},
+            "cpu_model": cpu_model(),
+            "parity_checked": f"GPU outputs of {min(4, len(timed))} timed layers within the "
+                              f"tolerance (worst ratio {worst:.3f}) before timing"}
 
 
 def read_traffic(kernel: str, workload: str):
@@ -240,41 +317,83 @@ def read_traffic(kernel: str, workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+class GraphTimer:
+    """fn() captured once into a graph on `stream` (after one eager warm-up call on that
+    stream); timed replays with events recorded on `stream`."""
+
+    def __init__(self, fn, stream):
+        import torch
+        # every input was written on the default stream: finish that work first, or the
+        # caching allocator's reuse of freed temporaries can overlap buffers used here
+        torch.cuda.synchronize()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            fn()
+        stream.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=stream):
+            fn()
+        self.stream = stream
+
+    def replay(self, n):
+        import torch
+        with torch.cuda.stream(self.stream):
+            for _ in range(n):
+                self.graph.replay()
+
+    def timed(self, steps, warmup):
+        """warmup untimed replays, then `steps` replays between two events; ms per replay."""
+        import torch
+        self.replay(warmup)
+        self.stream.synchronize()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        self.replay(steps)
+        e1.record(self.stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def rounds(self, n_rounds=3, samples=30):
+        """n_rounds rounds of `samples` replays, each between its own pair of events:
+        per round the median and the min-max (ms per replay)."""
+        import statistics
+        import torch
+        out = []
+        for _ in range(n_rounds):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+            with torch.cuda.stream(self.stream):
+                ev[0].record(self.stream)
+                for i in range(samples):
+                    self.graph.replay()
+                    ev[i + 1].record(self.stream)
+            ev[-1].synchronize()
+            t = [ev[i].elapsed_time(ev[i + 1]) for i in range(samples)]
+            out.append({"median": statistics.median(t), "min": min(t), "max": max(t)})
+        return out
+
+
 def time_graph(fn, stream, steps, warmup):
-    """Capture fn() once into a graph on `stream`, replay `warmup` times, then time `steps`
-    replays with events recorded on `stream`.  Returns ms per replay."""
-    import torch
-    # every input was written on the default stream: finish that work first, or the
-    # caching allocator's reuse of freed temporaries can overlap buffers used here
-    torch.cuda.synchronize()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
-        fn()  # eager warm-up on the capture stream
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        fn()
-    with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            graph.replay()
-    stream.synchronize()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(steps):
-            graph.replay()
-        e1.record(stream)
-    e1.synchronize()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    """ms per replay of fn() captured into a graph (see GraphTimer)."""
+    return GraphTimer(fn, stream).timed(steps, warmup)
 
 
-def calibration(dev, stream):
-    """Context recorded with every run: a 1 GiB device copy (read + write GB/s) and the
+def calibration(dev, stream, B):
+    """Context recorded with every run: the achievable read bandwidth (one streaming read of
+    a 2 GiB buffer per replay, 10 replays), a 1 GiB device copy (read + write GB/s) and the
     per-launch floor of a graph of 256 one-element kernels."""
     import torch
+    rb = 2 << 30
+    rbuf = torch.empty(rb, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    gt = GraphTimer(lambda: B.stream_read(rbuf, sink), stream)
+    ms_read = gt.timed(10, 3)
+    read_rounds = gt.rounds(3, 10)
+    del gt, rbuf
+    torch.cuda.empty_cache()
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
@@ -288,7 +407,10 @@ def calibration(dev, stream):
     ms_tiny = time_graph(tiny, stream, 10, 3)
     del src, dst
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
+    return {"achievable_read_GBps": round(rb / (ms_read * 1e-3) / 1e9, 1),
+            "read_rounds_GBps": [round(rb / (r["median"] * 1e-3) / 1e9, 1) for r in read_rounds],
+            "read_bytes": rb,
+            "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1),
             "graph_launch_floor_us": round(ms_tiny * 1000.0 / 256, 3)}
 
 
@@ -299,6 +421,7 @@ def distinct_experts(logits, k):
 
 
 def bench_moe(w, args, dev, stream, B):
+    import numpy as np
     import torch
     T, E, H, I, k, G = (w[s] for s in ("T", "E", "H", "I", "k", "group"))
     fmt = {FP4: B.FMT_FP4_E2M1, INT4: B.FMT_INT4, FP8: B.FMT_FP8_E4M3}[w["fmt"]]
@@ -313,31 +436,96 @@ def bench_moe(w, args, dev, stream, B):
     rws = B.router_logits_workspace(T, H, E, dev) if router else None
     torch.cuda.synchronize()
 
-    def call(l, L):
+    def call(l, L, out=None, workspace=None):
         xin = xs[l] if chain else x
+        out = xs[l + 1] if out is None else out
+        workspace = ws if workspace is None else workspace
         if router:
             B.moe_fp4_layer_from_hidden(xin, L["wr"], k, L["w_gu"], L["s_gu"], L["w_d"],
                                         L["s_d"], G, fmt, residual=xin if chain else None,
-                                        out=xs[l + 1], workspace=ws, flags=flags)
+                                        out=out, workspace=workspace, flags=flags)
             return
         if L["efmt"] is not None:
             B.moe_fp4_layer_mixed(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"],
                                   L["efmt"], G, codebooks=L["cb"], residual=xin if chain else None,
-                                  out=xs[l + 1], workspace=ws, flags=flags)
+                                  out=out, workspace=workspace, flags=flags)
             return
         B.moe_fp4_layer(xin, L["logits"], k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
-                        residual=xin if chain else None, out=xs[l + 1], workspace=ws,
+                        residual=xin if chain else None, out=out, workspace=workspace,
                         flags=flags)
 
     def one_pass():
         for l, L in enumerate(layers):
             call(l, L)
 
-    ms_per_step = time_graph(one_pass, stream, args.steps, args.warmup)
+    gt = GraphTimer(one_pass, stream)
+    ms_per_step = gt.timed(args.steps, args.warmup)
     n_layers = len(layers)
     us_per_layer = ms_per_step * 1000.0 / n_layers
+    rounds = gt.rounds(3, 30)
+
+    # validation of the timed run: no error bit in the workspace; the last replay's output
+    # of layer l0 equals an eager call's bit for bit; and it meets the method's tolerance
+    # against the oracle on that layer's host copy (the eager call reads the same inputs)
+    err_word = int(ws[:4].view(torch.int32).item())
+    if err_word != 0:
+        raise SystemExit(f"bench: workspace error word {err_word:#x} after the timed replays")
+    l0 = n_layers // 2
+    ws_v = B.moe_workspace(T, H, I, E, k, dev)
+    eager = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        call(l0, layers[l0], out=eager, workspace=ws_v)
+    stream.synchronize()
+    replay_bits = xs[l0 + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+    if not np.array_equal(replay_bits, eager.view(torch.int16).cpu().numpy().view(np.uint16)):
+        raise SystemExit("bench: a replayed layer's output differs from an eager call")
+    validation = {"error_word": 0, "replay_equals_eager_layer": l0}
+    plain = not router and layers[0]["efmt"] is None
+    timed_host = []
+    if plain:
+        xin_bits = (xs[l0] if chain else x).view(torch.int16).cpu().numpy().view(np.uint16)
+        lg, sl = host_layer(layers[l0], k)
+        ok, ratio = within_method_tolerance(
+            replay_bits, oracle_layer_out(xin_bits, lg, sl, k, G, w["fmt"],
+                                          residual_bits=xin_bits if chain else None))
+        if not ok:
+            raise SystemExit(f"bench: timed layer {l0} is outside the tolerance ({ratio:.3f})")
+        validation["oracle_worst_ratio_layer"] = round(ratio, 4)
+        if not chain and args.workload == DEFAULT_WORKLOAD and not args.no_cpu_baseline:
+            x_bits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+            for l in range(min(n_layers, 12)):
+                lg, sl = host_layer(layers[l], k)
+                timed_host.append((lg, sl, xs[l + 1].view(torch.int16).cpu().numpy()
+                                   .view(np.uint16)))
+            validation["cpu_x"] = x_bits
+    del ws_v
+
+    # warm figure (context, not HBM): one layer's weights called n_layers times in a graph
+    warm_us = None
+    if not chain and not args.graph_only:
+        def warm_pass():
+            for l in range(n_layers):
+                call(0, layers[0])
+        warm_us = GraphTimer(warm_pass, stream).timed(max(5, args.steps // 4), 3) * 1000.0 / n_layers
+
+    # context only: events right before and after each eager layer call (includes the
+    # host launch overhead that the graph replay hides)
+    eager_us = None
+    if not args.graph_only:
+        per = []
+        with torch.cuda.stream(stream):
+            for rep in range(3):
+                for l, L in enumerate(layers):
+                    a0 = torch.cuda.Event(enable_timing=True)
+                    a1 = torch.cuda.Event(enable_timing=True)
+                    a0.record(stream)
+                    call(l, L)
+                    a1.record(stream)
+                    per.append((a0, a1))
+        stream.synchronize()
+        eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
     separate_us = None
-    if router:
+    if router and not args.graph_only:
         # context: the same layers as two calls, the router call then the logits-taking layer
         def two_calls():
             for l, L in enumerate(layers):
@@ -345,21 +533,6 @@ def bench_moe(w, args, dev, stream, B):
                 B.moe_fp4_layer(x, lbuf, k, L["w_gu"], L["s_gu"], L["w_d"], L["s_d"], G, fmt,
                                 out=xs[l + 1], workspace=ws, flags=flags)
         separate_us = time_graph(two_calls, stream, args.steps, args.warmup) * 1000.0 / n_layers
-
-    # context only: events right before and after each eager layer call (includes the
-    # host launch overhead that the graph replay hides)
-    per = []
-    with torch.cuda.stream(stream):
-        for rep in range(3):
-            for l, L in enumerate(layers):
-                a0 = torch.cuda.Event(enable_timing=True)
-                a1 = torch.cuda.Event(enable_timing=True)
-                a0.record(stream)
-                call(l, L)
-                a1.record(stream)
-                per.append((a0, a1))
-    stream.synchronize()
-    eager_us = sorted(a0.elapsed_time(a1) * 1000.0 for a0, a1 in per)[len(per) // 2]
 
     per_expert = expert_bytes(H, I, G, 1 if w["fmt"] == FP8 else 2)
     lgs = [L["logits"] if not router else x.float() @ L["wr"].float() for L in layers]
@@ -401,11 +574,17 @@ def bench_moe(w, args, dev, stream, B):
         "avg_launch_us": round(us_per_layer, 3),
         "timing": "events on the replay stream around the K timed graph replays, divided "
                   "by the layer calls they contain (steps x layers)",
-        "eager_call_us_median": round(eager_us, 3),
+        "rounds_us_per_layer": [{key: round(r[key] * 1000.0 / n_layers, 3) for key in r}
+                                for r in rounds],
     }
+    if eager_us is not None:
+        roofline["eager_call_us_median"] = round(eager_us, 3)
+    if warm_us is not None:
+        roofline["warm_us_per_layer"] = round(warm_us, 3)
     if router:
         roofline["router_in_launch"] = fused and E <= 128 and E % 8 == 0 and T <= 4
-        roofline["router_call_then_layer_us"] = round(separate_us, 3)
+        if separate_us is not None:
+            roofline["router_call_then_layer_us"] = round(separate_us, 3)
     config = {"workload": args.workload, "T": T, "E": E, "H": H, "I": I, "k": k,
               "format": {FP4: "fp4_e2m1", INT4: "int4", FP8: "fp8_e4m3"}[w["fmt"]], "group": G,
               "layers_per_step": n_layers, "chained": chain, "path": args.path,
@@ -415,11 +594,17 @@ def bench_moe(w, args, dev, stream, B):
         config["int2_experts_share"] = w.get("int2_frac", 0.0)
         config["fexc_experts_share"] = w.get("fexc_frac", 0.0)
         config["two_bit_active_experts_per_layer_mean"] = round(n_int2, 2)
+    cpu = None
+    if timed_host:
+        cpu = cpu_baseline(timed_host, validation.pop("cpu_x"), k, G, w["fmt"])
+    validation.pop("cpu_x", None)
     return dict(value=round(us_per_layer, 3), unit="us/layer", ms_per_step=ms_per_step,
-                achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
+                achieved_GBps=round(gbps, 1), roofline=roofline, config=config,
+                validation=validation, cpu_baseline=cpu)
 
 
 def bench_gemv(w, args, dev, stream, B):
+    import numpy as np
     import torch
     T, K, N, G = w["T"], w["K"], w["N"], w["group"]
     x, sets = build_gemv_workload(w, device=dev)
@@ -431,8 +616,31 @@ def bench_gemv(w, args, dev, stream, B):
         for S_, y in zip(sets, ys):
             B.packed_gemv_int4(x, S_["w"], S_["s"], G, y=y, workspace=ws)
 
-    ms_per_step = time_graph(one_pass, stream, args.steps, args.warmup)
+    gt = GraphTimer(one_pass, stream)
+    ms_per_step = gt.timed(args.steps, args.warmup)
+    rounds = gt.rounds(3, 30)
     us = ms_per_step * 1000.0 / len(sets)
+    # validation: error word clear, a replayed call equals an eager one, and the oracle bound
+    # on 512 sampled columns of that call
+    if ws is not None and int(ws[:4].view(torch.int32).item()) != 0:
+        raise SystemExit("bench: GEMV workspace error word set after the timed replays")
+    y_e = torch.empty_like(ys[0])
+    with torch.cuda.stream(stream):
+        B.packed_gemv_int4(x, sets[0]["w"], sets[0]["s"], G, y=y_e,
+                           workspace=B.gemv_workspace(T, K, N, G, dev))
+    stream.synchronize()
+    rb = ys[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    if not np.array_equal(rb, y_e.view(torch.int16).cpu().numpy().view(np.uint16)):
+        raise SystemExit("bench: a replayed GEMV differs from an eager call")
+    from oracle import moe_oracle as O
+    cols = np.unique(np.random.default_rng(0).choice(N, min(N, 512), replace=False))
+    want = O.packed_gemv(x.view(torch.int16).cpu().numpy().view(np.uint16),
+                         sets[0]["w"].cpu().numpy(),
+                         sets[0]["s"].view(torch.int16).cpu().numpy().view(np.uint16), G,
+                         cols=cols)
+    ok, ratio = within_method_tolerance(rb[:, cols], want)
+    if not ok:
+        raise SystemExit(f"bench: timed GEMV outside the tolerance ({ratio:.3f})")
     abytes = (K // 2) * N + (K // G) * N * 2
     gbps = abytes / (us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "gemv_ex_kernel", "achieved": round(gbps, 1),
@@ -440,11 +648,16 @@ def bench_gemv(w, args, dev, stream, B):
                 "traffic": read_traffic("gemv_ex_kernel", args.workload), "bytes_per_launch": abytes,
                 "avg_launch_us": round(us, 3),
                 "timing": "events around the K timed graph replays / GEMV calls (one "
-                          "launch per call)"}
+                          "launch per call)",
+                "rounds_us_per_call": [{key: round(r[key] * 1000.0 / len(sets), 3) for key in r}
+                                       for r in rounds]}
     config = {"workload": args.workload, "T": T, "K": K, "N": N, "group": G, "format": "int4",
               "weight_copies": len(sets)}
     return dict(value=round(us, 3), unit="us/call", ms_per_step=ms_per_step,
-                achieved_GBps=round(gbps, 1), roofline=roofline, config=config)
+                achieved_GBps=round(gbps, 1), roofline=roofline, config=config,
+                validation={"error_word": 0, "replay_equals_eager": True,
+                            "oracle_worst_ratio_512_cols": round(ratio, 4)},
+                cpu_baseline=None)
 
 
 def main():
@@ -455,6 +668,9 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="skip the context measurements that are not graph replays of the timed "
+                         "layers (eager per-call timing, the cache-warm figure): profiling runs")
     ap.add_argument("--path", choices=["auto", "unfused", "gemv", "mfma"], default="auto",
                     help="MoE kernel path: auto, or force the multi-launch path with its "
                          "automatic / vector-ALU-only / matrix-core-only expert tiles")
@@ -486,8 +702,12 @@ def main():
     w = WORKLOADS[args.workload]
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream(dev))
-    cal = None if args.no_calibration else calibration(dev, stream)
+    cal = None if args.no_calibration else calibration(dev, stream, B)
     r = (bench_moe if w["kind"] == "moe" else bench_gemv)(w, args, dev, stream, B)
+    roof = r["roofline"]
+    if cal:
+        roof["achievable_read_GBps"] = cal["achievable_read_GBps"]
+        roof["frac_of_achievable"] = round(roof["achieved"] / cal["achievable_read_GBps"], 4)
     rec = {
         "metric": METRIC if args.workload == DEFAULT_WORKLOAD else
         f"{r['unit'].replace('us/', 'µs per ')} and achieved HBM GB/s vs peak ({args.workload})",
@@ -504,13 +724,14 @@ def main():
         "data": "synthetic (seeded device RNG; inputs resident in HBM)",
         "config": r["config"],
         "achieved_GBps": r["achieved_GBps"],
-        "roofline": r["roofline"],
+        "roofline": roof,
         "calibration": cal,
+        "validation": r["validation"],
         "device": torch.cuda.get_device_name(dev),
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
-        rec["cpu_baseline"] = cpu_baseline()
+    if r.get("cpu_baseline"):
+        rec["cpu_baseline"] = r["cpu_baseline"]
     print(json.dumps(rec), flush=True)
 
 

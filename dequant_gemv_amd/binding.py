@@ -55,6 +55,7 @@ SIGNATURES = {
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_gemv_int4_noalloc": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
+    "dqg_stream_read": (_I, [_P, _Z, _P, _P]),
 }
 
 
@@ -345,3 +346,11 @@ def packed_dequant_f32(w, s, group: int, fmt: int, out=None) -> torch.Tensor:
     _check("packed_dequant_f32", LIB.packed_dequant_f32(
         _ptr(w), _ptr(s), K, N, group, fmt, _ptr(out), _stream(w)))
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement aid: one streaming read of ``buf`` (uint8, contiguous, size a multiple of
+    16) on the current stream; ``sink`` is a one-element int32 device tensor."""
+    _need(buf, "buf", 1)
+    _need(sink, "sink", 4, (1,), buf.device)
+    _check("dqg_stream_read", LIB.dqg_stream_read(_ptr(buf), buf.numel(), _ptr(sink), _stream(buf)))

@@ -547,4 +547,11 @@ int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int gr
                                                                                      : DQG_ERR_HIP;
 }
 
+int dqg_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!p || !sink || bytes == 0) return DQG_ERR_INVALID_ARG;
+  if (bytes % 16 || bytes / 16 / 4096 >= (size_t)1 << 31) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(p) || ((uintptr_t)sink & 3u)) return DQG_ERR_MISALIGNED;
+  return dqg::launch_stream_read(p, bytes, sink, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+}
+
 }  // extern "C"

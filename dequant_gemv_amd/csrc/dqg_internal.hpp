@@ -106,6 +106,8 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st);
 int ex_max_split_gemv();
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st);
+// measurement aid: read `bytes` (a multiple of 16) from p once (see stream_read_kernel)
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t st);
 // router logits[T, E] = x W_r through partials [router_splits(H)][T][E] (see router_unit)
 int router_splits(int H);
 hipError_t launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, int E, float* part,

@@ -367,6 +367,44 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
 // =====================================================================================
 // host launchers
 // =====================================================================================
+// =====================================================================================
+// measurement aid: a plain streaming read (achievable HBM read bandwidth).  Each workgroup
+// reads one contiguous 64 KiB chunk with 16-byte non-temporal loads, 8 in flight per thread
+// (measured on MI355X: 6.1-6.2 TB/s over 2 GiB; grid-strided reads of the same bytes were
+// 5-10 % slower).  The loaded words are folded with xor and written to sink only when the
+// result equals `key`, so no load can be dropped.
+// =====================================================================================
+constexpr int SR_THREADS = 256;
+constexpr int SR_CHUNK16 = 4096;  // 16-byte words per workgroup (64 KiB)
+constexpr int SR_UNROLL = 8;
+__global__ void __launch_bounds__(SR_THREADS) stream_read_kernel(const uint4* __restrict__ p,
+                                                                 size_t n16, uint32_t key,
+                                                                 uint32_t* sink) {
+  const size_t b = (size_t)blockIdx.x * SR_CHUNK16;
+  uint32_t acc = 0;
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  for (int i = threadIdx.x; i < SR_CHUNK16; i += SR_THREADS * SR_UNROLL) {
+    u4 v[SR_UNROLL];
+#pragma unroll
+    for (int j = 0; j < SR_UNROLL; ++j) {
+      const size_t idx = b + i + (size_t)j * SR_THREADS;
+      v[j] = idx < n16 ? __builtin_nontemporal_load(reinterpret_cast<const u4*>(p + idx))
+                       : u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < SR_UNROLL; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  if (acc == key) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)((n16 + SR_CHUNK16 - 1) / SR_CHUNK16);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(SR_THREADS), 0, st,
+                     static_cast<const uint4*>(p), n16, 0x9E3779B9u, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* wts,
                        hipStream_t st) {
   const int grid = (T + 3) / 4;

@@ -290,6 +290,15 @@ int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8
 int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,
                        int format, float* out, hipStream_t stream);
 
+/*
+ * dqg_stream_read -- MEASUREMENT AID: read `bytes` (a multiple of 16) at p (16-byte aligned)
+ * once with 16-byte non-temporal loads, one contiguous 64 KiB chunk per workgroup, to
+ * calibrate the achievable HBM read bandwidth against which the compute kernels are judged.
+ * sink: a device uint32 that the kernel may write (the xor of the data is stored only when it
+ * equals a fixed key, so that no load can be optimized away).
+ */
+int dqg_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
