@@ -15,7 +15,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdqg.so")
+# DQG_LIBRARY names another build of the same library (the host-sanitizer build that the
+# CPU tests load); the in-tree libdqg.so otherwise
+LIB_PATH = os.environ.get("DQG_LIBRARY") or os.path.join(_HERE, "libdqg.so")
 
 DQG_OK = 0
 DQG_ERR_INVALID_ARG = -1

@@ -58,5 +58,48 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI layer (argument
+# checks, workspace layout, plan selection).  Only the host pass of dqg_api.cpp is
+# instrumented (every -fsanitize= goes through -Xarch_host); the kernel objects of the normal
+# build are linked in unchanged.  The result is loaded with the ASan runtime preloaded, on
+# the CPU only: it is a checking build, never the library the product loads.
+SAN_LIB = os.path.join(BUILD, "san", "libdqg.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+             "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libsan"]
+
+
+def asan_runtime() -> str:
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the clang ASan runtime was not found next to hipcc")
+    return path
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    san = os.path.dirname(SAN_LIB)
+    os.makedirs(san, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES
+            if s != "dqg_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    api_obj = os.path.join(san, "dqg_api.o")
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, "dqg_api.cpp"), "-o", api_obj]
+           + common_flags() + ["-g"] + SAN_FLAGS)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    cmd = ([hipcc(), "-shared", "-o", SAN_LIB] + objs + [api_obj, f"--offload-arch={ARCH}",
+                                                          "-fPIC"] + SAN_FLAGS)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}", file=sys.stderr)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    build_sanitized() if "--sanitize" in sys.argv[1:] else build()
