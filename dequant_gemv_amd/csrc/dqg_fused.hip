@@ -72,8 +72,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p) {
 // A gate_up unit covers 16 row-lanes x GUR byte rows; GUR = 8 for one token and 16 for
 // several, where there are T times more slots and fewer, larger units keep all of them
 // resident (measured at the 128-expert shape: T = 4 is 12 % faster with 16, T = 1 the same).
-constexpr int FX_D_ROWS = 8;                    // byte rows per lane, down unit
-constexpr int FX_DROWS = 32 * FX_D_ROWS;        // down byte rows per unit (32 row-lanes)
+// A down unit covers 32 row-lanes x DR byte rows: DR = 8 (256-row chunks) in general, DR = 4
+// (128-row chunks) for one token where that spreads the layer's bytes more evenly over the
+// compute units (fx_down_rows).
+constexpr int FX_DR_MAX = 8;
 constexpr int fx_krows(int gur) { return 16 * gur; }
 constexpr int fx_max_ks(int gur) { return 2048 / 2 / fx_krows(gur); }  // H <= 2048
 static inline int fx_gu_rows(int H, int T) { return (T > 1 && (H / 2) % fx_krows(16) == 0) ? 16 : 8; }
@@ -392,13 +394,14 @@ __device__ __forceinline__ float load_x_rows(const uint16_t* x, int r0, uint32_t
 // instruction cache that the weight stream has left cold, and code size is time there.
 // Returns false on timeout.
 constexpr int FX_GATHER = 16;
+template <int NG>
 __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n, float* v) {
   for (unsigned spins = 0; spins < FX_SPIN_LIMIT; ++spins) {
     bool ready = true;
 #pragma unroll
-    for (int i = 0; i < FX_GATHER; ++i) v[i] = ld_sc1(p, (size_t)(i < n ? i : n - 1) * stride);
+    for (int i = 0; i < NG; ++i) v[i] = ld_sc1(p, (size_t)(i < n ? i : n - 1) * stride);
 #pragma unroll
-    for (int i = 0; i < FX_GATHER; ++i) ready = ready && (__float_as_uint(v[i]) != 0u);
+    for (int i = 0; i < NG; ++i) ready = ready && (__float_as_uint(v[i]) != 0u);
     if (ready) return true;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -409,13 +412,17 @@ __device__ __forceinline__ bool gather_sc1(const float* p, size_t stride, int n,
 // codebooks or the logits output.  Without them (EXT false) those paths are compiled out:
 // the plain layer's code is then shorter and denser, which the cold instruction fetches on
 // its dependency chain repay (Q30 T = 1 12.3 -> 11.6 us, T = 4 24.7 -> 22.9 us).
-template <int FMT, int GUR, bool EXT>
+template <int FMT, int GUR, int DR, bool EXT>
 __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   constexpr int KB = fmt_kb(FMT);                  // K indices per stored byte
   constexpr int KROWS = fx_krows(GUR);             // gate_up byte rows per unit
   constexpr int MAX_KS = 2048 / KB / KROWS;        // gate_up K splits (H <= 2048)
-  constexpr int NH = KB * FX_DROWS;                // h values of a down unit
-  constexpr int NPL = KB * FX_D_ROWS;              // h values of a down lane
+  constexpr int DROWS = 32 * DR;                   // down byte rows per unit
+  constexpr int NH = KB * DROWS;                   // h values of a down unit
+  constexpr int NPL = KB * DR;                     // h values of a down lane
+  // the final units gather a token's chunk rows in rounds of FXG loads (128-row chunks: up
+  // to 33 chunks per token in one round)
+  constexpr int FXG = DR == 4 ? 32 : FX_GATHER;
   __shared__ int s_ids[32];
   __shared__ int s_key[32];
   __shared__ float s_w[32];
@@ -640,7 +647,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   const int mt = ub / NC, c = ub - mt * NC;
   const int rl = tid >> 3, ch = tid & 7;
   const int col0 = 128 * mt + 16 * ch;
-  const int R = c * FX_DROWS + FX_D_ROWS * rl;   // row in the concatenated slot list
+  const int R = c * DROWS + DR * rl;   // row in the concatenated slot list
   const int rows_per_slot = I / KB;
   const bool active = R < S * rows_per_slot;
   const int sl = active ? R / rows_per_slot : tok * k;  // slot of the row
@@ -662,7 +669,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     }
     __syncthreads();
   }
-  uint4 wvv[FX_D_ROWS];
+  uint4 wvv[DR];
   float sf[16];
   bool i2 = false;  // an INT2 or FE-XC expert of a mixed layer
   bool fx = false;  // FE-XC: codebook set `cset` (the chunk's first or second slot)
@@ -671,13 +678,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // I / 2 >= 256, which the host requires with codebooks), copied into LDS by the whole
   // workgroup once the weight loads are issued, so that they land during the h gather
   int stage_e[2] = {-1, -1};
-  const int sl_a = (c * FX_DROWS) / rows_per_slot;
+  const int sl_a = (c * DROWS) / rows_per_slot;
   if constexpr (FMT == FMT_FP4) {
     if (a.efmt != nullptr && a.cb != nullptr) {
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
         const int slz = sl_a + z;
-        if (slz < S && slz * rows_per_slot < (c + 1) * FX_DROWS) {
+        if (slz < S && slz * rows_per_slot < (c + 1) * DROWS) {
           const int ez = s_ids[slz - tok * k];
           if (s_fmt[ez] == FMT_FEXC) stage_e[z] = ez;
         }
@@ -697,7 +704,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     const uint8_t* wd = a.wd + (size_t)e * rows_per_slot * H;
     if (i2)
       load_rows(wd + (size_t)(r0 / 2) * H + col0, H,
-                reinterpret_cast<uint4(&)[FX_D_ROWS / 2]>(wvv), nt);
+                reinterpret_cast<uint4(&)[DR / 2]>(wvv), nt);
     else
       load_rows(wd + (size_t)r0 * H + col0, H, wvv, nt);
     scales16(a.sd + (size_t)e * (I / a.group) * H + (size_t)((KB * r0) / a.group) * H + col0,
@@ -773,7 +780,7 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
   if (active) {
-    float hf[2 * FX_D_ROWS];  // the lane's NPL h values
+    float hf[2 * DR];  // the lane's NPL h values
 #pragma unroll
     for (int i = 0; i < NPL / 4; ++i) {
       const float4 v = reinterpret_cast<const float4*>(hl)[(NPL / 4) * rl + i];
@@ -785,23 +792,23 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
     float corr = 0.0f;
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-      for (int i = 0; i < 2 * FX_D_ROWS; ++i) corr += hf[i];
+      for (int i = 0; i < 2 * DR; ++i) corr += hf[i];
       corr *= -8.0f;
     }
     float accb[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) accb[q] = 0.0f;
     if constexpr (FMT == FMT_FP8) {
-      rows_dot_f32_fp8<FX_D_ROWS>(wvv, reinterpret_cast<const float(&)[FX_D_ROWS]>(hf), accb);
+      rows_dot_f32_fp8<DR>(wvv, reinterpret_cast<const float(&)[DR]>(hf), accb);
     } else {
       if (fx)
-        rows_dot_f32_fexc<FX_D_ROWS>(reinterpret_cast<const uint4(&)[FX_D_ROWS / 2]>(wvv), hf,
+        rows_dot_f32_fexc<DR>(reinterpret_cast<const uint4(&)[DR / 2]>(wvv), hf,
                                      s_cb + 512 * cset, accb);
       else if (i2)
-        corr = rows_dot_f32_int2<FX_D_ROWS>(reinterpret_cast<const uint4(&)[FX_D_ROWS / 2]>(wvv),
+        corr = rows_dot_f32_int2<DR>(reinterpret_cast<const uint4(&)[DR / 2]>(wvv),
                                             hf, accb);
       else
-        rows_dot_f32<FMT, FX_D_ROWS>(wvv, hf, accb);
+        rows_dot_f32<FMT, DR>(wvv, hf, accb);
     }
     const float wj = s_w[j];
 #pragma unroll
@@ -822,12 +829,13 @@ __global__ void __launch_bounds__(FX_THREADS) fused_layer_kernel(FusedArgs a) {
   // the token's last chunk of the tile: gather its earlier chunks' rows (all in flight),
   // ascending c
   float y = 0.0f;
-  for (int c0 = 0; c0 < NCt - 1; c0 += FX_GATHER) {
-    const int n = min(FX_GATHER, NCt - 1 - c0);
-    float pv[FX_GATHER];
-    if (!gather_sc1(pbuf + (row0 + c_first + c0) * 128 + tid, 128, n, pv)) atomicOr(a.err, 2);
+  for (int c0 = 0; c0 < NCt - 1; c0 += FXG) {
+    const int n = min(FXG, NCt - 1 - c0);
+    float pv[FXG];
+    if (!gather_sc1<FXG>(pbuf + (row0 + c_first + c0) * 128 + tid, 128, n, pv))
+      atomicOr(a.err, 2);
 #pragma unroll
-    for (int i = 0; i < FX_GATHER; ++i)
+    for (int i = 0; i < FXG; ++i)
       if (i < n) y += pv[i];
   }
   y += mine;
@@ -854,15 +862,49 @@ bool fused_supported(int H, int I, int k) {
 // T > 1: a token's down rows must fill whole chunks, so that no chunk spans two tokens
 bool fused_supported_t(int T, int H, int I, int k, int fmt) {
   return fused_supported(H, I, k) && T >= 1 && T <= FX_MAX_T &&
-         (T == 1 || (k * (I / fmt_kb(fmt))) % FX_DROWS == 0);
+         (T == 1 || (k * (I / fmt_kb(fmt))) % (32 * FX_DR_MAX) == 0);
 }
 
 // gate_up rows per lane: FP8 always 16 (one byte per K index: H / 256 splits at most 8)
 static inline int fx_gur(int H, int T, int fmt) { return fmt == FMT_FP8 ? 16 : fx_gu_rows(H, T); }
 
+// Weight bytes of the most loaded compute unit when the gate_up units (n_a of ga bytes) come
+// first and the down units (n_b of db bytes) after them.  Measured on MI355X: the dispatcher
+// puts workgroup b on XCD b mod 8 and hands each XCD's workgroups to its 32 compute units in
+// turn (local index i on unit i mod 32); with every unit's loads in flight at once, a compute
+// unit receives its bytes at a roughly fixed share of the bandwidth, so the most loaded one
+// ends the weight stream.
+static long long fx_max_cu_bytes(int n_a, long long ga, int n_b, long long db) {
+  constexpr int XCD = 8, CU = 32;
+  long long load[XCD * CU] = {};
+  for (int b = 0; b < n_a + n_b; ++b)
+    load[(b % XCD) * CU + (b / XCD) % CU] += b < n_a ? ga : db;
+  long long m = 0;
+  for (long long v : load) m = v > m ? v : m;
+  return m;
+}
+
+// Down byte rows per lane (DR): 8, or 4 for one token when the smaller down units spread the
+// layer's bytes more evenly (the 128-expert shape: 384 gate_up units + 192 down units put
+// three 36 KB units on a quarter of the compute units; 384 + 384 smaller ones put at most
+// 90 KB on any).  Router units are left out, so that the choice, and with it the workspace
+// layout, does not depend on them.
+static int fx_down_rows(int H, int I, int k, int T, int fmt) {
+  if (T != 1) return FX_DR_MAX;
+  const int kb = fmt_kb(fmt);
+  const long long rows = (long long)k * (I / kb);                  // down byte rows
+  const int ks = H / kb / fx_krows(fx_gur(H, T, fmt));
+  const int n_a = k * (I / 128) * ks;
+  const long long ga = (long long)fx_krows(fx_gur(H, T, fmt)) * 256;
+  const int n_mt = H / 128;
+  const int n8 = n_mt * (int)((rows + 255) / 256), n4 = n_mt * (int)((rows + 127) / 128);
+  return fx_max_cu_bytes(n_a, ga, n4, 128 * 128) < fx_max_cu_bytes(n_a, ga, n8, 256 * 128)
+             ? 4 : FX_DR_MAX;
+}
+
 // Sizes of one call's exchange buffers (T tokens, format class of fmt)
 struct FxSizes {
-  int ks, n_chunks, n_mt;
+  int ks, n_chunks, n_mt, dr;
   size_t gpart, ypart, rpart, total;
 };
 static FxSizes fx_sizes(int H, int I, int E, int k, int T, int fmt) {
@@ -870,7 +912,8 @@ static FxSizes fx_sizes(int H, int I, int E, int k, int T, int fmt) {
   const int kb = fmt_kb(fmt);
   z.ks = H / kb / fx_krows(fx_gur(H, T, fmt));
   z.n_mt = H / 128;
-  z.n_chunks = (T * k * (I / kb) + FX_DROWS - 1) / FX_DROWS;
+  z.dr = fx_down_rows(H, I, k, T, fmt);
+  z.n_chunks = (T * k * (I / kb) + 32 * z.dr - 1) / (32 * z.dr);
   z.gpart = 2 * (size_t)T * k * (I / 128) * z.ks * 256 * 4;   // gate/up partial rows
   z.ypart = 2 * (size_t)z.n_mt * z.n_chunks * 128 * 4;        // output partial rows
   z.rpart = fused_router_supported(E, T) ? 2 * (size_t)router_splits(H) * T * E * 4 : 0;
@@ -905,6 +948,7 @@ void fused_layout(FusedArgs& f, void* ws, int H, int I, int E, int k, int T, boo
   f.ks = z.ks;
   f.n_mt = z.n_mt;
   f.n_chunks = z.n_chunks;
+  f.dr = z.dr;
   f.chunks_per_token = f.n_chunks / T;
   f.n_a = T * k * (I / 128) * f.ks;
   f.n_b = f.n_mt * f.n_chunks;
@@ -921,18 +965,28 @@ static void launch_fused_ext(const FusedArgs& f, hipStream_t st) {
   const int grid = f.n_r + f.n_a + f.n_b;
   const bool big = fx_gur(f.H, f.T, f.fmt) == 16;
   const dim3 g(grid), b(FX_THREADS);
+  // 128-row down chunks (dr 4) are only chosen for one token, where gate_up has 8 rows per
+  // lane (16 for FP8)
+  const bool d4 = f.dr == 4;
   if (f.fmt == FMT_FP8) {
-    hipLaunchKernelGGL((fused_layer_kernel<FMT_FP8, 16, EXT>), g, b, 0, st, f);
+    if (d4)
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP8, 16, 4, EXT>), g, b, 0, st, f);
+    else
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP8, 16, 8, EXT>), g, b, 0, st, f);
   } else if (f.fmt == FMT_FP4) {
     if (big)
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 16, EXT>), g, b, 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 16, 8, EXT>), g, b, 0, st, f);
+    else if (d4)
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8, 4, EXT>), g, b, 0, st, f);
     else
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8, EXT>), g, b, 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_FP4, 8, 8, EXT>), g, b, 0, st, f);
   } else {
     if (big)
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 16, EXT>), g, b, 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 16, 8, EXT>), g, b, 0, st, f);
+    else if (d4)
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8, 4, EXT>), g, b, 0, st, f);
     else
-      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8, EXT>), g, b, 0, st, f);
+      hipLaunchKernelGGL((fused_layer_kernel<FMT_INT4, 8, 8, EXT>), g, b, 0, st, f);
   }
 }
 

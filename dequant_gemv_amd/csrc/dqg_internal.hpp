@@ -79,6 +79,7 @@ struct FusedArgs {
   int n_a, n_b, n_chunks, ks, n_mt;
   int T, chunks_per_token;  // tokens (1 .. FX_MAX_T) and down chunks per token
   int hold_down;        // down units load their weights only once gate/up results appear
+  int dr;               // down byte rows per lane: 8 (256-row chunks) or 4 (128-row chunks)
 };
 // tokens of the single-launch layer, at most (measured at the 128-expert shape against the
 // multi-launch path: T = 5 30 vs 45 us, T = 8 46 vs 55 us, T = 12 65 vs 68 us, T = 16 84 vs 78 us)
