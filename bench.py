@@ -58,11 +58,18 @@ WORKLOADS = {
                              scales=(0.002, 0.01), logits="normal", layers=48),
     "q30_fp8_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
                              scales=(0.002, 0.01), logits="normal+bias", layers=24),
+    "q30_fp8_layer_t16": dict(kind="moe", T=16, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
+                              scales=(0.002, 0.01), logits="normal+bias", layers=12),
+    "q30_fp8_layer_t64": dict(kind="moe", T=64, E=128, H=2048, I=768, k=8, group=32, fmt=FP8,
+                              scales=(0.002, 0.01), logits="normal+bias", layers=8),
     "q30_mixed_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                                scales=(0.002, 0.01), logits="normal", layers=48, int2_frac=0.25),
     "q30_codebook_layer_t1": dict(kind="moe", T=1, E=128, H=2048, I=768, k=8, group=32,
                                   fmt=FP4, scales=(0.002, 0.01), logits="normal", layers=48,
                                   int2_frac=0.25, fexc_frac=0.25),
+    "q30_codebook_layer_t16": dict(kind="moe", T=16, E=128, H=2048, I=768, k=8, group=32,
+                                   fmt=FP4, scales=(0.002, 0.01), logits="normal+bias",
+                                   layers=24, int2_frac=0.25, fexc_frac=0.25),
     "tiny_moe_layer_t1": dict(kind="moe", T=1, E=8, H=256, I=128, k=2, group=32, fmt=INT4,
                               scales=(0.005, 0.02), logits="normal", layers=48),
     "gemv_int4_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48),

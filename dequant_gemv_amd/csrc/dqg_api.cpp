@@ -157,6 +157,8 @@ int check_moe_common(const uint16_t* x, int T, int H, int I, int E, int k, const
   if (group != 32 && group != 128) return DQG_ERR_UNSUPPORTED;
   if (!moe_sizes_ok(T, H, I, E, k)) return DQG_ERR_UNSUPPORTED;
   if (H % group || I % group) return DQG_ERR_UNSUPPORTED;
+  // one code per byte: an FP8 expert matrix of 2 H I bytes must fit the kernels' 32-bit offsets
+  if (fmt == DQG_FMT_FP8_E4M3 && (long long)H * I > (1LL << 30)) return DQG_ERR_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(wgu) || !aligned16(sgu) || !aligned16(wd) || !aligned16(sd) ||
       !aligned16(out) || (res && !aligned16(res)))
     return DQG_ERR_MISALIGNED;
@@ -357,7 +359,6 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
   int rc = check_moe_common(x, T, H, I, E, k, w_gate_up, s_gate_up, w_down, s_down, group,
                             format, residual, out, workspace, workspace_bytes);
   if (rc != DQG_OK) return rc;
-  if ((format & 0xFF) == DQG_FMT_FP8_E4M3) return DQG_ERR_UNSUPPORTED;  // single launch only
   if (((uintptr_t)ids & 3u) || ((uintptr_t)weights & 3u)) return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
@@ -378,8 +379,6 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
   if (rc != DQG_OK) return rc;
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
-  if ((format & 0xFF) == DQG_FMT_FP8_E4M3 && !use_fused(T, H, I, E, k, format))
-    return DQG_ERR_UNSUPPORTED;  // FP8 weights: single launch only
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   if (use_fused(T, H, I, E, k, format))
     return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
@@ -426,8 +425,6 @@ int moe_fp4_layer_from_hidden(const uint16_t* x, const uint16_t* w_router, int T
   if (!aligned16(w_router)) return DQG_ERR_MISALIGNED;
   if (((uintptr_t)logits_out & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
-  if ((format & 0xFF) == DQG_FMT_FP8_E4M3 && !use_fused(T, H, I, E, k, format))
-    return DQG_ERR_UNSUPPORTED;  // FP8 weights: single launch only
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
   char* b = static_cast<char*>(workspace);
   if (use_fused(T, H, I, E, k, format) && dqg::fused_router_supported(E, T))
@@ -464,16 +461,25 @@ int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, in
   if ((format & 0xFF) != DQG_FMT_FP4_E2M1) return DQG_ERR_UNSUPPORTED;  // FP4 hot experts
   if (E % 4) return DQG_ERR_UNSUPPORTED;                                // table read as words
   if ((uintptr_t)expert_formats & 3u) return DQG_ERR_MISALIGNED;
-  // FE-XC: a down unit's rows span at most two slots, whose codebooks it stages
-  if (codebooks && I / 2 < 256) return DQG_ERR_UNSUPPORTED;
   if (codebooks && !aligned16(codebooks)) return DQG_ERR_MISALIGNED;
-  if (!use_fused(T, H, I, E, k, format)) return DQG_ERR_UNSUPPORTED;   // single launch only
   if (((uintptr_t)logits & 3u) || ((uintptr_t)ids_out & 3u) || ((uintptr_t)weights_out & 3u))
     return DQG_ERR_MISALIGNED;
   const MoePlan p = plan_moe(T, H, I, E, k, workspace_bytes);
-  return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down, group,
-                   format, residual, out, ids_out, weights_out, workspace, stream,
-                   expert_formats, codebooks);
+  // the single launch stages the codebooks of at most two slots per down unit (256 rows):
+  // with FE-XC experts it needs I / 2 >= 256
+  if (use_fused(T, H, I, E, k, format) && !(codebooks && I / 2 < 256))
+    return run_fused(p, x, logits, nullptr, nullptr, w_gate_up, s_gate_up, w_down, s_down,
+                     group, format, residual, out, ids_out, weights_out, workspace, stream,
+                     expert_formats, codebooks);
+  MoeArgs a = make_moe_args(p, x, w_gate_up, s_gate_up, w_down, s_down, group, format, residual,
+                            out, workspace);
+  a.efmt = expert_formats;
+  a.cb = codebooks;
+  a.ids_w = ids_out ? ids_out : a.ws.ids;
+  a.wts_w = weights_out ? weights_out : a.ws.wts;
+  a.ids = a.ids_w;
+  a.wts = a.wts_w;
+  return run_moe(a, p, logits, stream);
 }
 
 size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group) {

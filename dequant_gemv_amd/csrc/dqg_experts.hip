@@ -137,8 +137,16 @@ __device__ __forceinline__ float4 f4_add(float4 a, float4 b) {
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // ---- weights of one block for one lane ----------------------------------------------------
-struct WBlock {
-  uint2 w[4];  // byte rows 16 b + 4 kg + j, 8 columns
+// A lane's share of one block (32 K indices): the byte rows that hold K = 32 b + 8 kg .. +7 of
+// 8 columns -- 4 rows of 4-bit pairs, 8 rows of FP8 codes, or 2 rows of 2-bit codes (INT2:
+// four K indices per byte; FE-XC: the two codebook codes of the 8 K indices) -- and the
+// columns' scales.
+template <int FMT>
+struct WBlockT {
+  static constexpr int R = FMT == FMT_FP8                        ? 8
+                           : (FMT == FMT_INT2 || FMT == FMT_FEXC) ? 2
+                                                                  : 4;  // byte rows per lane
+  uint2 w[R];  // byte rows 4 R b + R kg + j, 8 columns
   uint4 s;     // the 8 columns' bf16 scales of the block's group
 };
 
@@ -158,13 +166,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t view_rsrc(const void* p, size_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
-template <int WAUX>
+// Expert e's view of a [K, ld] matrix read in format F, its slabs slab_rows byte rows apart
+// (the 2-bit codes of a mixed layer's cold experts fill the first K / 4 rows of a 4-bit slab).
+template <int F>
+__device__ __forceinline__ ExpertView expert_view(const uint8_t* w, const uint16_t* s, int e,
+                                                  int K, int slab_rows, size_t ld, int group) {
+  const int rows = F == FMT_FP8 ? K : (F == FMT_INT2 || F == FMT_FEXC) ? K / 4 : K / 2;
+  return ExpertView{view_rsrc(w + (size_t)e * slab_rows * ld, (size_t)rows * ld),
+                    view_rsrc(s + (size_t)e * (K / group) * ld, (size_t)(K / group) * ld * 2),
+                    (int)ld, group};
+}
+
+template <int FMT, int WAUX>
 __device__ __forceinline__ void load_wblock(const ExpertView& v, int blk, int kg, int col,
-                                            bool ok, WBlock& o) {
-  const int wo = ok ? (16 * blk + 4 * kg) * v.ld + col : EX_OOB;
+                                            bool ok, WBlockT<FMT>& o) {
+  constexpr int R = WBlockT<FMT>::R;
+  const int wo = ok ? (4 * R * blk + R * kg) * v.ld + col : EX_OOB;
   const int so = ok ? (((32 * blk) / v.group) * v.ld + col) * 2 : EX_OOB;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < R; ++j) {
     const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(v.w, wo, j * v.ld, WAUX);
     o.w[j] = make_uint2(d.x, d.y);
   }
@@ -183,13 +203,47 @@ __device__ __forceinline__ uint32_t dec_pair(uint32_t d) {
   }
 }
 
-// the lane's 4 pairs of column I (byte rows j = 0..3 of the block)
+// INT2: lane row j holds K 4 j .. 4 j + 3 of every column byte in bits 0-1, 2-3, 4-5, 6-7
+// (code c means c - 2).  The masks move the codes of K 4 j, 4 j + 1 (lo) or 4 j + 2, 4 j + 3
+// (hi) of every byte into its two nibbles, which the FP4 conversion reads as c / 2 exactly
+// (E2M1 codes 0..3 are 0, 0.5, 1, 1.5): the tiles double the scale and add -sum(x).
+__device__ __forceinline__ uint32_t int2_lo_nibbles(uint32_t d) {
+  return (d & 0x03030303u) | ((d << 2) & 0x30303030u);
+}
+__device__ __forceinline__ uint32_t int2_hi_nibbles(uint32_t d) {
+  return ((d >> 4) & 0x03030303u) | ((d >> 2) & 0x30303030u);
+}
+constexpr uint32_t BF16_MINUS_ONE_PAIR = 0xBF80BF80u;
+
+// the lane's 4 pairs of column I: K = 32 b + 8 kg + 2 p, + 1 (p = 0..3) as 16-bit pairs.
+// 4-bit formats: byte I % 4 of row p holds the pair; FP8: rows 2 p and 2 p + 1 hold one code
+// each, interleaved by one v_perm_b32 so that one conversion yields the bf16 pair (E4M3
+// values are exact in bf16).
 template <int FMT, int I>
-__device__ __forceinline__ u32x4_t decode_col(const WBlock& b) {
-  const uint32_t d0 = (I < 4) ? b.w[0].x : b.w[0].y, d1 = (I < 4) ? b.w[1].x : b.w[1].y;
-  const uint32_t d2 = (I < 4) ? b.w[2].x : b.w[2].y, d3 = (I < 4) ? b.w[3].x : b.w[3].y;
-  return u32x4_t{dec_pair<FMT, I % 4>(d0), dec_pair<FMT, I % 4>(d1), dec_pair<FMT, I % 4>(d2),
-                 dec_pair<FMT, I % 4>(d3)};
+__device__ __forceinline__ u32x4_t decode_col(const WBlockT<FMT>& b) {
+  if constexpr (FMT == FMT_FP8) {
+    constexpr uint32_t B = I % 4;
+    constexpr uint32_t sel = B | ((4u + B) << 8) | (B << 16) | ((4u + B) << 24);
+    uint32_t r[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = (I < 4) ? b.w[2 * p].x : b.w[2 * p].y;
+      const uint32_t hi = (I < 4) ? b.w[2 * p + 1].x : b.w[2 * p + 1].y;
+      r[p] = __builtin_bit_cast(uint32_t, fp8_pair_bf16<0>(__builtin_amdgcn_perm(hi, lo, sel)));
+    }
+    return u32x4_t{r[0], r[1], r[2], r[3]};
+  } else if constexpr (FMT == FMT_INT2) {
+    const uint32_t d0 = (I < 4) ? b.w[0].x : b.w[0].y, d1 = (I < 4) ? b.w[1].x : b.w[1].y;
+    return u32x4_t{dec_pair<FMT_FP4, I % 4>(int2_lo_nibbles(d0)),
+                   dec_pair<FMT_FP4, I % 4>(int2_hi_nibbles(d0)),
+                   dec_pair<FMT_FP4, I % 4>(int2_lo_nibbles(d1)),
+                   dec_pair<FMT_FP4, I % 4>(int2_hi_nibbles(d1))};
+  } else {
+    const uint32_t d0 = (I < 4) ? b.w[0].x : b.w[0].y, d1 = (I < 4) ? b.w[1].x : b.w[1].y;
+    const uint32_t d2 = (I < 4) ? b.w[2].x : b.w[2].y, d3 = (I < 4) ? b.w[3].x : b.w[3].y;
+    return u32x4_t{dec_pair<FMT, I % 4>(d0), dec_pair<FMT, I % 4>(d1), dec_pair<FMT, I % 4>(d2),
+                   dec_pair<FMT, I % 4>(d3)};
+  }
 }
 
 __device__ __forceinline__ void scales8(const uint4& s, float (&sf)[8]) {
@@ -199,9 +253,10 @@ __device__ __forceinline__ void scales8(const uint4& s, float (&sf)[8]) {
   sf[6] = bf16_lo(s.w); sf[7] = bf16_hi(s.w);
 }
 
+// 16-bit operands: bf16 for FP4 and FP8 (x stays bf16), fp16 for INT4
 template <int FMT>
 __device__ __forceinline__ float dot2p(uint32_t p, uint32_t x, float c) {
-  if constexpr (FMT == FMT_FP4)
+  if constexpr (FMT != FMT_INT4)
     return dot2_bf16(__builtin_bit_cast(bf16x2_t, p), __builtin_bit_cast(bf16x2_t, x), c);
   else
     return dot2_f16(__builtin_bit_cast(f16x2_t, p), __builtin_bit_cast(f16x2_t, x), c);
@@ -231,12 +286,12 @@ __device__ __forceinline__ uint4 op_from_bf16(const uint16_t* row, int q8) {
   }
   return v;
 }
-// from an fp32 row (h): rounded to bf16 (FP4) or fp16 (INT4), nearest even
+// from an fp32 row (h): rounded to bf16 (FP4, FP8) or fp16 (INT4), nearest even
 template <int FMT>
 __device__ __forceinline__ uint4 op_from_f32(const float* row, int q8) {
   const float4 a = reinterpret_cast<const float4*>(row)[2 * q8];
   const float4 b = reinterpret_cast<const float4*>(row)[2 * q8 + 1];
-  if constexpr (FMT == FMT_FP4)
+  if constexpr (FMT != FMT_INT4)
     return make_uint4(f32pair_to_bf16pair(a.x, a.y), f32pair_to_bf16pair(a.z, a.w),
                       f32pair_to_bf16pair(b.x, b.y), f32pair_to_bf16pair(b.z, b.w));
   else
@@ -247,7 +302,7 @@ __device__ __forceinline__ uint4 op_from_f32(const float* row, int q8) {
 template <int FMT>
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const u32x4_t& b, f32x4_t c) {
   const u32x4_t av = {a.x, a.y, a.z, a.w};
-  if constexpr (FMT == FMT_FP4)
+  if constexpr (FMT != FMT_INT4)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   else
@@ -312,14 +367,14 @@ struct Acc<BODY_MFMA, MT> {
 // The lane's weights of one group: RBW blocks (b = g0 + off + step * r); blocks past b1
 // (and columns past the tile) load as zero.  WAUX: the loads' cache policy (EX_STREAM for
 // weights that are read once per call).
-template <int RBW, int WAUX = 0>
+template <int FMT, int RBW, int WAUX = 0>
 __device__ __forceinline__ void load_group(const ExpertView& v, int g0, int off, int step,
                                            int b1, int kg, int col, bool col_ok,
-                                           WBlock (&wb)[RBW]) {
+                                           WBlockT<FMT> (&wb)[RBW]) {
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     const int b = g0 + off + step * r;
-    load_wblock<WAUX>(v, b, kg, col, col_ok && b < b1, wb[r]);
+    load_wblock<FMT, WAUX>(v, b, kg, col, col_ok && b < b1, wb[r]);
   }
 }
 
@@ -355,8 +410,8 @@ struct Window {
 // The vector-ALU tiles keep INT4 pairs biased, (1024 + lo, 64 + hi): the bias
 // 1032 x[2r] + 72 x[2r+1] of the lane's rows is removed once per token and block (corr).
 template <int FMT, int I>
-__device__ __forceinline__ u32x4_t decode_col_valu(const WBlock& b) {
-  if constexpr (FMT == FMT_FP4) {
+__device__ __forceinline__ u32x4_t decode_col_valu(const WBlockT<FMT>& b) {
+  if constexpr (FMT != FMT_INT4) {
     return decode_col<FMT, I>(b);
   } else {
     const uint32_t d0 = (I < 4) ? b.w[0].x : b.w[0].y, d1 = (I < 4) ? b.w[1].x : b.w[1].y;
@@ -369,7 +424,7 @@ __device__ __forceinline__ u32x4_t decode_col_valu(const WBlock& b) {
 }
 
 template <int FMT, int NTOK, int VT, int I>
-__device__ __forceinline__ void valu_col(const WBlock& b, float sc, const uint4 (&op)[NTOK],
+__device__ __forceinline__ void valu_col(const WBlockT<FMT>& b, float sc, const uint4 (&op)[NTOK],
                                          const float (&corr)[NTOK], float (&acc)[VT][8]) {
   const u32x4_t P = decode_col_valu<FMT, I>(b);
 #pragma unroll
@@ -381,26 +436,92 @@ __device__ __forceinline__ void valu_col(const WBlock& b, float sc, const uint4 
     acc[t][I] = fmaf(sc, d, acc[t][I]);
   }
 }
+// c0: the products' initial value (zero; for INT2 the tile's -sum(x) per token row)
 template <int FMT, int MT, int I>
-__device__ __forceinline__ void mfma_col(const WBlock& b, float sc, const uint4 (&A)[MT],
-                                         f32x4_t (&acc)[MT][8]) {
+__device__ __forceinline__ void mfma_col(const WBlockT<FMT>& b, float sc, const uint4 (&A)[MT],
+                                         const f32x4_t (&c0)[MT], f32x4_t (&acc)[MT][8]) {
   const u32x4_t B = decode_col<FMT, I>(b);
-  const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const f32x4_t D = mfma_16x16x32<FMT>(A[m], B, zero);
+    const f32x4_t D = mfma_16x16x32<FMT>(A[m], B, c0[m]);
     acc[m][I] += sc * D;
+  }
+}
+
+// FE-XC: lane row j of a block holds codebook j's code of the lane's 8 K indices for 8
+// columns; the weights are C[0][c0] + C[1][c1] (8 bf16 each: one uint4 of the LDS copy cbl,
+// [2][256] vectors) times the scale.  A vector's 8 values line up with the token's 8 K
+// values as they are, so each codebook gives one dot2 chain (vector ALU) or one product
+// into the column's accumulator (matrix cores): the decomposition is exact.
+template <int BODY, int MT, int NTOK>
+__device__ __forceinline__ void fexc_block(const WBlockT<FMT_FEXC>& b, const uint4* wrow,
+                                           const uint4* cbl, const float (&sf)[8],
+                                           Acc<BODY, MT>& acc) {
+  if constexpr (BODY == BODY_VALU) {
+    uint4 op[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) op[t] = wrow[t * EX_WROW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t d0 = (i < 4) ? b.w[0].x : b.w[0].y, d1 = (i < 4) ? b.w[1].x : b.w[1].y;
+      const uint4 v0 = cbl[(d0 >> (8 * (i & 3))) & 0xFFu];
+      const uint4 v1 = cbl[256 + ((d1 >> (8 * (i & 3))) & 0xFFu)];
+#pragma unroll
+      for (int t = 0; t < NTOK; ++t) {
+        float d = dot2p<FMT_FEXC>(v0.x, op[t].x, 0.0f);
+        d = dot2p<FMT_FEXC>(v0.y, op[t].y, d);
+        d = dot2p<FMT_FEXC>(v0.z, op[t].z, d);
+        d = dot2p<FMT_FEXC>(v0.w, op[t].w, d);
+        d = dot2p<FMT_FEXC>(v1.x, op[t].x, d);
+        d = dot2p<FMT_FEXC>(v1.y, op[t].y, d);
+        d = dot2p<FMT_FEXC>(v1.z, op[t].z, d);
+        d = dot2p<FMT_FEXC>(v1.w, op[t].w, d);
+        acc.v[t][i] = fmaf(sf[i], d, acc.v[t][i]);
+      }
+    }
+  } else {
+    const int q = threadIdx.x & 15;
+    uint4 A[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) A[m] = wrow[(16 * m + q) * EX_WROW];
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t d0 = (i < 4) ? b.w[0].x : b.w[0].y, d1 = (i < 4) ? b.w[1].x : b.w[1].y;
+      const uint4 v0 = cbl[(d0 >> (8 * (i & 3))) & 0xFFu];
+      const uint4 v1 = cbl[256 + ((d1 >> (8 * (i & 3))) & 0xFFu)];
+      const u32x4_t B0 = {v0.x, v0.y, v0.z, v0.w}, B1 = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const f32x4_t D = mfma_16x16x32<FMT_FEXC>(A[m], B1, mfma_16x16x32<FMT_FEXC>(A[m], B0, zero));
+        acc.v[m][i] += sf[i] * D;
+      }
+    }
   }
 }
 
 // One block: `wrow` = the window entry of this block and lane group for token row 0.
 // VALU: NTOK token rows; MFMA: MT tiles of 16 rows (rows past the pass are zero).
+// FP8 blocks hold twice the bytes of the 4-bit ones; left free, the scheduler decodes every
+// column of a block ahead of its products and the matrix-core kernel needs 264 registers
+// (one wave per SIMD).  A fence after each column keeps one column's operands live.
+template <int FMT>
+__device__ __forceinline__ void col_fence() {
+  if constexpr (FMT == FMT_FP8) __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int FMT, int BODY, int MT, int NTOK>
-__device__ __forceinline__ void compute_block(const WBlock& b, const uint4* wrow,
-                                              Acc<BODY, MT>& acc) {
+__device__ __forceinline__ void compute_block(const WBlockT<FMT>& b, const uint4* wrow,
+                                              Acc<BODY, MT>& acc, const uint4* cbl) {
   float sf[8];
   scales8(b.s, sf);
-  if constexpr (BODY == BODY_VALU) {
+  if constexpr (FMT == FMT_INT2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sf[i] *= 2.0f;  // the decoded pairs hold c / 2
+  }
+  if constexpr (FMT == FMT_FEXC) {
+    fexc_block<BODY, MT, NTOK>(b, wrow, cbl, sf, acc);
+  } else if constexpr (BODY == BODY_VALU) {
     uint4 op[NTOK];
     float corr[NTOK];
 #pragma unroll
@@ -414,39 +535,68 @@ __device__ __forceinline__ void compute_block(const WBlock& b, const uint4* wrow
         corr[t] = dot2p<FMT>(bb, op[t].y, corr[t]);
         corr[t] = dot2p<FMT>(bb, op[t].z, corr[t]);
         corr[t] = dot2p<FMT>(bb, op[t].w, corr[t]);
+      } else if constexpr (FMT == FMT_INT2) {  // -sum(x) of the lane's 8 K indices
+        corr[t] = dot2p<FMT>(BF16_MINUS_ONE_PAIR, op[t].x, corr[t]);
+        corr[t] = dot2p<FMT>(BF16_MINUS_ONE_PAIR, op[t].y, corr[t]);
+        corr[t] = dot2p<FMT>(BF16_MINUS_ONE_PAIR, op[t].z, corr[t]);
+        corr[t] = dot2p<FMT>(BF16_MINUS_ONE_PAIR, op[t].w, corr[t]);
       }
     }
     valu_col<FMT, NTOK, MT, 0>(b, sf[0], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 1>(b, sf[1], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 2>(b, sf[2], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 3>(b, sf[3], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 4>(b, sf[4], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 5>(b, sf[5], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 6>(b, sf[6], op, corr, acc.v);
+    col_fence<FMT>();
     valu_col<FMT, NTOK, MT, 7>(b, sf[7], op, corr, acc.v);
   } else {
     const int q = threadIdx.x & 15;
     uint4 A[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) A[m] = wrow[(16 * m + q) * EX_WROW];
-    mfma_col<FMT, MT, 0>(b, sf[0], A, acc.v);
-    mfma_col<FMT, MT, 1>(b, sf[1], A, acc.v);
-    mfma_col<FMT, MT, 2>(b, sf[2], A, acc.v);
-    mfma_col<FMT, MT, 3>(b, sf[3], A, acc.v);
-    mfma_col<FMT, MT, 4>(b, sf[4], A, acc.v);
-    mfma_col<FMT, MT, 5>(b, sf[5], A, acc.v);
-    mfma_col<FMT, MT, 6>(b, sf[6], A, acc.v);
-    mfma_col<FMT, MT, 7>(b, sf[7], A, acc.v);
+    f32x4_t c0[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      c0[m] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (FMT == FMT_INT2) {  // -sum(x) of every token row, in every column
+        const u32x4_t mo = {BF16_MINUS_ONE_PAIR, BF16_MINUS_ONE_PAIR, BF16_MINUS_ONE_PAIR,
+                            BF16_MINUS_ONE_PAIR};
+        c0[m] = mfma_16x16x32<FMT>(A[m], mo, c0[m]);
+      }
+    }
+    mfma_col<FMT, MT, 0>(b, sf[0], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 1>(b, sf[1], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 2>(b, sf[2], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 3>(b, sf[3], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 4>(b, sf[4], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 5>(b, sf[5], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 6>(b, sf[6], A, c0, acc.v);
+    col_fence<FMT>();
+    mfma_col<FMT, MT, 7>(b, sf[7], A, c0, acc.v);
   }
 }
 
 template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP>
-__device__ __forceinline__ void compute_group(const WBlock (&wb)[RBW], const uint4* win, int off,
-                                              Acc<BODY, MT>& acc) {
+__device__ __forceinline__ void compute_group(const WBlockT<FMT> (&wb)[RBW], const uint4* win, int off,
+                                              Acc<BODY, MT>& acc, const uint4* cbl) {
   const int kg = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int r = 0; r < RBW; ++r)
-    compute_block<FMT, BODY, MT, NTOK>(wb[r], win + (off + STEP * r) * 4 + kg, acc);
+    compute_block<FMT, BODY, MT, NTOK>(wb[r], win + (off + STEP * r) * 4 + kg, acc, cbl);
 }
 
 // Streams blocks [b0, b1) of one expert matrix in batches of GB = RBW * STEP blocks: the
@@ -460,7 +610,8 @@ template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP, int WAUX = 0>
 __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool col_ok,
                                               const OpSrc& src, const int* s_slot, int nch,
                                               int b0, int b1, int off, float* lds,
-                                              WBlock (&wa)[RBW], Acc<BODY, MT>& acc) {
+                                              WBlockT<FMT> (&wa)[RBW], Acc<BODY, MT>& acc,
+                                              const uint4* cbl = nullptr) {
   constexpr int GB = RBW * STEP;
   const int kg = (threadIdx.x & 63) >> 4;
   uint4* win = reinterpret_cast<uint4*>(lds);
@@ -476,13 +627,13 @@ __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool
       for (int i = 0; i < 8; ++i) acc.v[m][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   for (int bb = b0; bb < b1; bb += GB) {
-    if (bb != b0) load_group<RBW, WAUX>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
+    if (bb != b0) load_group<FMT, RBW, WAUX>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
     Window<FMT, GB, NTOK> wnd;
     wnd.load(src, s_slot, nch, bb, b1);
     if (bb != b0) __syncthreads();  // the previous batch is done with the window
     wnd.store(win);
     __syncthreads();
-    compute_group<FMT, BODY, MT, NTOK, RBW, STEP>(wa, win, off, acc);
+    compute_group<FMT, BODY, MT, NTOK, RBW, STEP>(wa, win, off, acc, cbl);
   }
   __syncthreads();
 }
@@ -492,27 +643,95 @@ __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool
 template <int FMT, int VT, int RBW, int STEP, int WAUX = 0>
 __device__ __forceinline__ void stream_valu(const ExpertView& v, int col, bool col_ok,
                                             const OpSrc& src, const int* s_slot, int nch, int b0,
-                                            int b1, int off, float* lds, WBlock (&wa)[RBW],
-                                            Acc<BODY_VALU, VT>& acc) {
+                                            int b1, int off, float* lds, WBlockT<FMT> (&wa)[RBW],
+                                            Acc<BODY_VALU, VT>& acc, const uint4* cbl = nullptr) {
   if (VT <= 1 || nch <= 1)
     stream_expert<FMT, BODY_VALU, VT, 1, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
-                                                          b1, off, lds, wa, acc);
+                                                          b1, off, lds, wa, acc, cbl);
   else if (VT <= 2 || nch <= 2)
     stream_expert<FMT, BODY_VALU, VT, (VT < 2 ? VT : 2), RBW, STEP, WAUX>(
-        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc);
+        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc, cbl);
   else if (VT <= 4 || nch <= 4)
     stream_expert<FMT, BODY_VALU, VT, (VT < 4 ? VT : 4), RBW, STEP, WAUX>(
-        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc);
+        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc, cbl);
   else
     stream_expert<FMT, BODY_VALU, VT, VT, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
-                                                           b1, off, lds, wa, acc);
+                                                           b1, off, lds, wa, acc, cbl);
 }
 
-// 16-bit h operand pair (bf16 for FP4, fp16 for INT4) of SiLU(g) * u, two columns
+// One pass of a phase in weight format F: the first batch's weights load while the pass's
+// slot list is fetched into LDS, then the stream (matrix-core or vector-ALU body).
+template <int F, int BODY, int MT, int RBW, int STEP>
+__device__ __forceinline__ void run_pass(const MoeArgs& a, const ExpertView& v, int col,
+                                         bool col_ok, const OpSrc& src, int* s_slot, int first,
+                                         int nch, int b0, int b1, int off, float* lds,
+                                         const uint4* cbl, Acc<BODY, MT>& acc) {
+  const int kg = (threadIdx.x & 63) >> 4;
+  WBlockT<F> wa[RBW];
+  load_group<F, RBW>(v, b0, off, STEP, b1, kg, col, col_ok, wa);
+  if ((int)threadIdx.x < nch) s_slot[threadIdx.x] = slot_at(a, first + threadIdx.x);
+  __syncthreads();
+  if constexpr (BODY == BODY_MFMA)
+    stream_expert<F, BODY_MFMA, MT, 16 * MT, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0,
+                                                        b1, off, lds, wa, acc, cbl);
+  else
+    stream_valu<F, MT, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc,
+                                  cbl);
+}
+
+// The weight format of expert e in a kernel of base format FMT: with a per-expert table
+// (MIX), INT2 and FE-XC entries (FE-XC only with codebooks) run the 2-bit tiles, any other
+// entry the FP4 ones.
+template <int FMT, bool MIX>
+__device__ __forceinline__ int expert_format(const MoeArgs& a, int e) {
+  if constexpr (!MIX) {
+    return FMT;
+  } else {
+    const int f = a.efmt[e];
+    return (f == FMT_INT2 || (f == FMT_FEXC && a.cb != nullptr)) ? f : FMT_FP4;
+  }
+}
+
+// An FE-XC expert's two codebooks of one projection (m = 0 gate_up, 1 down) into LDS:
+// [2][256] uint4 from the bf16 table [E][2][2][256][8].  The caller's next barrier
+// publishes them.
+__device__ __forceinline__ void stage_codebooks(const MoeArgs& a, int e, int m, uint4* cbl) {
+  const uint4* src = reinterpret_cast<const uint4*>(a.cb) + ((size_t)e * 2 + m) * 512;
+  for (int i = threadIdx.x; i < 512; i += EX_THREADS) cbl[i] = src[i];
+}
+
+// A pass in the expert's format: FMT, or (MIX) the 2-bit formats of a mixed layer.
+template <int FMT, bool MIX, int BODY, int MT, int RBW, int STEP>
+__device__ __forceinline__ void run_pass_fmt(int ef, const MoeArgs& a, const uint8_t* w,
+                                             const uint16_t* sc, int e, int K, size_t ld,
+                                             int col, bool col_ok, const OpSrc& src,
+                                             int* s_slot, int first, int nch, int b0, int b1,
+                                             int off, float* lds, const uint4* cbl,
+                                             Acc<BODY, MT>& acc) {
+  const int slab = K / fmt_kb(FMT);
+  if constexpr (MIX) {
+    if (ef == FMT_INT2) {
+      run_pass<FMT_INT2, BODY, MT, RBW, STEP>(
+          a, expert_view<FMT_INT2>(w, sc, e, K, slab, ld, a.group), col, col_ok, src, s_slot,
+          first, nch, b0, b1, off, lds, cbl, acc);
+      return;
+    }
+    if (ef == FMT_FEXC) {
+      run_pass<FMT_FEXC, BODY, MT, RBW, STEP>(
+          a, expert_view<FMT_FEXC>(w, sc, e, K, slab, ld, a.group), col, col_ok, src, s_slot,
+          first, nch, b0, b1, off, lds, cbl, acc);
+      return;
+    }
+  }
+  run_pass<FMT, BODY, MT, RBW, STEP>(a, expert_view<FMT>(w, sc, e, K, slab, ld, a.group), col,
+                                     col_ok, src, s_slot, first, nch, b0, b1, off, lds, cbl, acc);
+}
+
+// 16-bit h operand pair (bf16 for FP4 and FP8, fp16 for INT4) of SiLU(g) * u, two columns
 template <int FMT>
 __device__ __forceinline__ uint32_t h_pair(float g0, float u0, float g1, float u1) {
   const float h0 = silu_mul(g0, u0), h1 = silu_mul(g1, u1);
-  if constexpr (FMT == FMT_FP4)
+  if constexpr (FMT != FMT_INT4)
     return f32pair_to_bf16pair(h0, h1);
   else
     return f32pair_to_f16pair(h0, h1);
@@ -530,7 +749,7 @@ __device__ __forceinline__ void store_h4(uint16_t* hop, size_t idx, float4 g, fl
 // gate_up + SiLU*up.  Grid: x = 128-column h tile, y = K split, z = active-expert index.
 // Waves: w & 1 = gate (0) or up (1) columns, w >> 1 = even or odd blocks of each group.
 // ======================================================================================
-template <int FMT, int MT, int VT>
+template <int FMT, int MT, int VT, bool MIX>
 __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
   constexpr int TS = VT < 4 ? VT : 4;  // token slots of the vector-ALU reduction
   __shared__ __align__(16) float lds[ex_lds_floats(MT, VT)];
@@ -550,10 +769,6 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
   const int ncols = min(128, I - n0);      // valid h columns (64 or 128)
   const bool col_ok = 8 * q < ncols;
   const int col = role * I + n0 + 8 * q;
-  const ExpertView v{view_rsrc(a.wgu + (size_t)e * (H / 2) * ld, (size_t)(H / 2) * ld),
-                     view_rsrc(a.sgu + (size_t)e * (H / a.group) * ld,
-                               (size_t)(H / a.group) * ld * 2),
-                     (int)ld, a.group};
   const OpSrc src{view_rsrc(a.x, (size_t)a.T * H * 2), true, 2 * H, k};
   // Experts with at least mfma_min tokens take MT matrix-core tiles of 16 rows (MT > 0),
   // the others VT-token vector-ALU passes, in the same launch.
@@ -607,17 +822,19 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
     return;
   }
 
+  const int ef = expert_format<FMT, MIX>(a, e);
+  __shared__ uint4 s_cb[MIX ? 512 : 1];
+  if constexpr (MIX)
+    if (ef == FMT_FEXC) stage_codebooks(a, e, 0, s_cb);
+
   for (int m0 = 0; m0 < cnt; m0 += CH) {
     const int nch = min(CH, cnt - m0);
-    WBlock wa[2];  // the first group's weights load while the slots are fetched
-    load_group<2>(v, b0, khalf, 2, b1, kg, col, col_ok, wa);
-    if (tid < nch) s_slot[tid] = slot_at(a, beg + m0 + tid);
-    __syncthreads();
     if constexpr (MT > 0) {
       if (use_mfma) {
         Acc<BODY_MFMA, MT> acc;
-        stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 2>(v, col, col_ok, src, s_slot, nch, b0,
-                                                         b1, khalf, lds, wa, acc);
+        run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 2>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok,
+                                                    src, s_slot, beg + m0, nch, b0, b1, khalf,
+                                                    lds, s_cb, acc);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (16 * m >= nch) break;
@@ -644,7 +861,9 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
       }
     }
     Acc<BODY_VALU, VT> acc;
-    stream_valu<FMT, VT, 2, 2>(v, col, col_ok, src, s_slot, nch, b0, b1, khalf, lds, wa, acc);
+    run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 2>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok, src,
+                                                s_slot, beg + m0, nch, b0, b1, khalf, lds, s_cb,
+                                                acc);
     // two halves of 4 tokens: red[role][khalf][kg][token 0..3][column 0..127]
 #pragma unroll
     for (int hh = 0; hh < (VT + 3) / 4; ++hh) {
@@ -718,7 +937,7 @@ __device__ __forceinline__ void combine_token(const MoeArgs& a, __amdgpu_buffer_
 
 constexpr int EX_COMBINE_TOKENS = 2;  // tokens per combiner workgroup (x 128 columns)
 
-template <int FMT, int MT, int VT>
+template <int FMT, int MT, int VT, bool MIX>
 __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
   constexpr int TS = VT < 4 ? VT : 4;  // token slots of the vector-ALU reduction
   __shared__ __align__(16) float lds[ex_lds_floats(MT, VT)];
@@ -750,10 +969,6 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
   const size_t ld = (size_t)H;
   const bool col_ok = 8 * q < ncols;
   const int col = m0c + 8 * q;
-  const ExpertView v{view_rsrc(a.wd + (size_t)e * (I / 2) * ld, (size_t)(I / 2) * ld),
-                     view_rsrc(a.sd + (size_t)e * (I / a.group) * ld,
-                               (size_t)(I / a.group) * ld * 2),
-                     (int)ld, a.group};
   const OpSrc src{view_rsrc(a.ws.hop, (size_t)TKc * I * 2), false, 2 * I, k};
   const bool use_mfma = MT > 0 && cnt >= a.mfma_min;  // as in gate_up
   const int CH = use_mfma ? 16 * MT : VT;
@@ -761,19 +976,21 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
     st4_sc1(pr, ((s * TKc + slot) * H + m0c + c4) * 4, pub4(y));
   };
 
+  const int ef = expert_format<FMT, MIX>(a, e);
+  __shared__ uint4 s_cb[MIX ? 512 : 1];
+  if constexpr (MIX)
+    if (ef == FMT_FEXC) stage_codebooks(a, e, 1, s_cb);
+
   for (int c0 = 0; c0 < cnt; c0 += CH) {
     const int nch = min(CH, cnt - c0);
-    WBlock wa[2];  // the first group's weights load while the slots are fetched
-    load_group<2>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
-    if (tid < nch) s_slot[tid] = slot_at(a, beg + c0 + tid);
-    __syncthreads();
     bool done = false;
     if constexpr (MT > 0) {
       if (use_mfma) {
       done = true;
       Acc<BODY_MFMA, MT> acc;
-      stream_expert<FMT, BODY_MFMA, MT, 16 * MT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1,
-                                                       wv, lds, wa, acc);
+      run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 4>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
+                                                  s_slot, beg + c0, nch, b0, b1, wv, lds, s_cb,
+                                                  acc);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (16 * m >= nch) break;
@@ -801,7 +1018,9 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
     }
     if (!done) {
       Acc<BODY_VALU, VT> acc;
-      stream_valu<FMT, VT, 2, 4>(v, col, col_ok, src, s_slot, nch, b0, b1, wv, lds, wa, acc);
+      run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 4>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
+                                                  s_slot, beg + c0, nch, b0, b1, wv, lds, s_cb,
+                                                  acc);
 #pragma unroll
       for (int hh = 0; hh < (VT + 3) / 4; ++hh) {
         if (4 * hh >= nch) break;
@@ -896,8 +1115,8 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 
   for (int c0 = 0; c0 < T; c0 += CH) {
     const int nch = min(CH, T - c0);
-    WBlock wa[2];  // the first group's weights load while the token list is set up
-    load_group<2, EX_STREAM>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
+    WBlockT<FMT> wa[2];  // the first group's weights load while the token list is set up
+    load_group<FMT, 2, EX_STREAM>(v, b0, wv, 4, b1, kg, col, col_ok, wa);
     if (tid < nch) s_slot[tid] = c0 + tid;
     __syncthreads();
     if constexpr (MT > 0) {
@@ -978,21 +1197,21 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
 int ex_max_split_gemv() { return EX_MAX_SPLIT_GEMV; }
 
 // ---- launchers --------------------------------------------------------------------------------
-template <int FMT, int MT, int VT>
+template <int FMT, int MT, int VT, bool MIX>
 static hipError_t launch_phase(const MoeArgs& a, int A, bool down, hipStream_t st) {
   if (!down) {
-    hipLaunchKernelGGL((gateup_ex_kernel<FMT, MT, VT>),
+    hipLaunchKernelGGL((gateup_ex_kernel<FMT, MT, VT, MIX>),
                        dim3((a.I + 127) / 128, a.S_gu + (a.S_gu > 1 ? 1 : 0), A),
                        dim3(EX_THREADS), 0, st, a);
   } else {
     const int zc = a.combine ? (a.T + EX_COMBINE_TOKENS - 1) / EX_COMBINE_TOKENS : 0;
-    hipLaunchKernelGGL((down_ex_kernel<FMT, MT, VT>), dim3((a.H + 127) / 128, a.S_dn, A + zc),
+    hipLaunchKernelGGL((down_ex_kernel<FMT, MT, VT, MIX>), dim3((a.H + 127) / 128, a.S_dn, A + zc),
                        dim3(EX_THREADS), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool MIX = false>
 static hipError_t launch_ex_t(const MoeArgs& a0, int A, int mt, hipStream_t st) {
   // one launch per phase: with matrix-core tiles (mt > 0) the kernel serves the experts
   // below the threshold with EX_VT-token vector-ALU passes in the same launch
@@ -1001,10 +1220,10 @@ static hipError_t launch_ex_t(const MoeArgs& a0, int A, int mt, hipStream_t st) 
   for (int down = 0; down < 2; ++down) {
     a.combine = down;  // the down launch also runs the per-token combiners
     hipError_t e;
-    if (mt == 1) e = launch_phase<FMT, 1, EX_VT>(a, A, down, st);
-    else if (vt == 1) e = launch_phase<FMT, 0, 1>(a, A, down, st);
-    else if (vt == 2) e = launch_phase<FMT, 0, 2>(a, A, down, st);
-    else e = launch_phase<FMT, 0, EX_VT>(a, A, down, st);
+    if (mt == 1) e = launch_phase<FMT, 1, EX_VT, MIX>(a, A, down, st);
+    else if (vt == 1) e = launch_phase<FMT, 0, 1, MIX>(a, A, down, st);
+    else if (vt == 2) e = launch_phase<FMT, 0, 2, MIX>(a, A, down, st);
+    else e = launch_phase<FMT, 0, EX_VT, MIX>(a, A, down, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1012,8 +1231,13 @@ static hipError_t launch_ex_t(const MoeArgs& a0, int A, int mt, hipStream_t st) 
 
 hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st) {
   if (mt < 0 || mt > 1) return hipErrorInvalidValue;
+  if (a.efmt) {  // a mixed layer: FP4 experts with 2-bit cold ones
+    if (a.fmt != FMT_FP4) return hipErrorInvalidValue;
+    return launch_ex_t<FMT_FP4, true>(a, A, mt, st);
+  }
   if (a.fmt == FMT_FP4) return launch_ex_t<FMT_FP4>(a, A, mt, st);
   if (a.fmt == FMT_INT4) return launch_ex_t<FMT_INT4>(a, A, mt, st);
+  if (a.fmt == FMT_FP8) return launch_ex_t<FMT_FP8>(a, A, mt, st);
   return hipErrorInvalidValue;
 }
 

@@ -38,6 +38,8 @@ struct MoeArgs {
   int S_gu, S_dn;
   int mfma_min;         // experts with at least this many tokens use the MFMA tiles
   int combine;          // this down launch also runs the per-token combine (the last one)
+  const uint8_t* efmt;  // per-expert formats [E] of a mixed FP4 layer, or null
+  const uint16_t* cb;   // FE-XC codebooks bf16 [E][2 (gate_up, down)][2][256][8], or null
 };
 
 struct GemvArgs {

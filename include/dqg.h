@@ -56,8 +56,8 @@ typedef enum dqg_format {
   DQG_FMT_INT4 = 0,     /* value = nibble - 8                                           */
   DQG_FMT_FP4_E2M1 = 1, /* value = E2M1(nibble)                                         */
   DQG_FMT_FP8_E4M3 = 2, /* value = E4M3(byte), one byte per weight: packed matrices are
-                           [K, N] instead of [K/2, N]; the MoE layer calls only, on their
-                           single launch (see moe_fp4_layer)                             */
+                           [K, N] instead of [K/2, N]; the MoE layer calls only
+                           (see moe_fp4_layer)                                           */
   DQG_FMT_INT2 = 3,     /* value = code - 2, four codes per byte: only as an entry of the
                            per-expert table of moe_fp4_layer_mixed                       */
   DQG_FMT_FEXC = 4      /* FE-XC 2x8 codebook codes: only as an entry of that table       */
@@ -120,7 +120,9 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *   w_gate_up  uint8 [E, H/2, 2I], s_gate_up bf16 [E, H/G, 2I]; columns [0, I) are the
  *              gate projection, [I, 2I) the up projection
  *   w_down     uint8 [E, I/2, H],  s_down    bf16 [E, I/G, H]
- *   group      G (32 or 128), format DQG_FMT_* optionally OR-ed with DQG_PATH_* flags
+ *              (DQG_FMT_FP8_E4M3: [E, H, 2I] and [E, I, H], one code per byte)
+ *   group      G (32 or 128), format DQG_FMT_INT4, DQG_FMT_FP4_E2M1 or DQG_FMT_FP8_E4M3,
+ *              optionally OR-ed with DQG_PATH_* flags
  *   residual   bf16 [T, H] or NULL
  *   out        bf16 [T, H]:
  *     out[t] = bf16_rne( residual[t] + sum_{j<k} weights[t,j] * y_{t,j} ), j ascending,
@@ -128,9 +130,9 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *   accumulated in fp32.
  * Each expert's weights are streamed once per call for up to 16 of its tokens (the
  * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
- * (FP4) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch per
- * projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16 (FP4)
- * or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch layer
+ * (FP4, FP8) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch
+ * per projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16
+ * (FP4, FP8) or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch layer
  * (moe_fp4_layer, T <= 8).
  * Results are deterministic (fixed reduction order, no floating-point atomics).
  * Requires H % 64 == 0, I % 64 == 0, H and I multiples of G, 1 <= k <= min(E, 32),
@@ -156,9 +158,9 @@ int moe_fp4_ffn(const uint16_t* x, int T, int H, int I, int E, int k, const int3
  * weights_out (fp32 [T, k]) are optional outputs of the routing (NULL to skip).
  * DQG_FMT_FP8_E4M3 (FireEcho page, "Quantization Formats": an 8-bit FP format; read as OCP
  * E4M3) takes w_gate_up uint8 [E, H, 2I] and w_down uint8 [E, I, H], one code per byte, with
- * the same scales; it runs on the single launch only (for T > 1, k * I a multiple of 256)
- * and returns DQG_ERR_UNSUPPORTED where that does not apply (also with DQG_PATH_NO_FUSED,
- * and always from moe_fp4_ffn).  E4M3 codes S.1111.111 (NaN) give unspecified results.
+ * the same scales, on both paths and in moe_fp4_ffn and moe_fp4_layer_from_hidden alike
+ * (H * I at most 2^30, else DQG_ERR_UNSUPPORTED).  E4M3 codes S.1111.111 (NaN) give
+ * unspecified results.
  */
 int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, int E, int k,
                   const uint8_t* w_gate_up, const uint16_t* s_gate_up, const uint8_t* w_down,
@@ -174,8 +176,7 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
  *                   an INT2 expert, DQG_FMT_FEXC an FE-XC expert; any other value means FP4
  *                   (format must be DQG_FMT_FP4_E2M1)
  *   codebooks       bf16 [E, 2, 2, 256, 8] (16-byte aligned) or NULL: per expert, for gate_up
- *                   then down, two codebooks of 256 vectors of 8; needs I >= 512 (a down unit's
- *                   256 rows then span at most two experts).  An FE-XC expert's codes fill the
+ *                   then down, two codebooks of 256 vectors of 8.  An FE-XC expert's codes fill the
  *                   first quarter-K rows of its slab as [K/8, 2, N] bytes (codebook m's code of
  *                   the group of K indices 8g .. 8g+7 in byte row 2g + m); its weights are
  *                   (C[0][c0] + C[1][c1])[i] * scale.  Without codebooks an FE-XC entry reads
@@ -184,8 +185,13 @@ int moe_fp4_layer(const uint16_t* x, const float* logits, int T, int H, int I, i
  *                   fill the first quarter-K rows of its slab: [H/4, 2I] and [I/4, H] bytes,
  *                   K index 4r + i in bits 2i .. 2i+1 of byte row r (code c means c - 2); the
  *                   scales keep their layout.  INT2 experts stream half the bytes.
- * Runs on the single launch only (the conditions of moe_fp4_layer) and returns
- * DQG_ERR_UNSUPPORTED otherwise.  Other arguments and rules as moe_fp4_layer.
+ * Runs as one launch where moe_fp4_layer would (with codebooks also I >= 512: a down unit's
+ * 256 rows then span at most two experts, whose codebooks it stages), otherwise on the
+ * multi-launch kernels, where INT2 and FE-XC experts take 2-bit tiles of their own: INT2
+ * codes decode to c / 2 (the scale doubled, -sum(x) per block added), FE-XC vectors meet
+ * the operands as they are, one product per codebook; both on the vector-ALU or the
+ * matrix-core body by token count, as FP4 experts (DQG_PATH_* flags apply).  Other
+ * arguments and rules as moe_fp4_layer.
  */
 int moe_fp4_layer_mixed(const uint16_t* x, const float* logits, int T, int H, int I, int E,
                         int k, const uint8_t* w_gate_up, const uint16_t* s_gate_up,

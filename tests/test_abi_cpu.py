@@ -108,18 +108,14 @@ def test_moe_layer_validation():
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
 
 
-def test_fp8_outside_the_single_launch_is_rejected_before_launch():
-    # moe_fp4_ffn never takes FP8
-    assert _moe(fmt=B.FMT_FP8_E4M3) == B.DQG_ERR_UNSUPPORTED
+def test_fp8_validation():
+    # FP8 runs on both paths; an expert matrix of 2 H I bytes must fit 32-bit offsets
     f = B.LIB.moe_fp4_layer
-    def layer(T, fmt):
-        return f(A, A, T, 256, 128, 8, 2, A, A, A, A, 32, fmt, 0, A, 0, 0, A, 1 << 30, None)
-    assert layer(16, B.FMT_FP8_E4M3) == B.DQG_ERR_UNSUPPORTED                   # T > 8
-    assert layer(1, B.FMT_FP8_E4M3 | B.PATH_NO_FUSED) == B.DQG_ERR_UNSUPPORTED
+    def layer(T, fmt, H=256, I=128):
+        return f(A, A, T, H, I, 8, 2, A, A, A, A, 32, fmt, 0, A, 0, 0, A, 1 << 40, None)
+    assert layer(16, B.FMT_FP8_E4M3, H=32768, I=65536) == B.DQG_ERR_UNSUPPORTED  # 2 H I > 2^31
     assert layer(1, 3) == B.DQG_ERR_UNSUPPORTED                                 # no format 3
-    g = B.LIB.moe_fp4_layer_from_hidden
-    assert g(A, A, 16, 256, 128, 8, 2, A, A, A, A, 32, B.FMT_FP8_E4M3, 0, A, 0, 0, 0, A,
-             1 << 30, None) == B.DQG_ERR_UNSUPPORTED
+    assert _moe(fmt=B.FMT_FP8_E4M3, H=32768, I=65536) == B.DQG_ERR_UNSUPPORTED
     d = B.LIB.packed_dequant_f32
     assert d(A, A, 64, 64, 32, 3, A, None) == B.DQG_ERR_UNSUPPORTED
 
@@ -131,13 +127,13 @@ def test_mixed_layer_validation():
     assert call(tab=0) == B.DQG_ERR_INVALID_ARG
     assert call(lg=0) == B.DQG_ERR_INVALID_ARG
     assert call(fmt=B.FMT_INT4) == B.DQG_ERR_UNSUPPORTED          # FP4 base only
-    assert call(fmt=B.FMT_FP4_E2M1 | B.PATH_NO_FUSED) == B.DQG_ERR_UNSUPPORTED
-    assert call(T=16) == B.DQG_ERR_UNSUPPORTED                    # single launch only
+    assert call(fmt=B.FMT_FP8_E4M3, T=16) == B.DQG_ERR_UNSUPPORTED
     assert call(lg=A + 2) == B.DQG_ERR_MISALIGNED
+    assert call(lg=A + 2, T=16) == B.DQG_ERR_MISALIGNED           # multi-launch calls too
     assert call(tab=A + 1) == B.DQG_ERR_MISALIGNED                # table read as words
-    assert call(cb=A) == B.DQG_ERR_UNSUPPORTED                    # FE-XC needs I >= 512
-    assert call(cb=A, I=512, T=16) == B.DQG_ERR_UNSUPPORTED       # single launch only
+    assert call(tab=A + 1, T=16) == B.DQG_ERR_MISALIGNED
     assert call(cb=A + 8, I=512) == B.DQG_ERR_MISALIGNED
+    assert call(cb=A + 8, T=16) == B.DQG_ERR_MISALIGNED
 
 
 def test_router_validation():
