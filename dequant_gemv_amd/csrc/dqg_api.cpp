@@ -19,7 +19,11 @@ using dqg::MoeArgs;
 constexpr int kMaxE = 4096;
 constexpr int kMaxK = 32;
 constexpr int kMaxTK = 65536;
-constexpr int kMfmaMinTokens = 16;  // experts with this many tokens use the matrix cores
+// Experts (and GEMV calls) with at least this many tokens use the matrix cores: a product of
+// two or more token rows with one weight matrix is a real contraction, and the matrix cores
+// take its multiply-adds off the vector ALU, which bounds the vector-ALU tiles (measured
+// best at 2 against 1, 3, 5, 9 and 16 on the batched Q30 layers and the T = 4 GEMV).
+constexpr int kMfmaMinTokens = 2;
 constexpr int kMaxSplitDown = 16;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

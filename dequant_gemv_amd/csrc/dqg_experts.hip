@@ -1178,19 +1178,14 @@ static int valu_width(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : EX_
 
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
   const dim3 grid((g.N + 127) / 128, g.S + (g.S > 1 ? 1 : 0)), block(EX_THREADS);
-  const int vt = valu_width(g.T);
+  // T = 1 on the vector-ALU tiles; more tokens on matrix-core tiles of 16 (mt = 1) or 32
+  // (mt = 2) rows per pass
   if (mt == 1)
     hipLaunchKernelGGL((gemv_ex_kernel<1, 1>), grid, block, 0, st, g);
   else if (mt == 2)
     hipLaunchKernelGGL((gemv_ex_kernel<2, 1>), grid, block, 0, st, g);
-  else if (vt == 1)
-    hipLaunchKernelGGL((gemv_ex_kernel<0, 1>), grid, block, 0, st, g);
-  else if (vt == 2)
-    hipLaunchKernelGGL((gemv_ex_kernel<0, 2>), grid, block, 0, st, g);
-  else if (vt == 4)
-    hipLaunchKernelGGL((gemv_ex_kernel<0, 4>), grid, block, 0, st, g);
   else
-    hipLaunchKernelGGL((gemv_ex_kernel<0, EX_VT>), grid, block, 0, st, g);
+    hipLaunchKernelGGL((gemv_ex_kernel<0, 1>), grid, block, 0, st, g);
   return hipGetLastError();
 }
 

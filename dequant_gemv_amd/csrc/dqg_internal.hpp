@@ -104,7 +104,7 @@ hipError_t launch_schedule(const MoeArgs& a, const float* logits, hipStream_t st
 hipError_t launch_moe_experts(const MoeArgs& a, int A, int mt, hipStream_t st);
 int ex_max_split();
 constexpr unsigned EX_SPIN_LIMIT = 1u << 16;  // polling rounds before a wait gives up
-// dense INT4 GEMV; mt = 0: vector-ALU tiles (T < 16), 1 or 2: matrix-core tiles
+// dense INT4 GEMV; mt = 0: vector-ALU tiles (T = 1), 1 or 2: matrix-core tiles
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st);
 int ex_max_split_gemv();
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,

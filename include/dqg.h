@@ -129,9 +129,9 @@ size_t moe_fp4_ffn_workspace_bytes(int T, int H, int I, int E, int k);
  *     y_{t,j} = (SiLU(g) * u) W_down[e],  [g | u] = x[t] W_gate_up[e],  e = ids[t,j],
  *   accumulated in fp32.
  * Each expert's weights are streamed once per call for up to 16 of its tokens (the
- * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 16 tokens run on bf16
- * (FP4, FP8) or fp16 (INT4) MFMA tiles, the others on vector-ALU dot2 tiles, in one launch
- * per projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16
+ * matrix-core tiles) or 4 (the vector-ALU tiles); experts with >= 2 tokens run on bf16
+ * (FP4, FP8) or fp16 (INT4) MFMA tiles, single-token experts on vector-ALU dot2 tiles, in
+ * one launch per projection.  h = SiLU(g) * u enters the down projection as a 16-bit operand, bf16
  * (FP4, FP8) or fp16 (INT4), on the multi-launch path, and in fp32 on the single-launch layer
  * (moe_fp4_layer, T <= 8).
  * Results are deterministic (fixed reduction order, no floating-point atomics).
@@ -255,8 +255,8 @@ size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
  *   x  bf16 [T, K];  w uint8 [K/2, N];  s bf16 [K/G, N];  y bf16 [T, N] out
  *   y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation.
  * x must satisfy |x| < 65504 (the INT4 tiles multiply in fp16 with fp32 accumulation;
- * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).  T >= 16
- * runs on fp16 MFMA tiles.  When the query returns a non-zero size the call splits K
+ * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).  T >= 2
+ * runs on fp16 MFMA tiles, T = 1 on vector-ALU dot2 tiles.  When the query returns a non-zero size the call splits K
  * across workgroups: pass a workspace of at least that many bytes, zero-filled before its
  * first use; every completed call leaves it zero-filled again, and one workspace serves
  * calls with any T up to the T it was sized for.  Its first int32 is an error word (bit 1:

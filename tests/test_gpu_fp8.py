@@ -187,8 +187,8 @@ def test_fp8_multi_launch_parity(T, path):
 
 @pytest.mark.parametrize("T", [40, 64])
 def test_fp8_hot_expert_takes_the_mfma_tiles(T):
-    """One expert with every token (T >= 16) runs the matrix-core body in passes of 16, the
-    others the vector-ALU body, in the same launches; then all on the vector-ALU body."""
+    """One expert with every token runs the matrix-core body in passes of 16, single-token
+    experts the vector-ALU body, in the same launches; then all on the vector-ALU body."""
     B = _b()
     cfg = FP8_BATCH.with_T(T)
     L, D = _routed(cfg, seed=T + 1, hot=5)

@@ -54,12 +54,12 @@ def test_gemv_configs(N, T):
 
 
 @pytest.mark.parametrize("T,K,N,group,use_ws", [
-    (3, 5120, 320, 128, True),     # token chunk with a missing token; 5 tiles
-    (5, 1024, 192, 32, True),      # two token chunks, G=32
+    (3, 5120, 320, 128, True),     # matrix-core tile with 13 empty rows; 5 tiles
+    (5, 1024, 192, 32, True),      # matrix-core tile, G=32
     (1, 5120, 8192, 128, False),   # no workspace: no K split
     (2, 256, 64, 128, True),       # one tile, short K
     (4, 5120, 64, 128, True),      # many K splits for one tile
-    (16, 5120, 320, 128, True),    # matrix-core tiles (T >= 16), half-full last tile
+    (16, 5120, 320, 128, True),    # one full matrix-core tile, half-full last column tile
     (40, 1024, 192, 32, True),     # matrix-core tiles, two token chunks of 32
     (20, 2048, 256, 128, False),   # matrix-core tiles, no workspace
 ])

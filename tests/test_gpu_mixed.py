@@ -161,8 +161,8 @@ def test_mixed_multi_launch_parity(name, cfg, T, path):
 
 @pytest.mark.parametrize("T", [16, 40])
 def test_hot_2bit_experts_take_the_mfma_tiles(T):
-    """An INT2 and an FE-XC expert that every token picks (T >= 16 tokens each) run the
-    matrix-core body by default; then everything on the vector-ALU body."""
+    """An INT2 and an FE-XC expert that every token picks run the matrix-core body in
+    passes of 16 by default; then everything on the vector-ALU body."""
     cfg = BATCH_CODEBOOK.with_T(T)
     seed = 3
     efmt = S.expert_formats(cfg, seed)

@@ -343,8 +343,8 @@ def _hot_layer(cfg, seed, hot=5, boost=12.0):
 
 @pytest.mark.parametrize("T", [16, 40, 64])
 def test_moe_hot_expert_uses_mfma_tiles(T):
-    """One expert with T >= 16 tokens takes the MFMA tiles by default (chunks of 32 tokens
-    at T = 40, 64); the other experts stay on the vector-ALU tiles."""
+    """One expert with all T tokens takes several 16-row MFMA passes by default, next to
+    experts with one token on the vector-ALU tiles; then everything on the vector-ALU tiles."""
     cfg = S.Q30_BATCH.with_T(T)
     L, D = _hot_layer(cfg, seed=T)
     want, oids, _ = _oracle_layer(cfg, L)
