@@ -136,11 +136,16 @@ MoePlan plan_moe(int T, int H, int I, int E, int k, size_t ws_bytes = 0) {
   }
   const int a_est = expected_active(T, E, k);
   const double gu_bytes = (double)a_est * H * I * 1.125, dn_bytes = gu_bytes / 2;
-  // blocks (16 byte rows) per workgroup: 8 for gate_up, 32 for down -- measured best over
-  // T = 4 .. 64 and the 128- and 512-expert shapes (smaller batches raise the partial
-  // traffic and the finisher work; down needs no K split at all for I <= 1024)
-  p.S_gu = std::min(pick_ex_split(H / 32, 8, dqg::ex_max_split(), gu_bytes, 8.0 * p.TK * I),
-                    p.sgu_max);
+  // gate_up: no K split when the unsplit grid (active experts x column tiles) already gives
+  // every compute unit 1.5 workgroups -- the partials and their finisher then cost more than
+  // the parallelism they add; otherwise splits of 16 blocks (32 K indices each).  Down: 32
+  // blocks per split (no split at all for I <= 1024).  Measured over T = 4 .. 64 on the
+  // 128- and 512-expert shapes, FP4 and FP8 (4, 8, 16, 32 and 64 blocks per split).
+  const bool wide_gu = (long long)a_est * p.tiles_gu >= 384;
+  p.S_gu = wide_gu ? 1
+                   : std::min(pick_ex_split(H / 32, 16, dqg::ex_max_split(), gu_bytes,
+                                            8.0 * p.TK * I),
+                              p.sgu_max);
   p.S_dn = std::min(pick_ex_split(I / 32, 32, kMaxSplitDown, dn_bytes, 4.0 * p.TK * H), p.sdn_max);
   return p;
 }
