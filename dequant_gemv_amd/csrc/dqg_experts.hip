@@ -606,7 +606,7 @@ __device__ __forceinline__ void compute_group(const WBlockT<FMT> (&wb)[RBW], con
 // workgroup streams a few batches (many workgroups keep the bytes in flight; fewer splits
 // keep the partial traffic low).
 // Leaves the LDS free (a barrier follows the last batch).
-template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP, int WAUX = 0>
+template <int FMT, int BODY, int MT, int NTOK, int RBW, int STEP, int WAUX = 0, bool PF = false>
 __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool col_ok,
                                               const OpSrc& src, const int* s_slot, int nch,
                                               int b0, int b1, int off, float* lds,
@@ -626,42 +626,60 @@ __device__ __forceinline__ void stream_expert(const ExpertView& v, int col, bool
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc.v[m][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  for (int bb = b0; bb < b1; bb += GB) {
-    if (bb != b0) load_group<FMT, RBW, WAUX>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
-    Window<FMT, GB, NTOK> wnd;
-    wnd.load(src, s_slot, nch, bb, b1);
-    if (bb != b0) __syncthreads();  // the previous batch is done with the window
-    wnd.store(win);
-    __syncthreads();
-    compute_group<FMT, BODY, MT, NTOK, RBW, STEP>(wa, win, off, acc, cbl);
+  if constexpr (!PF) {
+    for (int bb = b0; bb < b1; bb += GB) {
+      if (bb != b0) load_group<FMT, RBW, WAUX>(v, bb, off, STEP, b1, kg, col, col_ok, wa);
+      Window<FMT, GB, NTOK> wnd;
+      wnd.load(src, s_slot, nch, bb, b1);
+      if (bb != b0) __syncthreads();  // the previous batch is done with the window
+      wnd.store(win);
+      __syncthreads();
+      compute_group<FMT, BODY, MT, NTOK, RBW, STEP>(wa, win, off, acc, cbl);
+    }
+  } else {
+    // Double-buffered: batch g computes from `cur` while the next batch's weights load into
+    // `nxt`.  Those loads are issued after batch g's operand-window loads, so the in-order
+    // wait for the window leaves them in flight across the compute.
+    WBlockT<FMT> wb[RBW];
+    for (int bb = b0; bb < b1; bb += GB) {
+      Window<FMT, GB, NTOK> wnd;
+      wnd.load(src, s_slot, nch, bb, b1);
+      load_group<FMT, RBW, WAUX>(v, bb + GB, off, STEP, b1, kg, col, col_ok, wb);
+      if (bb != b0) __syncthreads();  // the previous batch is done with the window
+      wnd.store(win);
+      __syncthreads();
+      compute_group<FMT, BODY, MT, NTOK, RBW, STEP>(wa, win, off, acc, cbl);
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) wa[r] = wb[r];
+    }
   }
   __syncthreads();
 }
 
 // One pass of a phase: dispatch the token count (VALU: 1, 2, 4 or 8 rows; MFMA: MT tiles)
 // to a compile-time width.
-template <int FMT, int VT, int RBW, int STEP, int WAUX = 0>
+template <int FMT, int VT, int RBW, int STEP, int WAUX = 0, bool PF = false>
 __device__ __forceinline__ void stream_valu(const ExpertView& v, int col, bool col_ok,
                                             const OpSrc& src, const int* s_slot, int nch, int b0,
                                             int b1, int off, float* lds, WBlockT<FMT> (&wa)[RBW],
                                             Acc<BODY_VALU, VT>& acc, const uint4* cbl = nullptr) {
   if (VT <= 1 || nch <= 1)
-    stream_expert<FMT, BODY_VALU, VT, 1, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
-                                                          b1, off, lds, wa, acc, cbl);
+    stream_expert<FMT, BODY_VALU, VT, 1, RBW, STEP, WAUX, PF>(v, col, col_ok, src, s_slot, nch,
+                                                              b0, b1, off, lds, wa, acc, cbl);
   else if (VT <= 2 || nch <= 2)
-    stream_expert<FMT, BODY_VALU, VT, (VT < 2 ? VT : 2), RBW, STEP, WAUX>(
+    stream_expert<FMT, BODY_VALU, VT, (VT < 2 ? VT : 2), RBW, STEP, WAUX, PF>(
         v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc, cbl);
   else if (VT <= 4 || nch <= 4)
-    stream_expert<FMT, BODY_VALU, VT, (VT < 4 ? VT : 4), RBW, STEP, WAUX>(
+    stream_expert<FMT, BODY_VALU, VT, (VT < 4 ? VT : 4), RBW, STEP, WAUX, PF>(
         v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc, cbl);
   else
-    stream_expert<FMT, BODY_VALU, VT, VT, RBW, STEP, WAUX>(v, col, col_ok, src, s_slot, nch, b0,
-                                                           b1, off, lds, wa, acc, cbl);
+    stream_expert<FMT, BODY_VALU, VT, VT, RBW, STEP, WAUX, PF>(v, col, col_ok, src, s_slot, nch,
+                                                               b0, b1, off, lds, wa, acc, cbl);
 }
 
 // One pass of a phase in weight format F: the first batch's weights load while the pass's
 // slot list is fetched into LDS, then the stream (matrix-core or vector-ALU body).
-template <int F, int BODY, int MT, int RBW, int STEP>
+template <int F, int BODY, int MT, int RBW, int STEP, bool PF>
 __device__ __forceinline__ void run_pass(const MoeArgs& a, const ExpertView& v, int col,
                                          bool col_ok, const OpSrc& src, int* s_slot, int first,
                                          int nch, int b0, int b1, int off, float* lds,
@@ -672,11 +690,11 @@ __device__ __forceinline__ void run_pass(const MoeArgs& a, const ExpertView& v, 
   if ((int)threadIdx.x < nch) s_slot[threadIdx.x] = slot_at(a, first + threadIdx.x);
   __syncthreads();
   if constexpr (BODY == BODY_MFMA)
-    stream_expert<F, BODY_MFMA, MT, 16 * MT, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0,
-                                                        b1, off, lds, wa, acc, cbl);
+    stream_expert<F, BODY_MFMA, MT, 16 * MT, RBW, STEP, 0, PF>(
+        v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc, cbl);
   else
-    stream_valu<F, MT, RBW, STEP>(v, col, col_ok, src, s_slot, nch, b0, b1, off, lds, wa, acc,
-                                  cbl);
+    stream_valu<F, MT, RBW, STEP, 0, PF>(v, col, col_ok, src, s_slot, nch, b0, b1, off,
+                                                  lds, wa, acc, cbl);
 }
 
 // The weight format of expert e in a kernel of base format FMT: with a per-expert table
@@ -701,7 +719,7 @@ __device__ __forceinline__ void stage_codebooks(const MoeArgs& a, int e, int m, 
 }
 
 // A pass in the expert's format: FMT, or (MIX) the 2-bit formats of a mixed layer.
-template <int FMT, bool MIX, int BODY, int MT, int RBW, int STEP>
+template <int FMT, bool MIX, int BODY, int MT, int RBW, int STEP, bool PF>
 __device__ __forceinline__ void run_pass_fmt(int ef, const MoeArgs& a, const uint8_t* w,
                                              const uint16_t* sc, int e, int K, size_t ld,
                                              int col, bool col_ok, const OpSrc& src,
@@ -711,19 +729,19 @@ __device__ __forceinline__ void run_pass_fmt(int ef, const MoeArgs& a, const uin
   const int slab = K / fmt_kb(FMT);
   if constexpr (MIX) {
     if (ef == FMT_INT2) {
-      run_pass<FMT_INT2, BODY, MT, RBW, STEP>(
+      run_pass<FMT_INT2, BODY, MT, RBW, STEP, PF>(
           a, expert_view<FMT_INT2>(w, sc, e, K, slab, ld, a.group), col, col_ok, src, s_slot,
           first, nch, b0, b1, off, lds, cbl, acc);
       return;
     }
     if (ef == FMT_FEXC) {
-      run_pass<FMT_FEXC, BODY, MT, RBW, STEP>(
+      run_pass<FMT_FEXC, BODY, MT, RBW, STEP, PF>(
           a, expert_view<FMT_FEXC>(w, sc, e, K, slab, ld, a.group), col, col_ok, src, s_slot,
           first, nch, b0, b1, off, lds, cbl, acc);
       return;
     }
   }
-  run_pass<FMT, BODY, MT, RBW, STEP>(a, expert_view<FMT>(w, sc, e, K, slab, ld, a.group), col,
+  run_pass<FMT, BODY, MT, RBW, STEP, PF>(a, expert_view<FMT>(w, sc, e, K, slab, ld, a.group), col,
                                      col_ok, src, s_slot, first, nch, b0, b1, off, lds, cbl, acc);
 }
 
@@ -749,7 +767,8 @@ __device__ __forceinline__ void store_h4(uint16_t* hop, size_t idx, float4 g, fl
 // gate_up + SiLU*up.  Grid: x = 128-column h tile, y = K split, z = active-expert index.
 // Waves: w & 1 = gate (0) or up (1) columns, w >> 1 = even or odd blocks of each group.
 // ======================================================================================
-template <int FMT, int MT, int VT, bool MIX>
+// PF: double-buffered weights (for unsplit launches, whose workgroups walk all of K)
+template <int FMT, int MT, int VT, bool MIX, bool PF>
 __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
   constexpr int TS = VT < 4 ? VT : 4;  // token slots of the vector-ALU reduction
   __shared__ __align__(16) float lds[ex_lds_floats(MT, VT)];
@@ -832,7 +851,7 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
     if constexpr (MT > 0) {
       if (use_mfma) {
         Acc<BODY_MFMA, MT> acc;
-        run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 2>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok,
+        run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 2, PF>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok,
                                                     src, s_slot, beg + m0, nch, b0, b1, khalf,
                                                     lds, s_cb, acc);
 #pragma unroll
@@ -861,7 +880,7 @@ __global__ void __launch_bounds__(EX_THREADS) gateup_ex_kernel(MoeArgs a) {
       }
     }
     Acc<BODY_VALU, VT> acc;
-    run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 2>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok, src,
+    run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 2, PF>(ef, a, a.wgu, a.sgu, e, H, ld, col, col_ok, src,
                                                 s_slot, beg + m0, nch, b0, b1, khalf, lds, s_cb,
                                                 acc);
     // two halves of 4 tokens: red[role][khalf][kg][token 0..3][column 0..127]
@@ -988,7 +1007,7 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
       if (use_mfma) {
       done = true;
       Acc<BODY_MFMA, MT> acc;
-      run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 4>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
+      run_pass_fmt<FMT, MIX, BODY_MFMA, MT, 2, 4, false>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
                                                   s_slot, beg + c0, nch, b0, b1, wv, lds, s_cb,
                                                   acc);
 #pragma unroll
@@ -1018,7 +1037,7 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
     }
     if (!done) {
       Acc<BODY_VALU, VT> acc;
-      run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 4>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
+      run_pass_fmt<FMT, MIX, BODY_VALU, VT, 2, 4, false>(ef, a, a.wd, a.sd, e, I, ld, col, col_ok, src,
                                                   s_slot, beg + c0, nch, b0, b1, wv, lds, s_cb,
                                                   acc);
 #pragma unroll
@@ -1195,9 +1214,15 @@ int ex_max_split_gemv() { return EX_MAX_SPLIT_GEMV; }
 template <int FMT, int MT, int VT, bool MIX>
 static hipError_t launch_phase(const MoeArgs& a, int A, bool down, hipStream_t st) {
   if (!down) {
-    hipLaunchKernelGGL((gateup_ex_kernel<FMT, MT, VT, MIX>),
-                       dim3((a.I + 127) / 128, a.S_gu + (a.S_gu > 1 ? 1 : 0), A),
-                       dim3(EX_THREADS), 0, st, a);
+    // unsplit gate_up workgroups stream all of K: they prefetch each next batch's weights
+    // (measured faster there, slower for the short streams of split launches)
+    const dim3 grid((a.I + 127) / 128, a.S_gu + (a.S_gu > 1 ? 1 : 0), A);
+    if (a.S_gu == 1)
+      hipLaunchKernelGGL((gateup_ex_kernel<FMT, MT, VT, MIX, true>), grid, dim3(EX_THREADS), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((gateup_ex_kernel<FMT, MT, VT, MIX, false>), grid, dim3(EX_THREADS), 0,
+                         st, a);
   } else {
     const int zc = a.combine ? (a.T + EX_COMBINE_TOKENS - 1) / EX_COMBINE_TOKENS : 0;
     hipLaunchKernelGGL((down_ex_kernel<FMT, MT, VT, MIX>), dim3((a.H + 127) / 128, a.S_dn, A + zc),
