@@ -1192,10 +1192,169 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
   }
 }
 
+// ======================================================================================
+// Dense packed INT4 GEMV for one token (FastInfer page, "Specialized matrix-vector result";
+// eole page, "Packed Marlin projections" for the fused gate/up width).
+//
+// Same grid as gemv_ex_kernel (128-column tile fastest, K split, then one finisher
+// workgroup per tile), a cheaper decode.  A lane owns 8 columns and, in each block of 16
+// byte rows, the 4 rows 4 kq .. 4 kq + 3.  Two rows r, r + 1 of one column are decoded
+// together: one v_perm_b32 puts byte c of row r in bits 0-7 and byte c of row r + 1 in bits
+// 16-23, and one and-or per nibble gives the fp16 pairs (1024 + lo_r, 1024 + lo_r+1) and
+// (64 + hi_r, 64 + hi_r+1), which meet the activation pairs (x[2r], x[2r+2]) and
+// (x[2r+1], x[2r+3]) in v_dot2_f32_f16: 1.5 decode instructions and one dot2 per byte
+// (the byte-at-a-time decode takes 3 and one).  The activations of a round of 16 blocks
+// are converted once per workgroup into that paired fp16 order in LDS, together with the
+// bias -(1032 sum x[even] + 72 sum x[odd]) of each 8 K values (n - 8 times 1024- and
+// 64-based magic pairs).  A wave sums 4 whole blocks per chunk before it applies a group
+// scale (G = 128: one scale per chunk and column; G = 32: one per block).
+// ======================================================================================
+constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
+
+template <int G>
+__global__ void __launch_bounds__(EX_THREADS) gemv_t1_kernel(GemvArgs g) {
+  __shared__ __align__(16) uint4 xs[GV_ROUND * 4];  // per 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7)
+  __shared__ float cs[GV_ROUND * 4];                 // per 8 K: the bias term
+  __shared__ __align__(16) float red[4][4][128];     // [wave][row lane][column]
+  const int K = g.K, N = g.N, S = g.S;
+  const int tiles = (N + 127) / 128;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, q = l & 15, kq = l >> 4;
+  const __amdgpu_buffer_rsrc_t pr = ex_rsrc(g.part);
+  const int Wc = tiles * S;
+  if ((int)blockIdx.x >= Wc) {  // finisher of one tile: the S split partials in split order
+    const int tile = blockIdx.x - Wc, c = tid;
+    if (c < 128 && c < N - 128 * tile) {
+      float y = 0.0f;
+      for (int p0 = 0; p0 < S; p0 += 16) {
+        int off[16];
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          off[i] = ((min(p0 + i, S - 1) * g.t_cap) * N + 128 * tile + c) * 4;
+        if (!take16(pr, off, min(16, S - p0), v) && g.err) atomicOr(g.err, 2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (p0 + i < S) y += v[i];
+      }
+      g.y[128 * tile + c] = f32_to_bf16(y + 0.0f);  // -0.0 sums become +0.0
+    }
+    return;
+  }
+  const int tile = blockIdx.x % tiles, s = blockIdx.x / tiles;
+  const int nblk = K / 32;
+  const int blk0 = s * g.wb, blk1 = min(blk0 + g.wb, nblk);
+  const int ncols = min(128, N - 128 * tile);
+  const int col = 128 * tile + 8 * q;
+  const bool col_ok = 8 * q < ncols;
+  const __amdgpu_buffer_rsrc_t wr = view_rsrc(g.w, (size_t)(K / 2) * N);
+  const __amdgpu_buffer_rsrc_t sr = view_rsrc(g.s, (size_t)(K / G) * N * 2);
+  constexpr int NS = G == 128 ? 1 : 4;  // scale loads per chunk
+  uint2 w[16];
+  uint4 sc[NS];
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  // fp16 constants kept in registers so that each nibble takes one v_and_or_b32
+  uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, F_LO = 0x64006400u, F_HI = 0x54005400u;
+  asm volatile("" : "+s"(M_LO), "+s"(M_HI), "+v"(F_LO), "+v"(F_HI));
+  for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
+    const int cb = r0 + 4 * wv;  // the wave's 4 blocks of this round
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = (col_ok && cb + j < blk1) ? (16 * (cb + j) + 4 * kq) * N + col : EX_OOB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wr, o, r * N, EX_STREAM);
+        w[4 * j + r] = make_uint2(d.x, d.y);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int o = (col_ok && cb + j < blk1) ? ((32 * (cb + j) / G) * N + col) * 2 : EX_OOB;
+      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, EX_STREAM);
+      sc[j] = make_uint4(d.x, d.y, d.z, d.w);
+    }
+    if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
+    if (tid < GV_ROUND * 4) {  // one group of 8 K values per thread; zero past the range
+      const int k0 = 32 * r0 + 8 * tid;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k0 < 32 * blk1) v = *reinterpret_cast<const uint4*>(g.x + k0);
+      const uint32_t h01 = bf16pair_to_f16pair(v.x), h23 = bf16pair_to_f16pair(v.y);
+      const uint32_t h45 = bf16pair_to_f16pair(v.z), h67 = bf16pair_to_f16pair(v.w);
+      const uint32_t e0 = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+      const uint32_t o0 = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+      const uint32_t e1 = __builtin_amdgcn_perm(h67, h45, 0x05040100u);
+      const uint32_t o1 = __builtin_amdgcn_perm(h67, h45, 0x07060302u);
+      xs[tid] = make_uint4(e0, o0, e1, o1);
+      const uint32_t m1032 = 0xE408E408u, m72 = 0xD480D480u;  // fp16 (-1032, -1032), (-72, -72)
+      float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
+      c = dot2p<FMT_INT4>(o0, m72, c);
+      c = dot2p<FMT_INT4>(e1, m1032, c);
+      cs[tid] = dot2p<FMT_INT4>(o1, m72, c);
+    }
+    __syncthreads();
+    float d[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gi = (4 * wv + j) * 4 + kq;  // the lane's 8 K values of block cb + j
+      const uint4 xv = xs[gi];
+      const float cc = cs[gi];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = (G == 128 && j > 0) ? d[i] + cc : cc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
+          const uint32_t p = __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+          const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
+          d[i] = dot2p<FMT_INT4>(lo, pp == 0 ? xv.x : xv.z, d[i]);
+          d[i] = dot2p<FMT_INT4>(hi, pp == 0 ? xv.y : xv.w, d[i]);
+        }
+      }
+      if (G != 128 || j == 3) {
+        float sf[8];
+        scales8(sc[G == 128 ? 0 : j], sf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(sf[i], d[i], acc[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wv][kq][8 * q + i] = acc[i];
+  __syncthreads();
+  if (tid < ncols) {
+    float v = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][tid];
+    if (S == 1)
+      g.y[128 * tile + tid] = f32_to_bf16(v + 0.0f);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pub1(v)), pr,
+                                            ((s * g.t_cap) * N + 128 * tile + tid) * 4, 0,
+                                            EX_CPOL_SC1);
+  }
+}
+
 // tokens per vector-ALU pass for calls with T tokens (no expert has more than T)
 static int valu_width(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : EX_VT; }
 
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
+  if (mt == 0 && g.T == 1) {
+    // one token: whole rounds of GV_ROUND blocks per split, at most the plan's S splits
+    GemvArgs h = g;
+    const int nblk = g.K / 32, tiles = (g.N + 127) / 128;
+    const int per = (nblk + g.S - 1) / g.S;
+    h.wb = GV_ROUND * ((per + GV_ROUND - 1) / GV_ROUND);
+    h.S = (nblk + h.wb - 1) / h.wb;
+    const dim3 grid1(tiles * h.S + (h.S > 1 ? tiles : 0));
+    if (g.group == 128)
+      hipLaunchKernelGGL((gemv_t1_kernel<128>), grid1, dim3(EX_THREADS), 0, st, h);
+    else
+      hipLaunchKernelGGL((gemv_t1_kernel<32>), grid1, dim3(EX_THREADS), 0, st, h);
+    return hipGetLastError();
+  }
   const dim3 grid((g.N + 127) / 128, g.S + (g.S > 1 ? 1 : 0)), block(EX_THREADS);
   // T = 1 on the vector-ALU tiles; more tokens on matrix-core tiles of 16 (mt = 1) or 32
   // (mt = 2) rows per pass

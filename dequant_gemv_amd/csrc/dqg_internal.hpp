@@ -51,6 +51,7 @@ struct GemvArgs {
   float* part;          // [S_max, t_cap, N] split partials (S > 1; zero between calls)
   int t_cap;            // tokens of the workspace's capacity: the partials' split stride
   int S;
+  int wb;               // blocks (32 K) per K split of the one-token kernel (set by the launcher)
   int* err;             // error word (bit 1: a wait gave up), may be null
 };
 

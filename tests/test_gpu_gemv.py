@@ -62,6 +62,12 @@ def test_gemv_configs(N, T):
     (16, 5120, 320, 128, True),    # one full matrix-core tile, half-full last column tile
     (40, 1024, 192, 32, True),     # matrix-core tiles, two token chunks of 32
     (20, 2048, 256, 128, False),   # matrix-core tiles, no workspace
+    (1, 5120, 320, 128, True),     # one token: 3 column tiles, the last half full
+    (1, 1024, 192, 32, True),      # one token, G=32 (a scale per block)
+    (1, 96, 64, 32, True),         # one token, 3 blocks: a partial chunk, one tile of 64
+    (1, 384, 128, 128, True),      # one token, 12 blocks: the last wave's chunk is empty
+    (1, 2048, 64, 32, False),      # one token, no workspace: 4 rounds in one workgroup
+    (1, 65536, 64, 128, True),     # one token, the largest K
 ])
 def test_gemv_ragged(T, K, N, group, use_ws):
     g = S.make_gemv(S.GemvConfig("r", T=T, K=K, N=N, group=group), seed=3)
@@ -95,6 +101,26 @@ def test_gemv_one_hot_rows_exact(rows):
     Wd = O.dequant(w, s, G, O.FMT_INT4)
     want = S.f32_to_bf16_bits(Wd[rows].astype(np.float32))
     assert np.array_equal(bits16(y), want)
+
+
+@pytest.mark.parametrize("group", [128, 32])
+def test_gemv_one_token_one_hot_rows_exact(group):
+    """One token, x = e_k with power-of-two scales: y must equal row k of W exactly (the
+    paired-row decode and its bias term cancel exactly for a single nonzero activation)."""
+    rng = np.random.default_rng(6)
+    K, N = 5120, 320
+    w = rng.integers(0, 256, size=(K // 2, N), dtype=np.uint8)
+    s = ((rng.integers(-8, 4, size=(K // group, N)) + 127).astype(np.uint32) << 7).astype(np.uint16)
+    B = _b()
+    ws = B.gemv_workspace(1, K, N, group, "cuda")
+    Wd = O.dequant(w, s, group, O.FMT_INT4)
+    for k in (0, 1, 2, 3, 31, 32, 127, 128, 129, 2559, 2560, 5118, 5119):
+        x = np.zeros((1, K), np.uint16)
+        x[0, k] = 0x3F80
+        y = B.packed_gemv_int4(dev(x), dev(w), dev(s), group, workspace=ws)
+        torch.cuda.synchronize()
+        want = S.f32_to_bf16_bits(Wd[[k]].astype(np.float32))
+        assert np.array_equal(bits16(y), want), f"row {k}"
 
 
 def test_gemv_deterministic_and_workspace_reusable():
