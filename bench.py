@@ -82,7 +82,7 @@ DEFAULT_WORKLOAD = "q30_moe_layer_t1"
 KERNEL_SOURCES = {
     "fused_layer_kernel": ("dqg_fused.hip", "dqg_device.hpp", "dqg_internal.hpp"),
     "gemv_ex_kernel": ("dqg_experts.hip", "dqg_device.hpp", "dqg_internal.hpp"),
-    "gemv_t1_kernel": ("dqg_experts.hip", "dqg_device.hpp", "dqg_internal.hpp"),
+    "gemv_tok_kernel": ("dqg_experts.hip", "dqg_device.hpp", "dqg_internal.hpp"),
     "moe_layer_multi_launch": ("dqg_kernels.hip", "dqg_experts.hip", "dqg_device.hpp",
                                "dqg_internal.hpp"),
 }
@@ -651,8 +651,9 @@ def bench_gemv(w, args, dev, stream, B):
         raise SystemExit(f"bench: timed GEMV outside the tolerance ({ratio:.3f})")
     abytes = (K // 2) * N + (K // G) * N * 2
     gbps = abytes / (us * 1e-6) / 1e9
-    # one token runs the paired-row kernel, more tokens the expert tiles' E = 1 case
-    kernel = "gemv_t1_kernel" if T == 1 else "gemv_ex_kernel"
+    # one or two tokens run the paired-row vector-ALU kernel, more tokens the matrix-core
+    # tiles of the expert kernels' E = 1 case
+    kernel = "gemv_tok_kernel" if T <= 2 else "gemv_ex_kernel"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "traffic": read_traffic(kernel, args.workload), "bytes_per_launch": abytes,

@@ -1070,17 +1070,17 @@ __global__ void __launch_bounds__(EX_THREADS) down_ex_kernel(MoeArgs a) {
 }
 
 // ======================================================================================
-// dense packed INT4 GEMV: y [T, N] = x [T, K] W, the E = 1 case of the expert tiles.
-// Grid: x = 128-column tile, y = K split; wave w takes blocks g0 + w + 4 r.  Splits are
-// summed by the last workgroup of a tile, in split order, which also resets the counter.
-// (FastInfer page, "Specialized matrix-vector result": a single-row matrix-vector product
-// over contiguous stored weights with fp32 reductions; here the weights are packed 4-bit
-// codes decoded in registers.)
+// dense packed INT4 GEMV for three or more tokens: y [T, N] = x [T, K] W on matrix-core tiles,
+// the E = 1 case of the expert tiles.  Grid: x = 128-column tile, y = K split (+ one finisher
+// row); wave w takes blocks g0 + w + 4 r.  Split partials are summed in split order by the
+// finisher row.  (FastInfer page, "Specialized matrix-vector result": a matrix-vector
+// product over contiguous stored weights with fp32 reductions; here the weights are packed
+// 4-bit codes decoded in registers.)  One or two tokens run gemv_tok_kernel.
 // ======================================================================================
 template <int MT, int VT>
 __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
+  static_assert(MT > 0, "one or two tokens run gemv_tok_kernel");
   constexpr int FMT = FMT_INT4;
-  constexpr int TS = VT < 4 ? VT : 4;  // token slots of the vector-ALU reduction
   __shared__ __align__(16) float lds[ex_lds_floats(MT, VT)];
   __shared__ int s_slot[EX_MAXCH];
   const int T = g.T, K = g.K, N = g.N;
@@ -1162,103 +1162,81 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
         }
         __syncthreads();
       }
-    } else {
-      Acc<BODY_VALU, VT> acc;
-      stream_valu<FMT, VT, 2, 4, EX_STREAM>(v, col, col_ok, src, s_slot, nch, b0, b1, wv, lds, wa,
-                                       acc);
-#pragma unroll
-      for (int hh = 0; hh < (VT + 3) / 4; ++hh) {
-        if (4 * hh >= nch) break;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (4 * hh + t < VT)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              lds[(((wv * 4 + kg) * TS + t) * 128) + 8 * q + i] = acc.v[4 * hh + t][i];
-        __syncthreads();
-        if (tid < TS * 32) {
-          const int t = tid >> 5, c4 = 4 * (tid & 31);
-          if (4 * hh + t < nch && c4 < ncols) {
-            const float4* r4 = reinterpret_cast<const float4*>(lds);
-            float4 y = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-            for (int p = 0; p < 16; ++p) y = f4_add(y, r4[((p * TS + t) * 128 + c4) / 4]);
-            emit(c0 + 4 * hh + t, c4, y);
-          }
-        }
-        __syncthreads();
-      }
     }
   }
 }
 
 // ======================================================================================
-// Dense packed INT4 GEMV for one token (FastInfer page, "Specialized matrix-vector result";
-// eole page, "Packed Marlin projections" for the fused gate/up width).
+// Dense packed INT4 GEMV for one or two tokens, on the vector ALUs (FastInfer page,
+// "Specialized matrix-vector result"; eole page, "Packed Marlin projections" for the fused
+// gate/up width).
 //
-// Same grid as gemv_ex_kernel (128-column tile fastest, K split, then one finisher
-// workgroup per tile), a cheaper decode.  A lane owns 8 columns and, in each block of 16
-// byte rows, the 4 rows 4 kq .. 4 kq + 3.  Two rows r, r + 1 of one column are decoded
-// together: one v_perm_b32 puts byte c of row r in bits 0-7 and byte c of row r + 1 in bits
-// 16-23, and one and-or per nibble gives the fp16 pairs (1024 + lo_r, 1024 + lo_r+1) and
-// (64 + hi_r, 64 + hi_r+1), which meet the activation pairs (x[2r], x[2r+2]) and
-// (x[2r+1], x[2r+3]) in v_dot2_f32_f16: 1.5 decode instructions and one dot2 per byte
-// (the byte-at-a-time decode takes 3 and one).  The activations of a round of 16 blocks
-// are converted once per workgroup into that paired fp16 order in LDS, together with the
-// bias -(1032 sum x[even] + 72 sum x[odd]) of each 8 K values (n - 8 times 1024- and
-// 64-based magic pairs).  A wave sums 4 whole blocks per chunk before it applies a group
-// scale (G = 128: one scale per chunk and column; G = 32: one per block).
+// Grid: 128-column tile fastest, then the K split, then one finisher workgroup per tile.  A
+// lane owns 8 columns and, in each block of 16 byte rows, the 4 rows 4 kq .. 4 kq + 3; a wave
+// takes 4 consecutive blocks of each round of 16.  Two rows r, r + 1 of one column are
+// decoded together: one v_perm_b32 puts byte c of row r in bits 0-7 and byte c of row r + 1
+// in bits 16-23, and one and-or per nibble gives the fp16 pairs (1024 + lo_r, 1024 + lo_r+1)
+// and (64 + hi_r, 64 + hi_r+1), which meet the activation pairs (x[2r], x[2r+2]) and
+// (x[2r+1], x[2r+3]) in v_dot2_f32_f16: 1.5 decode instructions and one dot2 per byte (the
+// byte-at-a-time decode takes 3 and one).  The activations of a round are converted once per
+// workgroup into that paired fp16 order in LDS, with the bias -(1032 sum x[even] + 72 sum
+// x[odd]) of each 8 K values (n - 8 against the 1024- and 64-based magic pairs).  A wave sums
+// its 4 blocks before it applies the group scale (G = 128: one per chunk and column; G = 32:
+// one per block).  Two tokens share a pass: each decoded pair meets both tokens' activations.
 // ======================================================================================
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
+constexpr int GV_MAX_RP = 2;  // tokens per pass, at most
+constexpr int GV_MAX_T = 2;   // tokens of the vector-ALU GEMV (more take matrix cores)
 
-template <int G>
-__global__ void __launch_bounds__(EX_THREADS) gemv_t1_kernel(GemvArgs g) {
-  __shared__ __align__(16) uint4 xs[GV_ROUND * 4];  // per 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7)
-  __shared__ float cs[GV_ROUND * 4];                 // per 8 K: the bias term
-  __shared__ __align__(16) float red[4][4][128];     // [wave][row lane][column]
-  const int K = g.K, N = g.N, S = g.S;
+template <int G, int RP>
+__global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
+  // activations of a round, per token and 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7) and the bias
+  __shared__ __align__(16) uint4 xs[GV_MAX_T + 1][GV_ROUND * 4];
+  __shared__ float cs[GV_MAX_T + 1][GV_ROUND * 4];
+  __shared__ __align__(16) float red[4][4][RP][128];     // [wave][row lane][token][column]
+  const int T = g.T, K = g.K, N = g.N, S = g.S, Tc = g.t_cap;
   const int tiles = (N + 127) / 128;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, q = l & 15, kq = l >> 4;
   const __amdgpu_buffer_rsrc_t pr = ex_rsrc(g.part);
   const int Wc = tiles * S;
   if ((int)blockIdx.x >= Wc) {  // finisher of one tile: the S split partials in split order
-    const int tile = blockIdx.x - Wc, c = tid;
-    if (c < 128 && c < N - 128 * tile) {
+    const int tile = blockIdx.x - Wc;
+    const int ncols = min(128, N - 128 * tile);
+    for (int it = tid; it < T * 128; it += EX_THREADS) {
+      const int t = it >> 7, c = it & 127;
+      if (c >= ncols) continue;
       float y = 0.0f;
       for (int p0 = 0; p0 < S; p0 += 16) {
         int off[16];
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          off[i] = ((min(p0 + i, S - 1) * g.t_cap) * N + 128 * tile + c) * 4;
+          off[i] = ((min(p0 + i, S - 1) * Tc + t) * N + 128 * tile + c) * 4;
         if (!take16(pr, off, min(16, S - p0), v) && g.err) atomicOr(g.err, 2);
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (p0 + i < S) y += v[i];
       }
-      g.y[128 * tile + c] = f32_to_bf16(y + 0.0f);  // -0.0 sums become +0.0
+      g.y[(size_t)t * N + 128 * tile + c] = f32_to_bf16(y + 0.0f);  // -0.0 sums become +0.0
     }
     return;
   }
   const int tile = blockIdx.x % tiles, s = blockIdx.x / tiles;
   const int nblk = K / 32;
   const int blk0 = s * g.wb, blk1 = min(blk0 + g.wb, nblk);
+  const bool one_round = blk1 - blk0 <= GV_ROUND;  // uniform
   const int ncols = min(128, N - 128 * tile);
   const int col = 128 * tile + 8 * q;
   const bool col_ok = 8 * q < ncols;
   const __amdgpu_buffer_rsrc_t wr = view_rsrc(g.w, (size_t)(K / 2) * N);
   const __amdgpu_buffer_rsrc_t sr = view_rsrc(g.s, (size_t)(K / G) * N * 2);
+  const __amdgpu_buffer_rsrc_t xr = view_rsrc(g.x, (size_t)T * K * 2);
   constexpr int NS = G == 128 ? 1 : 4;  // scale loads per chunk
   uint2 w[16];
   uint4 sc[NS];
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  // fp16 constants kept in registers so that each nibble takes one v_and_or_b32
-  uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, F_LO = 0x64006400u, F_HI = 0x54005400u;
-  asm volatile("" : "+s"(M_LO), "+s"(M_HI), "+v"(F_LO), "+v"(F_HI));
-  for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
-    const int cb = r0 + 4 * wv;  // the wave's 4 blocks of this round
+  // the wave's 4 blocks of the round from block r0 (blocks past blk1 load as zero)
+  auto load_round = [&](int r0) {
+    const int cb = r0 + 4 * wv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int o = (col_ok && cb + j < blk1) ? (16 * (cb + j) + 4 * kq) * N + col : EX_OOB;
@@ -1274,66 +1252,111 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_t1_kernel(GemvArgs g) {
       const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, EX_STREAM);
       sc[j] = make_uint4(d.x, d.y, d.z, d.w);
     }
-    if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
-    if (tid < GV_ROUND * 4) {  // one group of 8 K values per thread; zero past the range
-      const int k0 = 32 * r0 + 8 * tid;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (k0 < 32 * blk1) v = *reinterpret_cast<const uint4*>(g.x + k0);
-      const uint32_t h01 = bf16pair_to_f16pair(v.x), h23 = bf16pair_to_f16pair(v.y);
-      const uint32_t h45 = bf16pair_to_f16pair(v.z), h67 = bf16pair_to_f16pair(v.w);
-      const uint32_t e0 = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
-      const uint32_t o0 = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
-      const uint32_t e1 = __builtin_amdgcn_perm(h67, h45, 0x05040100u);
-      const uint32_t o1 = __builtin_amdgcn_perm(h67, h45, 0x07060302u);
-      xs[tid] = make_uint4(e0, o0, e1, o1);
-      const uint32_t m1032 = 0xE408E408u, m72 = 0xD480D480u;  // fp16 (-1032, -1032), (-72, -72)
-      float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
-      c = dot2p<FMT_INT4>(o0, m72, c);
-      c = dot2p<FMT_INT4>(e1, m1032, c);
-      cs[tid] = dot2p<FMT_INT4>(o1, m72, c);
-    }
-    __syncthreads();
-    float d[8];
+  };
+  if (one_round) load_round(blk0);
+  // fp16 constants kept in registers so that each nibble takes one v_and_or_b32
+  uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, F_LO = 0x64006400u, F_HI = 0x54005400u;
+  asm volatile("" : "+s"(M_LO), "+s"(M_HI), "+v"(F_LO), "+v"(F_HI));
+  // A split of one round stages every token's activations once and keeps its weights in
+  // registers across passes; a split of several rounds reloads both per round.
+  for (int t0 = 0; t0 < T; t0 += RP) {
+    float acc[RP][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gi = (4 * wv + j) * 4 + kq;  // the lane's 8 K values of block cb + j
-      const uint4 xv = xs[gi];
-      const float cc = cs[gi];
+    for (int tt = 0; tt < RP; ++tt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) d[i] = (G == 128 && j > 0) ? d[i] + cc : cc;
+      for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
+    for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
+      if (!one_round) load_round(r0);
+      if (t0 != 0) __syncthreads();  // the previous pass's reduction is done with red
+      if (!one_round || t0 == 0) {
+        if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
+        const int ta = one_round ? 0 : t0, nt = one_round ? T : min(RP, T - t0);
+        for (int it = tid; it < nt * GV_ROUND * 4; it += EX_THREADS) {
+          const int tt = it / (GV_ROUND * 4), gi = it - tt * (GV_ROUND * 4);
+          const int k0 = 32 * r0 + 8 * gi;
+          const int xo = k0 < 32 * blk1 ? ((ta + tt) * K + k0) * 2 : EX_OOB;
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0);  // zero past
+          const uint32_t h01 = bf16pair_to_f16pair(v.x), h23 = bf16pair_to_f16pair(v.y);
+          const uint32_t h45 = bf16pair_to_f16pair(v.z), h67 = bf16pair_to_f16pair(v.w);
+          const uint32_t e0 = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+          const uint32_t o0 = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+          const uint32_t e1 = __builtin_amdgcn_perm(h67, h45, 0x05040100u);
+          const uint32_t o1 = __builtin_amdgcn_perm(h67, h45, 0x07060302u);
+          xs[tt][gi] = make_uint4(e0, o0, e1, o1);
+          const uint32_t m1032 = 0xE408E408u, m72 = 0xD480D480u;  // fp16 (-1032, -1032), (-72, -72)
+          float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
+          c = dot2p<FMT_INT4>(o0, m72, c);
+          c = dot2p<FMT_INT4>(e1, m1032, c);
+          cs[tt][gi] = dot2p<FMT_INT4>(o1, m72, c);
+        }
+        // a pass past T (T odd) reads the zeroed row GV_MAX_T
+        if (tid < GV_ROUND * 4) {
+          xs[GV_MAX_T][tid] = make_uint4(0u, 0u, 0u, 0u);
+          cs[GV_MAX_T][tid] = 0.0f;
+        }
+        __syncthreads();
+      }
+      int xt[RP];  // the pass's tokens' LDS rows (past T: the zero row)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
+      for (int tt = 0; tt < RP; ++tt)
+        xt[tt] = t0 + tt >= T ? GV_MAX_T : (one_round ? t0 + tt : tt);
+      float d[RP][8];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
-          const uint32_t p = __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
-          const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
-          d[i] = dot2p<FMT_INT4>(lo, pp == 0 ? xv.x : xv.z, d[i]);
-          d[i] = dot2p<FMT_INT4>(hi, pp == 0 ? xv.y : xv.w, d[i]);
+      for (int j = 0; j < 4; ++j) {
+        const int gi = (4 * wv + j) * 4 + kq;  // the lane's 8 K values of its block j
+        uint4 xv[RP];
+#pragma unroll
+        for (int tt = 0; tt < RP; ++tt) {
+          xv[tt] = xs[xt[tt]][gi];
+          const float cc = cs[xt[tt]][gi];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d[tt][i] = (G == 128 && j > 0) ? d[tt][i] + cc : cc;
+        }
+        // each pair is decoded once and meets every token of the pass
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
+            const uint32_t p =
+                __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+            const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
+#pragma unroll
+            for (int tt = 0; tt < RP; ++tt) {
+              d[tt][i] = dot2p<FMT_INT4>(lo, pp == 0 ? xv[tt].x : xv[tt].z, d[tt][i]);
+              d[tt][i] = dot2p<FMT_INT4>(hi, pp == 0 ? xv[tt].y : xv[tt].w, d[tt][i]);
+            }
+          }
+        }
+        if (G != 128 || j == 3) {
+          float sf[8];
+          scales8(sc[G == 128 ? 0 : j], sf);
+#pragma unroll
+          for (int tt = 0; tt < RP; ++tt)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[tt][i] = fmaf(sf[i], d[tt][i], acc[tt][i]);
         }
       }
-      if (G != 128 || j == 3) {
-        float sf[8];
-        scales8(sc[G == 128 ? 0 : j], sf);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(sf[i], d[i], acc[i]);
-      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[wv][kq][8 * q + i] = acc[i];
-  __syncthreads();
-  if (tid < ncols) {
-    float v = 0.0f;
+    for (int tt = 0; tt < RP; ++tt)
 #pragma unroll
-    for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][tid];
-    if (S == 1)
-      g.y[128 * tile + tid] = f32_to_bf16(v + 0.0f);
-    else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pub1(v)), pr,
-                                            ((s * g.t_cap) * N + 128 * tile + tid) * 4, 0,
-                                            EX_CPOL_SC1);
+      for (int i = 0; i < 8; ++i) red[wv][kq][tt][8 * q + i] = acc[tt][i];
+    __syncthreads();
+    for (int it = tid; it < RP * 128; it += EX_THREADS) {
+      const int tt = it >> 7, c = it & 127, t = t0 + tt;
+      if (t >= T || c >= ncols) continue;
+      float v = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][tt][c];
+      if (S == 1)
+        g.y[(size_t)t * N + 128 * tile + c] = f32_to_bf16(v + 0.0f);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pub1(v)), pr,
+                                              ((s * Tc + t) * N + 128 * tile + c) * 4, 0,
+                                              EX_CPOL_SC1);
+    }
   }
 }
 
@@ -1341,29 +1364,33 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_t1_kernel(GemvArgs g) {
 static int valu_width(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : EX_VT; }
 
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
-  if (mt == 0 && g.T == 1) {
-    // one token: whole rounds of GV_ROUND blocks per split, at most the plan's S splits
+  if (mt == 0) {
+    // vector-ALU tokens: whole rounds of GV_ROUND blocks per split, at most the plan's S
+    // splits; one token per pass for T = 1, else two
+    if (g.T > GV_MAX_T) return hipErrorInvalidValue;
     GemvArgs h = g;
     const int nblk = g.K / 32, tiles = (g.N + 127) / 128;
     const int per = (nblk + g.S - 1) / g.S;
     h.wb = GV_ROUND * ((per + GV_ROUND - 1) / GV_ROUND);
     h.S = (nblk + h.wb - 1) / h.wb;
     const dim3 grid1(tiles * h.S + (h.S > 1 ? tiles : 0));
-    if (g.group == 128)
-      hipLaunchKernelGGL((gemv_t1_kernel<128>), grid1, dim3(EX_THREADS), 0, st, h);
-    else
-      hipLaunchKernelGGL((gemv_t1_kernel<32>), grid1, dim3(EX_THREADS), 0, st, h);
+    if (g.group == 128) {
+      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<128, 1>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<128, GV_MAX_RP>), grid1, dim3(EX_THREADS), 0, st, h);
+    } else {
+      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<32, 1>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<32, GV_MAX_RP>), grid1, dim3(EX_THREADS), 0, st, h);
+    }
     return hipGetLastError();
   }
   const dim3 grid((g.N + 127) / 128, g.S + (g.S > 1 ? 1 : 0)), block(EX_THREADS);
-  // T = 1 on the vector-ALU tiles; more tokens on matrix-core tiles of 16 (mt = 1) or 32
-  // (mt = 2) rows per pass
+  // more tokens: matrix-core tiles of 16 (mt = 1) or 32 (mt = 2) rows per pass
   if (mt == 1)
     hipLaunchKernelGGL((gemv_ex_kernel<1, 1>), grid, block, 0, st, g);
   else if (mt == 2)
     hipLaunchKernelGGL((gemv_ex_kernel<2, 1>), grid, block, 0, st, g);
   else
-    hipLaunchKernelGGL((gemv_ex_kernel<0, 1>), grid, block, 0, st, g);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -68,6 +68,10 @@ def test_gemv_configs(N, T):
     (1, 384, 128, 128, True),      # one token, 12 blocks: the last wave's chunk is empty
     (1, 2048, 64, 32, False),      # one token, no workspace: 4 rounds in one workgroup
     (1, 65536, 64, 128, True),     # one token, the largest K
+    (2, 96, 64, 32, True),         # two tokens (one vector-ALU pass), a partial chunk
+    (2, 2048, 192, 32, False),     # two tokens, no workspace: 4 rounds in one workgroup
+    (2, 5120, 320, 128, True),     # two tokens, half-full last column tile
+    (3, 2048, 192, 128, True),     # three tokens: the matrix-core tiles
 ])
 def test_gemv_ragged(T, K, N, group, use_ws):
     g = S.make_gemv(S.GemvConfig("r", T=T, K=K, N=N, group=group), seed=3)
