@@ -501,3 +501,47 @@ def test_fused_layer_int4_w512_shape(T):
     assert np.array_equal(ids, oids)
     np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
     check_bf16(out, want, what=f"int4 w512 T={T}")
+
+
+# ---- multi-launch path: many tokens, 512 experts, tied logits -------------------------------
+MANY_CASES = [
+    ("tiny_t128", S.TINY.with_T(128), 0),                    # 128 tokens over 8 experts
+    ("tiny_t129", S.TINY.with_T(129), 0),                    # 129 tokens: five placement rounds
+    ("w512_t16", S.replace(S.W512, layers=1, T=16), 2),      # 512 experts: 8 keys per routing lane
+    ("q30_t9", S.Q30_BATCH.with_T(9), 3),                    # just past the single launch
+]
+
+
+@pytest.mark.parametrize("name,cfg,seed", MANY_CASES, ids=[c[0] for c in MANY_CASES])
+def test_moe_multi_launch_matches_oracle(name, cfg, seed):
+    """Ids bit-exact, weights to fp32 rounding and outputs within tolerance through the
+    schedule kernel and the expert tiles, at 8 and 512 experts."""
+    L, D = _layer(cfg, seed)
+    want, oids, ow = _oracle_layer(cfg, L)
+    out, ids, w = _run_layer(cfg, L, D)
+    assert np.array_equal(ids, oids)
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    check_bf16(out, want, what=name)
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "signed_zeros", "pairs"])
+def test_moe_multi_launch_tied_logits(kind):
+    """Tied logits on the multi-launch path: the schedule's routing keeps value descending,
+    index ascending, -0.0 equal to +0.0, so ids match the oracle bit for bit."""
+    cfg = S.Q30_BATCH.with_T(12)
+    L, D = _layer(cfg, 4)
+    lg = L.logits.copy()
+    if kind == "all_equal":
+        lg[:] = np.float32(0.25)
+    elif kind == "signed_zeros":
+        lg[:] = np.float32(-1.0)
+        lg[:, ::3] = np.float32(0.0)
+        lg[:, 1::3] = np.float32(-0.0)
+    else:
+        lg = np.round(lg * 2.0).astype(np.float32) / np.float32(2.0)  # many equal values
+    L.logits = lg
+    want, oids, ow = _oracle_layer(cfg, L)
+    out, ids, w = _run_layer(cfg, L, D)
+    assert np.array_equal(ids, oids)
+    np.testing.assert_allclose(w, ow, rtol=4e-6, atol=1e-7)
+    check_bf16(out, want, what=f"ties {kind}")
