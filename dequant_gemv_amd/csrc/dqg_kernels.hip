@@ -60,6 +60,19 @@ __host__ __device__ constexpr int sched_scratch_entries(int E) {
   return E <= 128 ? route_scratch(2) : route_scratch(8);
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4, 8 within each row of 16
+// lanes (lanes shifted in from outside the row add 0), then the last lane of row 0 into row 1
+// and of row 2 into row 3 (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // exclusive prefix sums over experts of cnt (-> pos) by wave 0 (lane l takes experts
 // [l * per, l * per + per)); with `records`, active experts also get their records.
 // Returns the number of active experts in lane 63's s_nact.
@@ -75,14 +88,7 @@ __device__ __forceinline__ void sched_scan(const MoeArgs& a, const int* cnt, int
       n += cnt[e] > 0;
     }
   }
-  int ci = c, ni = n;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int tc = __shfl_up(ci, off), tn = __shfl_up(ni, off);
-    if (lane >= off) {
-      ci += tc;
-      ni += tn;
-    }
-  }
+  const int ci = wave_incl_sum(c), ni = wave_incl_sum(n);
   int cx = ci - c, nx = ni - n;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
@@ -108,6 +114,11 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
   int* lids = chunk_ids + SCHED_THREADS;           // [SCHED_LDS_IDS] ids when TK fits
   const bool in_lds = TK <= SCHED_LDS_IDS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < E; i += SCHED_THREADS) cnt[i] = 0;
+  if (tid < 4) s_misc[tid] = 0;
+  // Routing from logits: the routing waves count their tokens' experts (always k distinct,
+  // in-range ids) as they select them, so no separate counting pass follows.
+  if (logits) __syncthreads();
 
   if (logits) {  // routing from logits, one wave per token
     const int RW = sched_route_waves(E);
@@ -138,7 +149,9 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
             a.ids_w[(size_t)t * k + lane] = e;
             a.wts_w[(size_t)t * k + lane] = w;
             if (in_lds) lids[t * k + lane] = e;
+            atomicAdd(&cnt[e], 1);
           }
+          if (lane == 0) a.ws.nvalid[t] = k;
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
             key[q][0] = key[q + 1][0];
@@ -161,33 +174,35 @@ __global__ void __launch_bounds__(SCHED_THREADS) schedule_kernel(MoeArgs a, cons
         a.ids_w[(size_t)t * k + lane] = e;
         a.wts_w[(size_t)t * k + lane] = w;
         if (in_lds) lids[t * k + lane] = e;
+        atomicAdd(&cnt[e], 1);
       }
+      if (lane == 0) a.ws.nvalid[t] = k;
     }
   } else if (in_lds) {
     for (int i = tid; i < TK; i += SCHED_THREADS) lids[i] = a.ids[i];
   }
   if (!in_lds) __threadfence_block();  // routing results are read back from memory
-  for (int i = tid; i < E; i += SCHED_THREADS) cnt[i] = 0;
-  if (tid < 4) s_misc[tid] = 0;
   __syncthreads();
   const int32_t* ids = in_lds ? lids : a.ids;
-  for (int i = tid; i < TK; i += SCHED_THREADS) {
-    const int e = ids[i];
-    if (e >= 0 && e < E)
-      atomicAdd(&cnt[e], 1);
-    else
-      s_misc[0] = 1;
-  }
-  for (int t = tid; t < T; t += SCHED_THREADS) {
-    int nv = 0;
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[t * k + j];
-      nv += (e >= 0 && e < E);
+  if (!logits) {  // given ids: count the valid ones, flag invalid ids and empty tokens
+    for (int i = tid; i < TK; i += SCHED_THREADS) {
+      const int e = ids[i];
+      if (e >= 0 && e < E)
+        atomicAdd(&cnt[e], 1);
+      else
+        s_misc[0] = 1;
     }
-    a.ws.nvalid[t] = nv;
-    if (nv == 0) s_misc[3] = 1;
+    for (int t = tid; t < T; t += SCHED_THREADS) {
+      int nv = 0;
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[t * k + j];
+        nv += (e >= 0 && e < E);
+      }
+      a.ws.nvalid[t] = nv;
+      if (nv == 0) s_misc[3] = 1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (tid == 0 && s_misc[0]) atomicOr(a.ws.err, 1);
   if (wv == 0) sched_scan(a, cnt, pos, E, true, &s_misc[1]);
   __syncthreads();
