@@ -76,6 +76,7 @@ WORKLOADS = {
     "gemv_int4_n8192_t1": dict(kind="gemv", T=1, K=5120, N=8192, group=128, copies=48),
     "gemv_int4_n8192_t4": dict(kind="gemv", T=4, K=5120, N=8192, group=128, copies=48),
     "gemv_int4_n34816_t1": dict(kind="gemv", T=1, K=5120, N=34816, group=128, copies=8),
+    "gemv_int4_n34816_t2": dict(kind="gemv", T=2, K=5120, N=34816, group=128, copies=8),
     "gemv_int4_n34816_t4": dict(kind="gemv", T=4, K=5120, N=34816, group=128, copies=8),
 }
 DEFAULT_WORKLOAD = "q30_moe_layer_t1"

@@ -1182,19 +1182,19 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // workgroup into that paired fp16 order in LDS, with the bias -(1032 sum x[even] + 72 sum
 // x[odd]) of each 8 K values (n - 8 against the 1024- and 64-based magic pairs).  A wave sums
 // its 4 blocks before it applies the group scale (G = 128: one per chunk and column; G = 32:
-// one per block).  Two tokens share a pass: each decoded pair meets both tokens' activations.
+// one per block).  With two tokens each decoded pair meets both tokens' activations.
 // ======================================================================================
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
-constexpr int GV_MAX_RP = 2;  // tokens per pass, at most
 constexpr int GV_MAX_T = 2;   // tokens of the vector-ALU GEMV (more take matrix cores)
 
-template <int G, int RP>
+template <int G, int NT>
 __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   // activations of a round, per token and 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7) and the bias
-  __shared__ __align__(16) uint4 xs[GV_MAX_T + 1][GV_ROUND * 4];
-  __shared__ float cs[GV_MAX_T + 1][GV_ROUND * 4];
-  __shared__ __align__(16) float red[4][4][RP][128];     // [wave][row lane][token][column]
-  const int T = g.T, K = g.K, N = g.N, S = g.S, Tc = g.t_cap;
+  __shared__ __align__(16) uint4 xs[NT][GV_ROUND * 4];
+  __shared__ float cs[NT][GV_ROUND * 4];
+  __shared__ __align__(16) float red[4][4][NT][128];     // [wave][row lane][token][column]
+  static_assert(NT * GV_ROUND * 4 <= EX_THREADS, "one activation group per thread");
+  const int K = g.K, N = g.N, S = g.S, Tc = g.t_cap;  // g.T == NT
   const int tiles = (N + 127) / 128;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, q = l & 15, kq = l >> 4;
   const __amdgpu_buffer_rsrc_t pr = ex_rsrc(g.part);
@@ -1202,7 +1202,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   if ((int)blockIdx.x >= Wc) {  // finisher of one tile: the S split partials in split order
     const int tile = blockIdx.x - Wc;
     const int ncols = min(128, N - 128 * tile);
-    for (int it = tid; it < T * 128; it += EX_THREADS) {
+    for (int it = tid; it < NT * 128; it += EX_THREADS) {
       const int t = it >> 7, c = it & 127;
       if (c >= ncols) continue;
       float y = 0.0f;
@@ -1224,19 +1224,41 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   const int tile = blockIdx.x % tiles, s = blockIdx.x / tiles;
   const int nblk = K / 32;
   const int blk0 = s * g.wb, blk1 = min(blk0 + g.wb, nblk);
-  const bool one_round = blk1 - blk0 <= GV_ROUND;  // uniform
   const int ncols = min(128, N - 128 * tile);
   const int col = 128 * tile + 8 * q;
   const bool col_ok = 8 * q < ncols;
   const __amdgpu_buffer_rsrc_t wr = view_rsrc(g.w, (size_t)(K / 2) * N);
   const __amdgpu_buffer_rsrc_t sr = view_rsrc(g.s, (size_t)(K / G) * N * 2);
-  const __amdgpu_buffer_rsrc_t xr = view_rsrc(g.x, (size_t)T * K * 2);
+  const __amdgpu_buffer_rsrc_t xr = view_rsrc(g.x, (size_t)NT * K * 2);
   constexpr int NS = G == 128 ? 1 : 4;  // scale loads per chunk
-  uint2 w[16];
-  uint4 sc[NS];
-  // the wave's 4 blocks of the round from block r0 (blocks past blk1 load as zero)
-  auto load_round = [&](int r0) {
+  // staging: thread tid < 64 NT converts the 8 activations of group tid % 64 of token tid / 64
+  const int xt = tid / (GV_ROUND * 4), xg = tid - xt * (GV_ROUND * 4);
+  // fp16 constants kept in registers so that each nibble takes one v_and_or_b32
+  uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, F_LO = 0x64006400u, F_HI = 0x54005400u;
+  asm volatile("" : "+s"(M_LO), "+s"(M_HI), "+v"(F_LO), "+v"(F_HI));
+  float acc[NT][8];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
+  for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
+    // The round's activations are loaded before its weights: in-order completion then lets
+    // the staging threads convert them while the weights are still in flight.  Groups past
+    // the split load as zero.
+    const int k0 = 32 * r0 + 8 * xg;
+    const int xo = (xt < NT && k0 < 32 * blk1) ? (xt * K + k0) * 2 : EX_OOB;
+    const u32x4_t xv4 = __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0);
+    // the wave's scales and 4 blocks of the round (blocks past blk1 load as zero); the
+    // scales go first, so that work the compiler places on them waits for no weight
+    uint2 w[16];
+    uint4 sc[NS];
     const int cb = r0 + 4 * wv;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int o = (col_ok && cb + j < blk1) ? ((32 * (cb + j) / G) * N + col) * 2 : EX_OOB;
+      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, EX_STREAM);
+      sc[j] = make_uint4(d.x, d.y, d.z, d.w);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int o = (col_ok && cb + j < blk1) ? (16 * (cb + j) + 4 * kq) * N + col : EX_OOB;
@@ -1246,117 +1268,78 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
         w[4 * j + r] = make_uint2(d.x, d.y);
       }
     }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int o = (col_ok && cb + j < blk1) ? ((32 * (cb + j) / G) * N + col) * 2 : EX_OOB;
-      const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, EX_STREAM);
-      sc[j] = make_uint4(d.x, d.y, d.z, d.w);
+    if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
+    if (xt < NT) {  // paired fp16 order and the bias term of the 8 values
+      const uint32_t h01 = bf16pair_to_f16pair(xv4.x), h23 = bf16pair_to_f16pair(xv4.y);
+      const uint32_t h45 = bf16pair_to_f16pair(xv4.z), h67 = bf16pair_to_f16pair(xv4.w);
+      const uint32_t e0 = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+      const uint32_t o0 = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+      const uint32_t e1 = __builtin_amdgcn_perm(h67, h45, 0x05040100u);
+      const uint32_t o1 = __builtin_amdgcn_perm(h67, h45, 0x07060302u);
+      xs[xt][xg] = make_uint4(e0, o0, e1, o1);
+      const uint32_t m1032 = 0xE408E408u, m72 = 0xD480D480u;  // fp16 (-1032, -1032), (-72, -72)
+      float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
+      c = dot2p<FMT_INT4>(o0, m72, c);
+      c = dot2p<FMT_INT4>(e1, m1032, c);
+      cs[xt][xg] = dot2p<FMT_INT4>(o1, m72, c);
     }
-  };
-  if (one_round) load_round(blk0);
-  // fp16 constants kept in registers so that each nibble takes one v_and_or_b32
-  uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u, F_LO = 0x64006400u, F_HI = 0x54005400u;
-  asm volatile("" : "+s"(M_LO), "+s"(M_HI), "+v"(F_LO), "+v"(F_HI));
-  // A split of one round stages every token's activations once and keeps its weights in
-  // registers across passes; a split of several rounds reloads both per round.
-  for (int t0 = 0; t0 < T; t0 += RP) {
-    float acc[RP][8];
+    __syncthreads();
+    float d[NT][8];
 #pragma unroll
-    for (int tt = 0; tt < RP; ++tt)
+    for (int j = 0; j < 4; ++j) {
+      const int gi = (4 * wv + j) * 4 + kq;  // the lane's 8 K values of its block j
+      uint4 xv[NT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
-    for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
-      if (!one_round) load_round(r0);
-      if (t0 != 0) __syncthreads();  // the previous pass's reduction is done with red
-      if (!one_round || t0 == 0) {
-        if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
-        const int ta = one_round ? 0 : t0, nt = one_round ? T : min(RP, T - t0);
-        for (int it = tid; it < nt * GV_ROUND * 4; it += EX_THREADS) {
-          const int tt = it / (GV_ROUND * 4), gi = it - tt * (GV_ROUND * 4);
-          const int k0 = 32 * r0 + 8 * gi;
-          const int xo = k0 < 32 * blk1 ? ((ta + tt) * K + k0) * 2 : EX_OOB;
-          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0);  // zero past
-          const uint32_t h01 = bf16pair_to_f16pair(v.x), h23 = bf16pair_to_f16pair(v.y);
-          const uint32_t h45 = bf16pair_to_f16pair(v.z), h67 = bf16pair_to_f16pair(v.w);
-          const uint32_t e0 = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
-          const uint32_t o0 = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
-          const uint32_t e1 = __builtin_amdgcn_perm(h67, h45, 0x05040100u);
-          const uint32_t o1 = __builtin_amdgcn_perm(h67, h45, 0x07060302u);
-          xs[tt][gi] = make_uint4(e0, o0, e1, o1);
-          const uint32_t m1032 = 0xE408E408u, m72 = 0xD480D480u;  // fp16 (-1032, -1032), (-72, -72)
-          float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
-          c = dot2p<FMT_INT4>(o0, m72, c);
-          c = dot2p<FMT_INT4>(e1, m1032, c);
-          cs[tt][gi] = dot2p<FMT_INT4>(o1, m72, c);
-        }
-        // a pass past T (T odd) reads the zeroed row GV_MAX_T
-        if (tid < GV_ROUND * 4) {
-          xs[GV_MAX_T][tid] = make_uint4(0u, 0u, 0u, 0u);
-          cs[GV_MAX_T][tid] = 0.0f;
-        }
-        __syncthreads();
+      for (int tt = 0; tt < NT; ++tt) {
+        xv[tt] = xs[tt][gi];
+        const float cc = cs[tt][gi];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[tt][i] = (G == 128 && j > 0) ? d[tt][i] + cc : cc;
       }
-      int xt[RP];  // the pass's tokens' LDS rows (past T: the zero row)
+      // each pair is decoded once and meets every token
 #pragma unroll
-      for (int tt = 0; tt < RP; ++tt)
-        xt[tt] = t0 + tt >= T ? GV_MAX_T : (one_round ? t0 + tt : tt);
-      float d[RP][8];
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gi = (4 * wv + j) * 4 + kq;  // the lane's 8 K values of its block j
-        uint4 xv[RP];
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
+          const uint32_t p =
+              __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+          const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
 #pragma unroll
-        for (int tt = 0; tt < RP; ++tt) {
-          xv[tt] = xs[xt[tt]][gi];
-          const float cc = cs[xt[tt]][gi];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) d[tt][i] = (G == 128 && j > 0) ? d[tt][i] + cc : cc;
-        }
-        // each pair is decoded once and meets every token of the pass
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
-            const uint32_t p =
-                __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
-            const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
-#pragma unroll
-            for (int tt = 0; tt < RP; ++tt) {
-              d[tt][i] = dot2p<FMT_INT4>(lo, pp == 0 ? xv[tt].x : xv[tt].z, d[tt][i]);
-              d[tt][i] = dot2p<FMT_INT4>(hi, pp == 0 ? xv[tt].y : xv[tt].w, d[tt][i]);
-            }
+          for (int tt = 0; tt < NT; ++tt) {
+            d[tt][i] = dot2p<FMT_INT4>(lo, pp == 0 ? xv[tt].x : xv[tt].z, d[tt][i]);
+            d[tt][i] = dot2p<FMT_INT4>(hi, pp == 0 ? xv[tt].y : xv[tt].w, d[tt][i]);
           }
         }
-        if (G != 128 || j == 3) {
-          float sf[8];
-          scales8(sc[G == 128 ? 0 : j], sf);
+      }
+      if (G != 128 || j == 3) {
+        float sf[8];
+        scales8(sc[G == 128 ? 0 : j], sf);
 #pragma unroll
-          for (int tt = 0; tt < RP; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[tt][i] = fmaf(sf[i], d[tt][i], acc[tt][i]);
-        }
+          for (int i = 0; i < 8; ++i) acc[tt][i] = fmaf(sf[i], d[tt][i], acc[tt][i]);
       }
     }
+  }
 #pragma unroll
-    for (int tt = 0; tt < RP; ++tt)
+  for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[wv][kq][tt][8 * q + i] = acc[tt][i];
-    __syncthreads();
-    for (int it = tid; it < RP * 128; it += EX_THREADS) {
-      const int tt = it >> 7, c = it & 127, t = t0 + tt;
-      if (t >= T || c >= ncols) continue;
-      float v = 0.0f;
+    for (int i = 0; i < 8; ++i) red[wv][kq][tt][8 * q + i] = acc[tt][i];
+  __syncthreads();
+  for (int it = tid; it < NT * 128; it += EX_THREADS) {
+    const int t = it >> 7, c = it & 127;
+    if (c >= ncols) continue;
+    float v = 0.0f;
 #pragma unroll
-      for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][tt][c];
-      if (S == 1)
-        g.y[(size_t)t * N + 128 * tile + c] = f32_to_bf16(v + 0.0f);
-      else
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pub1(v)), pr,
-                                              ((s * Tc + t) * N + 128 * tile + c) * 4, 0,
-                                              EX_CPOL_SC1);
-    }
+    for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][t][c];
+    if (S == 1)
+      g.y[(size_t)t * N + 128 * tile + c] = f32_to_bf16(v + 0.0f);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pub1(v)), pr,
+                                            ((s * Tc + t) * N + 128 * tile + c) * 4, 0,
+                                            EX_CPOL_SC1);
   }
 }
 
@@ -1366,8 +1349,8 @@ static int valu_width(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : EX_
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
   if (mt == 0) {
     // vector-ALU tokens: whole rounds of GV_ROUND blocks per split, at most the plan's S
-    // splits; one token per pass for T = 1, else two
-    if (g.T > GV_MAX_T) return hipErrorInvalidValue;
+    // splits; one instance per token count
+    if (g.T < 1 || g.T > GV_MAX_T) return hipErrorInvalidValue;
     GemvArgs h = g;
     const int nblk = g.K / 32, tiles = (g.N + 127) / 128;
     const int per = (nblk + g.S - 1) / g.S;
@@ -1376,10 +1359,10 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
     const dim3 grid1(tiles * h.S + (h.S > 1 ? tiles : 0));
     if (g.group == 128) {
       if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<128, 1>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<128, GV_MAX_RP>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<128, 2>), grid1, dim3(EX_THREADS), 0, st, h);
     } else {
       if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<32, 1>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<32, GV_MAX_RP>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<32, 2>), grid1, dim3(EX_THREADS), 0, st, h);
     }
     return hipGetLastError();
   }
