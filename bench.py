@@ -11,7 +11,7 @@ activations, logits) are synthetic and already resident in device memory.
 
 `--workload` selects the other sizes (Q30 at T = 4, 16, 64; the 48-layer chained
 512-expert stack at T = 1, 8; a tiny INT4 layer; the dense INT4 GEMV with N = 256, 8192,
-34816 at T = 1, 4), each timed the same way.
+34816 at T = 1, 4 and N = 34816 at T = 2), each timed the same way.
 
 Prints one JSON line.  `--gpus` above 1 exits: this benchmark is single-GPU.
 """
