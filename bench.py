@@ -78,6 +78,19 @@ WORKLOADS = {
     "gemv_int4_n34816_t1": dict(kind="gemv", T=1, K=5120, N=34816, group=128, copies=8),
     "gemv_int4_n34816_t2": dict(kind="gemv", T=2, K=5120, N=34816, group=128, copies=8),
     "gemv_int4_n34816_t4": dict(kind="gemv", T=4, K=5120, N=34816, group=128, copies=8),
+    # the same GEMVs on the prepacked (tile-contiguous) weights
+    "gemv_int4_tiled_n256_t1": dict(kind="gemv", T=1, K=5120, N=256, group=128, copies=48,
+                                    tiled=True),
+    "gemv_int4_tiled_n8192_t1": dict(kind="gemv", T=1, K=5120, N=8192, group=128, copies=48,
+                                     tiled=True),
+    "gemv_int4_tiled_n8192_t4": dict(kind="gemv", T=4, K=5120, N=8192, group=128, copies=48,
+                                     tiled=True),
+    "gemv_int4_tiled_n34816_t1": dict(kind="gemv", T=1, K=5120, N=34816, group=128, copies=8,
+                                      tiled=True),
+    "gemv_int4_tiled_n34816_t2": dict(kind="gemv", T=2, K=5120, N=34816, group=128, copies=8,
+                                      tiled=True),
+    "gemv_int4_tiled_n34816_t4": dict(kind="gemv", T=4, K=5120, N=34816, group=128, copies=8,
+                                      tiled=True),
 }
 DEFAULT_WORKLOAD = "q30_moe_layer_t1"
 KERNEL_SOURCES = {
@@ -616,14 +629,26 @@ def bench_gemv(w, args, dev, stream, B):
     import numpy as np
     import torch
     T, K, N, G = w["T"], w["K"], w["N"], w["group"]
+    tiled = bool(w.get("tiled"))
     x, sets = build_gemv_workload(w, device=dev)
-    ws = B.gemv_workspace(T, K, N, G, dev)
+    if tiled:  # prepacked once, outside the timed region (weights prepared before inference)
+        for S_ in sets:
+            S_["wt"], S_["st"] = B.packed_gemv_int4_prepack(S_["w"], S_["s"], G)
+        for S_ in sets[1:]:
+            del S_["w"], S_["s"]
+        def call(S_, y, ws_):
+            B.packed_gemv_int4_tiled(x, S_["wt"], S_["st"], N, G, y=y, workspace=ws_)
+    else:
+        def call(S_, y, ws_):
+            B.packed_gemv_int4(x, S_["w"], S_["s"], G, y=y, workspace=ws_)
+    mkws = lambda: B.gemv_workspace(T, K, N, G, dev)
+    ws = mkws()
     ys = [torch.empty((T, N), dtype=torch.bfloat16, device=dev) for _ in sets]
     torch.cuda.synchronize()
 
     def one_pass():
         for S_, y in zip(sets, ys):
-            B.packed_gemv_int4(x, S_["w"], S_["s"], G, y=y, workspace=ws)
+            call(S_, y, ws)
 
     gt = GraphTimer(one_pass, stream)
     ms_per_step = gt.timed(args.steps, args.warmup)
@@ -635,8 +660,7 @@ def bench_gemv(w, args, dev, stream, B):
         raise SystemExit("bench: GEMV workspace error word set after the timed replays")
     y_e = torch.empty_like(ys[0])
     with torch.cuda.stream(stream):
-        B.packed_gemv_int4(x, sets[0]["w"], sets[0]["s"], G, y=y_e,
-                           workspace=B.gemv_workspace(T, K, N, G, dev))
+        call(sets[0], y_e, mkws())
     stream.synchronize()
     rb = ys[0].view(torch.int16).cpu().numpy().view(np.uint16)
     if not np.array_equal(rb, y_e.view(torch.int16).cpu().numpy().view(np.uint16)):
@@ -654,7 +678,8 @@ def bench_gemv(w, args, dev, stream, B):
     gbps = abytes / (us * 1e-6) / 1e9
     # one or two tokens run the paired-row vector-ALU kernel, more tokens the matrix-core
     # tiles of the expert kernels' E = 1 case
-    kernel = "gemv_tok_kernel" if T <= 2 else "gemv_ex_kernel"
+    # (prepacked weights: the same vector-ALU kernel for up to 4 tokens)
+    kernel = "gemv_tok_kernel" if (T <= 2 or tiled) else "gemv_ex_kernel"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "traffic": read_traffic(kernel, args.workload), "bytes_per_launch": abytes,
@@ -664,7 +689,7 @@ def bench_gemv(w, args, dev, stream, B):
                 "rounds_us_per_call": [{key: round(r[key] * 1000.0 / len(sets), 3) for key in r}
                                        for r in rounds]}
     config = {"workload": args.workload, "T": T, "K": K, "N": N, "group": G, "format": "int4",
-              "weight_copies": len(sets)}
+              "weight_copies": len(sets), "layout": "prepacked" if tiled else "[K/2, N]"}
     return dict(value=round(us, 3), unit="us/call", ms_per_step=ms_per_step,
                 achieved_GBps=round(gbps, 1), roofline=roofline, config=config,
                 validation={"error_word": 0, "replay_equals_eager": True,

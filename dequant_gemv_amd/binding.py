@@ -56,6 +56,9 @@ SIGNATURES = {
     "packed_gemv_int4_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "packed_gemv_int4": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_gemv_int4_noalloc": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _P]),
+    "packed_gemv_int4_prepack_sizes": (_I, [_I, _I, _I, ctypes.POINTER(_Z), ctypes.POINTER(_Z)]),
+    "packed_gemv_int4_prepack": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+    "packed_gemv_int4_tiled": (_I, [_P, _I, _I, _I, _P, _P, _I, _P, _P, _Z, _P]),
     "packed_dequant_f32": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "dqg_stream_read": (_I, [_P, _Z, _P, _P]),
 }
@@ -334,6 +337,52 @@ def packed_gemv_int4_noalloc(x, w, s, group: int, y=None, status=None) -> torch.
         _need(status, "status", 4, (1,), x.device)
     _check("packed_gemv_int4_noalloc", LIB.packed_gemv_int4_noalloc(
         _ptr(x), T, K, N, _ptr(w), _ptr(s), group, _ptr(y), _ptr(status), _stream(x)))
+    return y
+
+
+def packed_gemv_int4_prepack_sizes(K: int, N: int, group: int):
+    wb, sb = _Z(0), _Z(0)
+    _check("packed_gemv_int4_prepack_sizes",
+           LIB.packed_gemv_int4_prepack_sizes(K, N, group, ctypes.byref(wb), ctypes.byref(sb)))
+    return int(wb.value), int(sb.value)
+
+
+def packed_gemv_int4_prepack(w, s, group: int, w_tiled=None, s_tiled=None):
+    """Prepacked copies (flat uint8 weights, flat bf16 scales) of an INT4 matrix w [K/2, N]
+    and its scales s [K/G, N]; returns (w_tiled, s_tiled)."""
+    Kp, N = w.shape
+    K = 2 * Kp
+    _need(w, "w", 1)
+    _need(s, "s", 2, (K // group, N), w.device)
+    wb, sb = packed_gemv_int4_prepack_sizes(K, N, group)
+    if w_tiled is None:
+        w_tiled = torch.empty(wb, dtype=torch.uint8, device=w.device)
+    if s_tiled is None:
+        s_tiled = torch.empty(sb // 2, dtype=torch.bfloat16, device=w.device)
+    _need(w_tiled, "w_tiled", 1, (wb,), w.device)
+    _need(s_tiled, "s_tiled", 2, (sb // 2,), w.device)
+    _check("packed_gemv_int4_prepack", LIB.packed_gemv_int4_prepack(
+        _ptr(w), _ptr(s), K, N, group, _ptr(w_tiled), _ptr(s_tiled), _stream(w)))
+    return w_tiled, s_tiled
+
+
+def packed_gemv_int4_tiled(x, w_tiled, s_tiled, N: int, group: int, y=None,
+                           workspace=None) -> torch.Tensor:
+    """The GEMV of packed_gemv_int4 on prepacked weights (packed_gemv_int4_prepack); T <= 4.
+    ``workspace``: as for packed_gemv_int4 (``gemv_workspace(T, K, N, group, device)``)."""
+    T, K = x.shape
+    _need(x, "x", 2)
+    wb, sb = packed_gemv_int4_prepack_sizes(K, N, group)
+    _need(w_tiled, "w_tiled", 1, (wb,), x.device)
+    _need(s_tiled, "s_tiled", 2, (sb // 2,), x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", 2, (T, N), x.device)
+    if workspace is not None:
+        _need(workspace, "workspace", 1, None, x.device)
+    _check("packed_gemv_int4_tiled", LIB.packed_gemv_int4_tiled(
+        _ptr(x), T, K, N, _ptr(w_tiled), _ptr(s_tiled), group, _ptr(y), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(x)))
     return y
 
 

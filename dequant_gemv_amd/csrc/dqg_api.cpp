@@ -554,6 +554,56 @@ int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8
   return dqg::launch_gemv_ex(g, gp.mt, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
 }
 
+int packed_gemv_int4_prepack_sizes(int K, int N, int group, size_t* w_bytes, size_t* s_bytes) {
+  if (!w_bytes || !s_bytes) return DQG_ERR_INVALID_ARG;
+  if (K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (!gemv_sizes_ok(1, K, N, group)) return DQG_ERR_UNSUPPORTED;
+  const size_t tiles = (size_t)(N + 127) / 128;
+  *w_bytes = tiles * (size_t)K * 64;
+  *s_bytes = tiles * (size_t)(K / group) * 256;
+  return DQG_OK;
+}
+
+int packed_gemv_int4_prepack(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                             uint8_t* w_tiled, uint16_t* s_tiled, hipStream_t stream) {
+  if (!w || !s || !w_tiled || !s_tiled) return DQG_ERR_INVALID_ARG;
+  if (K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (!gemv_sizes_ok(1, K, N, group)) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(w) || !aligned16(s) || !aligned16(w_tiled) || !aligned16(s_tiled))
+    return DQG_ERR_MISALIGNED;
+  return dqg::launch_gemv_prepack(w, s, K, N, group, w_tiled, s_tiled, stream) == hipSuccess
+             ? DQG_OK
+             : DQG_ERR_HIP;
+}
+
+int packed_gemv_int4_tiled(const uint16_t* x, int T, int K, int N, const uint8_t* w_tiled,
+                           const uint16_t* s_tiled, int group, uint16_t* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !w_tiled || !s_tiled || !y) return DQG_ERR_INVALID_ARG;
+  if (T < 1 || K < 1 || N < 1) return DQG_ERR_INVALID_ARG;
+  if (T > 4 || !gemv_sizes_ok(T, K, N, group)) return DQG_ERR_UNSUPPORTED;
+  // the prepacked weights are addressed with 32-bit byte offsets
+  if ((long long)((N + 127) / 128) * K * 64 >= (1LL << 31)) return DQG_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w_tiled) || !aligned16(s_tiled) || !aligned16(y))
+    return DQG_ERR_MISALIGNED;
+  // the workspace of packed_gemv_int4 for T tokens (the same split partials and error word)
+  GemvPlan gp = plan_gemv(T, K, N, workspace ? workspace_bytes : 0);
+
+  if (gp.S > 1 && (!workspace || workspace_bytes < gp.total)) {
+    if (workspace) return DQG_ERR_WORKSPACE;
+    gp.S = 1;  // no workspace: no K split
+  }
+  if (workspace && !aligned16(workspace)) return DQG_ERR_MISALIGNED;
+  GemvArgs g{};
+  g.x = x; g.T = T; g.K = K; g.N = N; g.group = group; g.w = w_tiled; g.s = s_tiled; g.y = y;
+  g.S = gp.S; g.t_cap = gp.t_cap;
+  if (gp.S > 1) {
+    g.err = static_cast<int*>(workspace);
+    g.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 256);
+  }
+  return dqg::launch_gemv_tiled(g, stream) == hipSuccess ? DQG_OK : DQG_ERR_HIP;
+}
+
 int packed_dequant_f32(const uint8_t* w, const uint16_t* s, int K, int N, int group,
                        int format, float* out, hipStream_t stream) {
   if (!w || !s || !out) return DQG_ERR_INVALID_ARG;

@@ -1186,15 +1186,16 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // ======================================================================================
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
 constexpr int GV_MAX_T = 2;   // tokens of the vector-ALU GEMV (more take matrix cores)
+constexpr int GV_PRE_MAX_T = 4;  // tokens of the vector-ALU GEMV on prepacked weights
 
-template <int G, int NT>
+template <int G, int NT, bool PRE>
 __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   // activations of a round, per token and 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7) and the bias
   __shared__ __align__(16) uint4 xs[NT][GV_ROUND * 4];
   __shared__ float cs[NT][GV_ROUND * 4];
   __shared__ __align__(16) float red[4][4][NT][128];     // [wave][row lane][token][column]
   static_assert(NT * GV_ROUND * 4 <= EX_THREADS, "one activation group per thread");
-  const int K = g.K, N = g.N, S = g.S, Tc = g.t_cap;  // g.T == NT
+  const int K = g.K, N = g.N, S = g.S, Tc = g.t_cap;  // g.T <= NT
   const int tiles = (N + 127) / 128;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, q = l & 15, kq = l >> 4;
   const __amdgpu_buffer_rsrc_t pr = ex_rsrc(g.part);
@@ -1204,7 +1205,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
     const int ncols = min(128, N - 128 * tile);
     for (int it = tid; it < NT * 128; it += EX_THREADS) {
       const int t = it >> 7, c = it & 127;
-      if (c >= ncols) continue;
+      if (t >= g.T || c >= ncols) continue;
       float y = 0.0f;
       for (int p0 = 0; p0 < S; p0 += 16) {
         int off[16];
@@ -1227,9 +1228,11 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   const int ncols = min(128, N - 128 * tile);
   const int col = 128 * tile + 8 * q;
   const bool col_ok = 8 * q < ncols;
-  const __amdgpu_buffer_rsrc_t wr = view_rsrc(g.w, (size_t)(K / 2) * N);
-  const __amdgpu_buffer_rsrc_t sr = view_rsrc(g.s, (size_t)(K / G) * N * 2);
-  const __amdgpu_buffer_rsrc_t xr = view_rsrc(g.x, (size_t)NT * K * 2);
+  const int ld = PRE ? 128 * tiles : N;  // scale row stride
+  const __amdgpu_buffer_rsrc_t wr =
+      view_rsrc(g.w, PRE ? (size_t)tiles * K * 64 : (size_t)(K / 2) * N);
+  const __amdgpu_buffer_rsrc_t sr = view_rsrc(g.s, (size_t)(K / G) * ld * 2);
+  const __amdgpu_buffer_rsrc_t xr = view_rsrc(g.x, (size_t)g.T * K * 2);
   constexpr int NS = G == 128 ? 1 : 4;  // scale loads per chunk
   // staging: thread tid < 64 NT converts the 8 activations of group tid % 64 of token tid / 64
   const int xt = tid / (GV_ROUND * 4), xg = tid - xt * (GV_ROUND * 4);
@@ -1246,7 +1249,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
     // the staging threads convert them while the weights are still in flight.  Groups past
     // the split load as zero.
     const int k0 = 32 * r0 + 8 * xg;
-    const int xo = (xt < NT && k0 < 32 * blk1) ? (xt * K + k0) * 2 : EX_OOB;
+    const int xo = (xt < g.T && k0 < 32 * blk1) ? (xt * K + k0) * 2 : EX_OOB;
     const u32x4_t xv4 = __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0);
     // the wave's scales and 4 blocks of the round (blocks past blk1 load as zero); the
     // scales go first, so that work the compiler places on them waits for no weight
@@ -1255,17 +1258,31 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
     const int cb = r0 + 4 * wv;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int o = (col_ok && cb + j < blk1) ? ((32 * (cb + j) / G) * N + col) * 2 : EX_OOB;
+      const int o = (col_ok && cb + j < blk1) ? ((32 * (cb + j) / G) * ld + col) * 2 : EX_OOB;
       const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, EX_STREAM);
       sc[j] = make_uint4(d.x, d.y, d.z, d.w);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int o = (col_ok && cb + j < blk1) ? (16 * (cb + j) + 4 * kq) * N + col : EX_OOB;
+      if constexpr (PRE) {
+        const int b = cb + j, rd = b >> 4;  // block b of round rd
+        const int o = (col_ok && b < blk1)
+                          ? (16 * rd * tiles + tile * min(16, nblk - 16 * rd) + (b & 15)) * 2048 +
+                                16 * l
+                          : EX_OOB;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wr, o, r * N, EX_STREAM);
-        w[4 * j + r] = make_uint2(d.x, d.y);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4_t d = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 1024 * h, EX_STREAM);
+          w[4 * j + 2 * h] = make_uint2(d.x, d.y);
+          w[4 * j + 2 * h + 1] = make_uint2(d.z, d.w);
+        }
+      } else {
+        const int o = (col_ok && cb + j < blk1) ? (16 * (cb + j) + 4 * kq) * N + col : EX_OOB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x2_t d = __builtin_amdgcn_raw_buffer_load_b64(wr, o, r * N, EX_STREAM);
+          w[4 * j + r] = make_uint2(d.x, d.y);
+        }
       }
     }
     if (r0 != blk0) __syncthreads();  // the previous round is done with xs / cs
@@ -1330,7 +1347,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   __syncthreads();
   for (int it = tid; it < NT * 128; it += EX_THREADS) {
     const int t = it >> 7, c = it & 127;
-    if (c >= ncols) continue;
+    if (t >= g.T || c >= ncols) continue;
     float v = 0.0f;
 #pragma unroll
     for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][t][c];
@@ -1358,11 +1375,11 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
     h.S = (nblk + h.wb - 1) / h.wb;
     const dim3 grid1(tiles * h.S + (h.S > 1 ? tiles : 0));
     if (g.group == 128) {
-      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<128, 1>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<128, 2>), grid1, dim3(EX_THREADS), 0, st, h);
+      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<128, 1, false>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<128, 2, false>), grid1, dim3(EX_THREADS), 0, st, h);
     } else {
-      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<32, 1>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<32, 2>), grid1, dim3(EX_THREADS), 0, st, h);
+      if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<32, 1, false>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<32, 2, false>), grid1, dim3(EX_THREADS), 0, st, h);
     }
     return hipGetLastError();
   }
@@ -1378,6 +1395,79 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
 }
 
 int ex_max_split_gemv() { return EX_MAX_SPLIT_GEMV; }
+
+// the vector-ALU GEMV on the prepacked layout: 1, 2 or 4 tokens per pass (3 run the 4-token
+// instance), whole rounds per split as launch_gemv_ex
+hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st) {
+  if (g.T < 1 || g.T > GV_PRE_MAX_T) return hipErrorInvalidValue;
+  GemvArgs h = g;
+  const int nblk = g.K / 32, tiles = (g.N + 127) / 128;
+  const int per = (nblk + g.S - 1) / g.S;
+  h.wb = GV_ROUND * ((per + GV_ROUND - 1) / GV_ROUND);
+  h.S = (nblk + h.wb - 1) / h.wb;
+  const dim3 grid(tiles * h.S + (h.S > 1 ? tiles : 0)), block(EX_THREADS);
+#define DQG_GT_LAUNCH(GG, NN) \
+  hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true>), grid, block, 0, st, h)
+  if (g.group == 128) {
+    if (g.T == 1) DQG_GT_LAUNCH(128, 1);
+    else if (g.T == 2) DQG_GT_LAUNCH(128, 2);
+    else DQG_GT_LAUNCH(128, 4);
+  } else {
+    if (g.T == 1) DQG_GT_LAUNCH(32, 1);
+    else if (g.T == 2) DQG_GT_LAUNCH(32, 2);
+    else DQG_GT_LAUNCH(32, 4);
+  }
+#undef DQG_GT_LAUNCH
+  return hipGetLastError();
+}
+
+// Rearranges w [K/2, N] and s [K/G, N] into the prepacked layout that gemv_tok_kernel<.., true>
+// reads: one thread per 16-byte unit, a grid-stride loop over the weight units, then the
+// scale units.
+__global__ void __launch_bounds__(256) gemv_prepack_kernel(const uint8_t* __restrict__ w,
+                                                           const uint16_t* __restrict__ s,
+                                                           int K, int N, int G,
+                                                           uint8_t* __restrict__ wt,
+                                                           uint16_t* __restrict__ st) {
+  const int nb = K / 32, ng = K / G, tiles = (N + 127) / 128;
+  const long long nw = (long long)tiles * nb * 128, ns = (long long)tiles * ng * 16;
+  for (long long u = blockIdx.x * 256LL + threadIdx.x; u < nw + ns; u += (long long)gridDim.x * 256) {
+    if (u < nw) {
+      // unit u of the output: round st, tile t, block b of the tile (nbi blocks per tile
+      // in this round)
+      const int l = (int)(u & 63), h = (int)((u >> 6) & 1);
+      const long long ob = u >> 7;  // output block
+      const int st = (int)(ob / (16LL * tiles));
+      const int nbi = min(16, nb - 16 * st);
+      const int rem = (int)(ob - 16LL * tiles * st);
+      const int t = rem / nbi, b = 16 * st + rem % nbi;
+      const int r = 16 * b + 4 * (l >> 4) + 2 * h, c = 128 * t + 8 * (l & 15);
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (c < N) {
+        const uint2 a = *reinterpret_cast<const uint2*>(w + (size_t)r * N + c);
+        const uint2 b2 = *reinterpret_cast<const uint2*>(w + (size_t)(r + 1) * N + c);
+        v = make_uint4(a.x, a.y, b2.x, b2.y);
+      }
+      reinterpret_cast<uint4*>(wt)[u] = v;
+    } else {
+      const long long v_ = u - nw;  // 8 scales of row gr, columns c .. c + 7
+      const int gr = (int)(v_ / (16LL * tiles)), c = 8 * (int)(v_ % (16LL * tiles));
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (c < N) v = *reinterpret_cast<const uint4*>(s + (size_t)gr * N + c);
+      reinterpret_cast<uint4*>(st)[v_] = v;
+    }
+  }
+}
+
+hipError_t launch_gemv_prepack(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                               uint8_t* wt, uint16_t* st_, hipStream_t st) {
+  const long long tiles = (N + 127) / 128;
+  const long long units = tiles * (K / 32) * 128 + tiles * (K / group) * 16;
+  const long long want = (units + 255) / 256, grid = want < 65536 ? want : 65536;
+  hipLaunchKernelGGL(gemv_prepack_kernel, dim3((unsigned)grid), dim3(256), 0, st, w, s, K, N,
+                     group, wt, st_);
+  return hipGetLastError();
+}
 
 // ---- launchers --------------------------------------------------------------------------------
 template <int FMT, int MT, int VT, bool MIX>

@@ -107,6 +107,11 @@ int ex_max_split();
 constexpr unsigned EX_SPIN_LIMIT = 1u << 16;  // polling rounds before a wait gives up
 // dense INT4 GEMV; mt = 0: vector-ALU tiles (T = 1), 1 or 2: matrix-core tiles
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st);
+// dense INT4 GEMV on the prepacked layout (1 <= T <= 4, vector ALUs), g.S K splits
+hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st);
+// rearranges a [K/2, N] INT4 matrix and its [K/G, N] scales into the prepacked layout
+hipError_t launch_gemv_prepack(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                               uint8_t* wt, uint16_t* st_, hipStream_t st);
 int ex_max_split_gemv();
 hipError_t launch_dequant(const uint8_t* w, const uint16_t* s, int K, int N, int group, int fmt,
                           float* out, hipStream_t st);

@@ -289,6 +289,53 @@ int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8
                              hipStream_t stream);
 
 /*
+ * Prepacked dense GEMV (eole page, "Packed Marlin projections": projection weights are
+ * rearranged once while the model is prepared for inference, ahead of the decode kernels
+ * that read them).  The same INT4 weights and scales as packed_gemv_int4, stored so that
+ * every workgroup of the GEMV streams one contiguous stretch of memory:
+ *   w_tiled uint8: blocks of 2048 bytes, block (t, b) = byte rows 16 b .. 16 b + 15 (32 K)
+ *     of column tile t (columns 128 t .. 128 t + 127; the last tile padded with zero bytes).
+ *     Inside a block, 128 units of 16 bytes, unit u = 64 h + l (h = 0, 1; l = 0 .. 63,
+ *     q = l % 16, kq = l / 16) hold byte row r = 16 b + 4 kq + 2 h of columns 128 t + 8 q ..
+ *     +7 (8 bytes) followed by row r + 1 of the same columns.  Blocks are ordered by step
+ *     i = b / 16, then tile, then b: with n_i = min(16, K/32 - 16 i) blocks in step i, block
+ *     (t, b) starts at byte 2048 (16 i tiles + t n_i + b - 16 i).  tiles = ceil(N / 128);
+ *     K * 64 bytes per tile in all.
+ *   s_tiled bf16 [K/G][tiles * 128]: s_tiled[g][c] = s[g][c] (0 for c >= N).
+ * The rearrangement is a permutation plus zero padding: the GEMV reads exactly the bytes of
+ * the [K/2, N] layout (plus the padding of a ragged last tile).
+ */
+
+/* Host only: bytes of the prepacked weights and scales for a [K/2, N] INT4 matrix with group
+ * G.  Sizes as for packed_gemv_int4 (T = 1); DQG_ERR_UNSUPPORTED otherwise. */
+int packed_gemv_int4_prepack_sizes(int K, int N, int group, size_t* w_bytes, size_t* s_bytes);
+
+/*
+ * packed_gemv_int4_prepack -- rearranges w uint8 [K/2, N] and s bf16 [K/G, N] into w_tiled
+ * and s_tiled (sizes from packed_gemv_int4_prepack_sizes; every byte of both is written).
+ * Asynchronous on `stream`; the inputs are only read.  All four pointers 16-byte aligned.
+ */
+int packed_gemv_int4_prepack(const uint8_t* w, const uint16_t* s, int K, int N, int group,
+                             uint8_t* w_tiled, uint16_t* s_tiled, hipStream_t stream);
+
+/*
+ * packed_gemv_int4_tiled -- the dense packed INT4 GEMV of packed_gemv_int4 (same
+ * y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation,
+ * same bounds on x) on the prepacked weights, for 1 <= T <= 4 tokens on vector-ALU dot2
+ * tiles (more return DQG_ERR_UNSUPPORTED).  x bf16 [T, K], y bf16 [T, N].  The workspace is
+ * that of packed_gemv_int4 for T tokens (size from packed_gemv_int4_workspace_bytes, the
+ * same contract: zero-filled before first use, left zero-filled by every completed call,
+ * error word bit 1 when a wait between workgroups gave up, NULL for no K split); one
+ * workspace may serve both calls.  Deterministic; for T <= 2 the summation order is that of
+ * packed_gemv_int4 (bitwise identical results), for T = 3, 4 it differs from packed_gemv_int4's
+ * matrix-core tiles (agreement within rounding).  Calls that may run at the same time must
+ * not share a workspace.
+ */
+int packed_gemv_int4_tiled(const uint16_t* x, int T, int K, int N, const uint8_t* w_tiled,
+                           const uint16_t* s_tiled, int group, uint16_t* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * packed_dequant_f32 -- TEST AID: dequantize one packed matrix with the same in-register
  * decode the compute kernels use.  w uint8 [K/2, N] (FP8: [K, N]), s bf16 [K/G, N] -> out
  * fp32 [K, N], out[k, n] = value(code[k, n]) * s[k/G, n], exact.

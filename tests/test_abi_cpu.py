@@ -191,6 +191,30 @@ def test_gemv_validation():
     assert f(A, 1, 5120, 8192, A, A, 128, A, A, 16, None) == B.DQG_ERR_WORKSPACE
 
 
+def test_tiled_gemv_sizes_and_validation():
+    """Prepacked sizes (tiles of 128 columns, the last padded) and host-side rejection before
+    any launch."""
+    wb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    q = B.LIB.packed_gemv_int4_prepack_sizes
+    assert q(5120, 34816, 128, ctypes.byref(wb), ctypes.byref(sb)) == B.DQG_OK
+    assert wb.value == 5120 // 2 * 34816 and sb.value == 5120 // 128 * 34816 * 2
+    assert q(96, 320, 32, ctypes.byref(wb), ctypes.byref(sb)) == B.DQG_OK
+    assert wb.value == 3 * 96 * 64 and sb.value == 3 * 3 * 256   # 3 tiles, 64 columns padded
+    assert q(5120, 100, 128, ctypes.byref(wb), ctypes.byref(sb)) == B.DQG_ERR_UNSUPPORTED
+    assert q(5120, 256, 128, None, ctypes.byref(sb)) == B.DQG_ERR_INVALID_ARG
+    p = B.LIB.packed_gemv_int4_prepack
+    assert p(0, A, 5120, 256, 128, A, A, None) == B.DQG_ERR_INVALID_ARG
+    assert p(A, A, 5120, 100, 128, A, A, None) == B.DQG_ERR_UNSUPPORTED
+    assert p(A, A, 5120, 256, 128, MIS, A, None) == B.DQG_ERR_MISALIGNED
+    f = B.LIB.packed_gemv_int4_tiled
+    assert f(0, 1, 5120, 256, A, A, 128, A, 0, 0, None) == B.DQG_ERR_INVALID_ARG
+    assert f(A, 5, 5120, 256, A, A, 128, A, 0, 0, None) == B.DQG_ERR_UNSUPPORTED   # T > 4
+    assert f(A, 1, 5120, 100, A, A, 128, A, 0, 0, None) == B.DQG_ERR_UNSUPPORTED
+    assert f(A, 1, 5120, 256, A, MIS, 128, A, 0, 0, None) == B.DQG_ERR_MISALIGNED
+    # a workspace that is given but too small is an error (NULL means "no K split")
+    assert f(A, 1, 5120, 8192, A, A, 128, A, A, 16, None) == B.DQG_ERR_WORKSPACE
+
+
 def test_dequant_validation():
     f = B.LIB.packed_dequant_f32
     assert f(0, A, 64, 64, 32, 0, A, None) == B.DQG_ERR_INVALID_ARG
