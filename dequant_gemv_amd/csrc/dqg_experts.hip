@@ -1167,9 +1167,10 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 }
 
 // ======================================================================================
-// Dense packed INT4 GEMV for one or two tokens, on the vector ALUs (FastInfer page,
-// "Specialized matrix-vector result"; eole page, "Packed Marlin projections" for the fused
-// gate/up width).
+// Dense packed INT4 GEMV for one or two tokens, on the vector ALUs, and on prepacked weights
+// for one to four tokens (FastInfer page, "Specialized matrix-vector result"; eole page,
+// "Packed Marlin projections" for the fused gate/up width and for weights rearranged once
+// while the model is prepared for inference).
 //
 // Grid: 128-column tile fastest, then the K split, then one finisher workgroup per tile.  A
 // lane owns 8 columns and, in each block of 16 byte rows, the 4 rows 4 kq .. 4 kq + 3; a wave
@@ -1183,18 +1184,39 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // x[odd]) of each 8 K values (n - 8 against the 1024- and 64-based magic pairs).  A wave sums
 // its 4 blocks before it applies the group scale (G = 128: one per chunk and column; G = 32:
 // one per block).  With two tokens each decoded pair meets both tokens' activations.
+//
+// PRE = true reads the prepacked layout: blocks of 2048 bytes holding exactly the 16-byte
+// pieces a wave's lanes take from one block, lane l at 16 l (rows 4 kq, 4 kq + 1) and at
+// 1024 + 16 l (rows 4 kq + 2, 4 kq + 3), 8 columns each; blocks ordered by round of 16, then
+// tile.  A workgroup's round is then one contiguous 32 KB stretch right after the previous
+// workgroup's, and each load instruction reads 1 KB contiguous (the [K/2, N] layout spreads
+// a round over 256 row segments of 128 bytes).  Scales [K/G][tiles x 128].  With one token,
+// the same arithmetic in the same order as the [K/2, N] call.
+//
+// MF = true (2 to 4 tokens, prepacked weights): the same decoded fp16 pairs become the B
+// operand of v_mfma_f32_16x16x32_f16 instead of meeting each token in dot2.  Lane (q, kq)
+// holds K group kq of its 8 columns 8 q + i, which is the B operand of one 16x16x32 product
+// over the 16 columns 8 q' + i (one product per i); the A operand is token q's paired
+// activations of group kq (zero rows past the tokens), and the accumulator input is each
+// token's bias term summed over the scale group (a lane-group sum at staging), so the
+// decode's 1024 / 64 offsets cancel exactly as on the vector ALUs.  The decode is shared by
+// every token; what the tokens add is one matrix-core product per column and block.
 // ======================================================================================
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
 constexpr int GV_MAX_T = 2;   // tokens of the vector-ALU GEMV (more take matrix cores)
-constexpr int GV_PRE_MAX_T = 4;  // tokens of the vector-ALU GEMV on prepacked weights
+constexpr int GV_PRE_MAX_T = 4;  // tokens of the GEMV on prepacked weights
 
-template <int G, int NT, bool PRE>
+template <int G, int NT, bool PRE, bool MF = false>
 __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   // activations of a round, per token and 8 K: (x0,x2),(x1,x3),(x4,x6),(x5,x7) and the bias
   __shared__ __align__(16) uint4 xs[NT][GV_ROUND * 4];
   __shared__ float cs[NT][GV_ROUND * 4];
-  __shared__ __align__(16) float red[4][4][NT][128];     // [wave][row lane][token][column]
+  // matrix-core body: the bias of each token summed per scale group of the round (G = 128:
+  // a wave's 4 blocks; G = 32: one block)
+  __shared__ float bs[MF ? NT : 1][GV_ROUND];
+  __shared__ __align__(16) float red[4][MF ? 1 : 4][NT][128];  // [wave][row lane][token][column]
   static_assert(NT * GV_ROUND * 4 <= EX_THREADS, "one activation group per thread");
+  static_assert(!MF || NT == 4, "the matrix-core body serves 2 to 4 tokens");
   const int K = g.K, N = g.N, S = g.S, Tc = g.t_cap;  // g.T <= NT
   const int tiles = (N + 127) / 128;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63, q = l & 15, kq = l >> 4;
@@ -1244,6 +1266,11 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
   for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[tt][i] = 0.0f;
+  float macc[MF ? 8 : 1][4];  // matrix-core body: [column i][token 4 kq + r]
+#pragma unroll
+  for (int i = 0; i < (MF ? 8 : 1); ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) macc[i][r] = 0.0f;
   for (int r0 = blk0; r0 < blk1; r0 += GV_ROUND) {
     // The round's activations are loaded before its weights: in-order completion then lets
     // the staging threads convert them while the weights are still in flight.  Groups past
@@ -1298,9 +1325,60 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
       float c = dot2p<FMT_INT4>(e0, m1032, 0.0f);
       c = dot2p<FMT_INT4>(o0, m72, c);
       c = dot2p<FMT_INT4>(e1, m1032, c);
-      cs[xt][xg] = dot2p<FMT_INT4>(o1, m72, c);
+      c = dot2p<FMT_INT4>(o1, m72, c);
+      cs[xt][xg] = c;
+      if constexpr (MF) {  // sum the group's bias terms over the lanes of one scale group
+        constexpr int W = G == 128 ? 16 : 4;  // 8-K groups per scale group
+#pragma unroll
+        for (int m = 1; m < W; m <<= 1) c += __shfl_xor(c, m, W);
+        if ((xg & (W - 1)) == 0) bs[xt][xg / W] = c;
+      }
     }
     __syncthreads();
+    if constexpr (MF) {
+      // lane (q, kq): A = token q's 8 K values of group kq (zero past the tokens), B = the
+      // 8 K values of column 8 q + i, one 16x16x32 product per column i: the 16 columns
+      // 8 q' + i of a product are the lanes' i-th columns.  D rows 4 kq .. 4 kq + 3 are
+      // tokens; the accumulator input carries the tokens' bias term of the scale group.
+      f32x4_t D[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gi = (4 * wv + j) * 4 + kq;
+        const uint4 av = q < NT ? xs[q][gi] : make_uint4(0u, 0u, 0u, 0u);
+        if (G != 128 || j == 0) {
+          f32x4_t c0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            c0[r] = 4 * kq + r < NT ? bs[4 * kq + r][G == 128 ? wv : 4 * wv + j] : 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) D[i] = c0;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
+          uint32_t bv[4];
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
+            const uint32_t p =
+                __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+            bv[2 * pp] = (p & M_LO) | F_LO;
+            bv[2 * pp + 1] = (p & M_HI) | F_HI;
+          }
+          const u32x4_t B = {bv[0], bv[1], bv[2], bv[3]};
+          D[i] = mfma_16x16x32<FMT_INT4>(av, B, D[i]);
+        }
+        if (G != 128 || j == 3) {
+          float sf[8];
+          scales8(sc[G == 128 ? 0 : j], sf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) macc[i][r] = fmaf(sf[i], D[i][r], macc[i][r]);
+        }
+      }
+      continue;
+    }
     float d[NT][8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1340,17 +1418,30 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
       }
     }
   }
+  if constexpr (MF) {
+    if (kq == 0)  // tokens 0 .. 3
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[wv][kq][tt][8 * q + i] = acc[tt][i];
+        for (int i = 0; i < 8; ++i) red[wv][0][r][8 * q + i] = macc[i][r];
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wv][kq][tt][8 * q + i] = acc[tt][i];
+  }
   __syncthreads();
   for (int it = tid; it < NT * 128; it += EX_THREADS) {
     const int t = it >> 7, c = it & 127;
     if (t >= g.T || c >= ncols) continue;
     float v = 0.0f;
+    if constexpr (MF) {
 #pragma unroll
-    for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][t][c];
+      for (int p = 0; p < 4; ++p) v += red[p][0][t][c];
+    } else {
+#pragma unroll
+      for (int p = 0; p < 16; ++p) v += red[p >> 2][p & 3][t][c];
+    }
     if (S == 1)
       g.y[(size_t)t * N + 128 * tile + c] = f32_to_bf16(v + 0.0f);
     else
@@ -1396,8 +1487,8 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
 
 int ex_max_split_gemv() { return EX_MAX_SPLIT_GEMV; }
 
-// the vector-ALU GEMV on the prepacked layout: 1, 2 or 4 tokens per pass (3 run the 4-token
-// instance), whole rounds per split as launch_gemv_ex
+// the GEMV on the prepacked layout: one token on the vector ALUs, 2 to 4 tokens on the
+// matrix-core body of the same kernel; whole rounds per split as launch_gemv_ex
 hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st) {
   if (g.T < 1 || g.T > GV_PRE_MAX_T) return hipErrorInvalidValue;
   GemvArgs h = g;
@@ -1406,16 +1497,17 @@ hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st) {
   h.wb = GV_ROUND * ((per + GV_ROUND - 1) / GV_ROUND);
   h.S = (nblk + h.wb - 1) / h.wb;
   const dim3 grid(tiles * h.S + (h.S > 1 ? tiles : 0)), block(EX_THREADS);
-#define DQG_GT_LAUNCH(GG, NN) \
-  hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true>), grid, block, 0, st, h)
+  // one token: the vector-ALU body; 2 to 4 tokens: the matrix-core body (measured at
+  // N = 34816: 2 tokens 20.6-21.4 vs 22.3-22.6 us, 4 tokens 22.3 vs 30.0 us; one token
+  // 20.0 vs 18.9 us, the products of three zero rows do not pay for the saved dot2 work)
+#define DQG_GT_LAUNCH(GG, NN, MM) \
+  hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true, MM>), grid, block, 0, st, h)
   if (g.group == 128) {
-    if (g.T == 1) DQG_GT_LAUNCH(128, 1);
-    else if (g.T == 2) DQG_GT_LAUNCH(128, 2);
-    else DQG_GT_LAUNCH(128, 4);
+    if (g.T == 1) DQG_GT_LAUNCH(128, 1, false);
+    else DQG_GT_LAUNCH(128, 4, true);
   } else {
-    if (g.T == 1) DQG_GT_LAUNCH(32, 1);
-    else if (g.T == 2) DQG_GT_LAUNCH(32, 2);
-    else DQG_GT_LAUNCH(32, 4);
+    if (g.T == 1) DQG_GT_LAUNCH(32, 1, false);
+    else DQG_GT_LAUNCH(32, 4, true);
   }
 #undef DQG_GT_LAUNCH
   return hipGetLastError();

@@ -321,15 +321,16 @@ int packed_gemv_int4_prepack(const uint8_t* w, const uint16_t* s, int K, int N, 
 /*
  * packed_gemv_int4_tiled -- the dense packed INT4 GEMV of packed_gemv_int4 (same
  * y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation,
- * same bounds on x) on the prepacked weights, for 1 <= T <= 4 tokens on vector-ALU dot2
- * tiles (more return DQG_ERR_UNSUPPORTED).  x bf16 [T, K], y bf16 [T, N].  The workspace is
+ * same bounds on x) on the prepacked weights, for 1 <= T <= 4 tokens: one token on
+ * vector-ALU dot2 tiles, 2 to 4 on fp16 matrix-core tiles with fp32 accumulation (more return
+ * DQG_ERR_UNSUPPORTED).  x bf16 [T, K], y bf16 [T, N].  The workspace is
  * that of packed_gemv_int4 for T tokens (size from packed_gemv_int4_workspace_bytes, the
  * same contract: zero-filled before first use, left zero-filled by every completed call,
  * error word bit 1 when a wait between workgroups gave up, NULL for no K split); one
- * workspace may serve both calls.  Deterministic; for T <= 2 the summation order is that of
- * packed_gemv_int4 (bitwise identical results), for T = 3, 4 it differs from packed_gemv_int4's
- * matrix-core tiles (agreement within rounding).  Calls that may run at the same time must
- * not share a workspace.
+ * workspace may serve both calls.  Deterministic; for T = 1 the summation order is that of
+ * packed_gemv_int4 (bitwise identical results), for T >= 2 it differs from packed_gemv_int4's
+ * (agreement within rounding).  Calls that may run at the same time must not share a
+ * workspace.
  */
 int packed_gemv_int4_tiled(const uint16_t* x, int T, int K, int N, const uint8_t* w_tiled,
                            const uint16_t* s_tiled, int group, uint16_t* y, void* workspace,
