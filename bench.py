@@ -676,10 +676,8 @@ def bench_gemv(w, args, dev, stream, B):
         raise SystemExit(f"bench: timed GEMV outside the tolerance ({ratio:.3f})")
     abytes = (K // 2) * N + (K // G) * N * 2
     gbps = abytes / (us * 1e-6) / 1e9
-    # one or two tokens run the paired-row vector-ALU kernel, more tokens the matrix-core
-    # tiles of the expert kernels' E = 1 case
-    # (prepacked weights: the same vector-ALU kernel for up to 4 tokens)
-    kernel = "gemv_tok_kernel" if (T <= 2 or tiled) else "gemv_ex_kernel"
+    # (up to 4 tokens: gemv_tok_kernel, its matrix-core body from 2 tokens, either layout)
+    kernel = "gemv_tok_kernel" if T <= 4 else "gemv_ex_kernel"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                 "traffic": read_traffic(kernel, args.workload), "bytes_per_launch": abytes,

@@ -24,11 +24,10 @@ constexpr int kMaxTK = 65536;
 // take its multiply-adds off the vector ALU, which bounds the vector-ALU tiles (measured
 // best at 2 against 1, 3, 5, 9 and 16 on the batched Q30 layers and the T = 4 GEMV).
 constexpr int kMfmaMinTokens = 2;
-// dense GEMV: calls with at most this many tokens run the vector-ALU kernel, more tokens the
-// matrix-core tiles (measured at N = 8192 and 34816, K = 5120: vector ALUs 23.8 / 9.6 us
-// against 30.4 / 11.7 us at 2 tokens; matrix cores ahead from 4 tokens on, where each pass
-// of two more tokens costs the vector-ALU kernel about a weight stream of dot2 work)
-constexpr int kGemvValuMaxTokens = 2;
+// dense GEMV: calls with at most this many tokens run gemv_tok_kernel (one token on its
+// vector ALUs, 2 to 4 on its matrix-core body, which decodes each weight once for all
+// tokens), more tokens the expert tiles' E = 1 case (16- or 32-row matrix-core tiles)
+constexpr int kGemvTokMaxTokens = 4;
 constexpr int kMaxSplitDown = 16;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -269,7 +268,7 @@ void gemv_layout(GemvPlan& g, int K, int N, int t_cap) {
 GemvPlan plan_gemv(int T, int K, int N, size_t ws_bytes = 0) {
   GemvPlan g{};
   g.tiles = (N + 127) / 128;
-  g.mt = (T <= kGemvValuMaxTokens) ? 0 : (T <= 16 ? 1 : 2);
+  g.mt = (T <= kGemvTokMaxTokens) ? 0 : (T <= 16 ? 1 : 2);
   gemv_layout(g, K, N, T);
   if (ws_bytes > g.total && g.total > 0) {
     int lo = T, hi = 4096;

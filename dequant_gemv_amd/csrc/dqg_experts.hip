@@ -1167,8 +1167,8 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 }
 
 // ======================================================================================
-// Dense packed INT4 GEMV for one or two tokens, on the vector ALUs, and on prepacked weights
-// for one to four tokens (FastInfer page, "Specialized matrix-vector result"; eole page,
+// Dense packed INT4 GEMV for one to four tokens: one on the vector ALUs, two to four on
+// matrix cores sharing the same decode, on the [K/2, N] or the prepacked layout (FastInfer page, "Specialized matrix-vector result"; eole page,
 // "Packed Marlin projections" for the fused gate/up width and for weights rearranged once
 // while the model is prepared for inference).
 //
@@ -1193,7 +1193,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // a round over 256 row segments of 128 bytes).  Scales [K/G][tiles x 128].  With one token,
 // the same arithmetic in the same order as the [K/2, N] call.
 //
-// MF = true (2 to 4 tokens, prepacked weights): the same decoded fp16 pairs become the B
+// MF = true (2 to 4 tokens, either layout): the same decoded fp16 pairs become the B
 // operand of v_mfma_f32_16x16x32_f16 instead of meeting each token in dot2.  Lane (q, kq)
 // holds K group kq of its 8 columns 8 q + i, which is the B operand of one 16x16x32 product
 // over the 16 columns 8 q' + i (one product per i); the A operand is token q's paired
@@ -1203,7 +1203,7 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // every token; what the tokens add is one matrix-core product per column and block.
 // ======================================================================================
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
-constexpr int GV_MAX_T = 2;   // tokens of the vector-ALU GEMV (more take matrix cores)
+constexpr int GV_MAX_T = 4;   // tokens of this kernel (more take the expert tiles' E = 1 case)
 constexpr int GV_PRE_MAX_T = 4;  // tokens of the GEMV on prepacked weights
 
 template <int G, int NT, bool PRE, bool MF = false>
@@ -1456,8 +1456,8 @@ static int valu_width(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : EX_
 
 hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
   if (mt == 0) {
-    // vector-ALU tokens: whole rounds of GV_ROUND blocks per split, at most the plan's S
-    // splits; one instance per token count
+    // gemv_tok_kernel: one token on the vector ALUs, 2 to 4 on its matrix-core body; whole
+    // rounds of GV_ROUND blocks per split, at most the plan's S splits
     if (g.T < 1 || g.T > GV_MAX_T) return hipErrorInvalidValue;
     GemvArgs h = g;
     const int nblk = g.K / 32, tiles = (g.N + 127) / 128;
@@ -1467,10 +1467,10 @@ hipError_t launch_gemv_ex(const GemvArgs& g, int mt, hipStream_t st) {
     const dim3 grid1(tiles * h.S + (h.S > 1 ? tiles : 0));
     if (g.group == 128) {
       if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<128, 1, false>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<128, 2, false>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<128, 4, false, true>), grid1, dim3(EX_THREADS), 0, st, h);
     } else {
       if (g.T == 1) hipLaunchKernelGGL((gemv_tok_kernel<32, 1, false>), grid1, dim3(EX_THREADS), 0, st, h);
-      else hipLaunchKernelGGL((gemv_tok_kernel<32, 2, false>), grid1, dim3(EX_THREADS), 0, st, h);
+      else hipLaunchKernelGGL((gemv_tok_kernel<32, 4, false, true>), grid1, dim3(EX_THREADS), 0, st, h);
     }
     return hipGetLastError();
   }
@@ -1499,7 +1499,8 @@ hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st) {
   const dim3 grid(tiles * h.S + (h.S > 1 ? tiles : 0)), block(EX_THREADS);
   // one token: the vector-ALU body; 2 to 4 tokens: the matrix-core body (measured at
   // N = 34816: 2 tokens 20.6-21.4 vs 22.3-22.6 us, 4 tokens 22.3 vs 30.0 us; one token
-  // 20.0 vs 18.9 us, the products of three zero rows do not pay for the saved dot2 work)
+  // 20.0 vs 18.9 us, the products of three zero rows do not pay for the saved dot2 work);
+  // the same instances as launch_gemv_ex on the [K/2, N] layout, so both calls agree bitwise
 #define DQG_GT_LAUNCH(GG, NN, MM) \
   hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true, MM>), grid, block, 0, st, h)
   if (g.group == 128) {

@@ -255,8 +255,9 @@ size_t packed_gemv_int4_workspace_bytes(int T, int K, int N, int group);
  *   x  bf16 [T, K];  w uint8 [K/2, N];  s bf16 [K/G, N];  y bf16 [T, N] out
  *   y[t, n] = bf16_rne( sum_k x[t,k] * (nibble[k,n] - 8) * s[k/G, n] ), fp32 accumulation.
  * x must satisfy |x| < 65504 (the INT4 tiles multiply in fp16 with fp32 accumulation;
- * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).  T >= 2
- * runs on fp16 MFMA tiles, T = 1 on vector-ALU dot2 tiles.  When the query returns a non-zero size the call splits K
+ * bf16 values convert to fp16 exactly above 2^-14 and within 2^-25 below).  T = 1 runs on
+ * vector-ALU dot2 tiles, T >= 2 on fp16 MFMA tiles (T <= 4: each weight decoded once for
+ * all tokens).  When the query returns a non-zero size the call splits K
  * across workgroups: pass a workspace of at least that many bytes, zero-filled before its
  * first use; every completed call leaves it zero-filled again, and one workspace serves
  * calls with any T up to the T it was sized for.  Its first int32 is an error word (bit 1:
@@ -327,10 +328,9 @@ int packed_gemv_int4_prepack(const uint8_t* w, const uint16_t* s, int K, int N, 
  * that of packed_gemv_int4 for T tokens (size from packed_gemv_int4_workspace_bytes, the
  * same contract: zero-filled before first use, left zero-filled by every completed call,
  * error word bit 1 when a wait between workgroups gave up, NULL for no K split); one
- * workspace may serve both calls.  Deterministic; for T = 1 the summation order is that of
- * packed_gemv_int4 (bitwise identical results), for T >= 2 it differs from packed_gemv_int4's
- * (agreement within rounding).  Calls that may run at the same time must not share a
- * workspace.
+ * workspace may serve both calls.  Deterministic, and the arithmetic and summation order
+ * are those of packed_gemv_int4 for the same T: the two calls give bitwise identical results.
+ * Calls that may run at the same time must not share a workspace.
  */
 int packed_gemv_int4_tiled(const uint16_t* x, int T, int K, int N, const uint8_t* w_tiled,
                            const uint16_t* s_tiled, int group, uint16_t* y, void* workspace,

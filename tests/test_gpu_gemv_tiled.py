@@ -161,10 +161,12 @@ def test_tiled_deterministic_and_workspace_reusable():
     assert int(ws[:4].view(torch.int32).item()) == 0
 
 
-@pytest.mark.parametrize("T,N,group", [(1, 34816, 128), (1, 320, 32), (1, 8192, 128)])
+@pytest.mark.parametrize("T,N,group", [(1, 34816, 128), (1, 320, 32), (1, 8192, 128),
+                                       (2, 34816, 128), (3, 320, 32), (4, 8192, 128),
+                                       (4, 34816, 128)])
 def test_tiled_equals_plain_bitwise(T, N, group):
-    """One token: the prepacked call runs the plain call's kernel on the same values in the
-    same order, so the outputs are identical bit for bit."""
+    """The prepacked call runs the plain call's kernel instance on the same values in the same
+    order (only the load addresses differ), so the outputs are identical bit for bit."""
     B = _b()
     g = S.make_gemv(S.GemvConfig("b", T=T, K=5120, N=N, group=group), seed=4)
     x, w, s = dev(g.x), dev(g.w), dev(g.s)
