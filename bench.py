@@ -44,6 +44,8 @@ WORKLOADS = {
                              scales=(0.002, 0.01), logits="normal+bias", layers=48),
     "q30_moe_layer_t16": dict(kind="moe", T=16, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                               scales=(0.002, 0.01), logits="normal+bias", layers=24),
+    "q30_moe_layer_t32": dict(kind="moe", T=32, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                              scales=(0.002, 0.01), logits="normal+bias", layers=16),
     "q30_moe_layer_t64": dict(kind="moe", T=64, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                               scales=(0.002, 0.01), logits="normal+bias", layers=12),
     "w512_stack_t1": dict(kind="moe", T=1, E=512, H=2048, I=512, k=10, group=32, fmt=FP4,
