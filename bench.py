@@ -42,6 +42,8 @@ WORKLOADS = {
                              scales=(0.002, 0.01), logits="normal", layers=48),
     "q30_moe_layer_t4": dict(kind="moe", T=4, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                              scales=(0.002, 0.01), logits="normal+bias", layers=48),
+    "q30_moe_layer_t8": dict(kind="moe", T=8, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
+                             scales=(0.002, 0.01), logits="normal+bias", layers=32),
     "q30_moe_layer_t16": dict(kind="moe", T=16, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
                               scales=(0.002, 0.01), logits="normal+bias", layers=24),
     "q30_moe_layer_t32": dict(kind="moe", T=32, E=128, H=2048, I=768, k=8, group=32, fmt=FP4,
