@@ -1189,8 +1189,9 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 //
 // PRE = true reads the prepacked layout: blocks of 2048 bytes holding exactly the 16-byte
 // pieces a wave's lanes take from one block, lane l at 16 l (rows 4 kq, 4 kq + 1) and at
-// 1024 + 16 l (rows 4 kq + 2, 4 kq + 3), 8 columns each; blocks ordered by round of 16, then
-// tile.  A workgroup's round is then one contiguous 32 KB stretch right after the previous
+// 1024 + 16 l (rows 4 kq + 2, 4 kq + 3), 8 columns each, the two rows' bytes interleaved per
+// column pair so that the decode needs one shift per 4 bytes instead of a byte permute per 2
+// (row_pair); blocks ordered by round of 16, then tile.  A workgroup's round is then one contiguous 32 KB stretch right after the previous
 // workgroup's, and each load instruction reads 1 KB contiguous (the [K/2, N] layout spreads
 // a round over 256 row segments of 128 bytes).  Scales [K/G][tiles x 128].  With one token,
 // the same arithmetic in the same order as the [K/2, N] call.
@@ -1204,6 +1205,24 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_ex_kernel(GemvArgs g) {
 // decode's 1024 / 64 offsets cancel exactly as on the vector ALUs.  The decode is shared by
 // every token; what the tokens add is one matrix-core product per column and block.
 // ======================================================================================
+// Byte c = i of rows r (bits 0-7) and r + 1 (bits 16-23) of the lane's row pair pp in block j,
+// ready for the nibble and-or (the other bits are masked off).  [K/2, N] layout: one byte
+// permute per column.  Prepacked: the unit already holds rows r and r + 1 of columns 2m, 2m + 1
+// as (r, 2m), (r, 2m + 1), (r + 1, 2m), (r + 1, 2m + 1) in dword m, so column 2m is that dword
+// and column 2m + 1 the dword shifted by 8: one shift per two columns.
+template <bool PRE>
+__device__ __forceinline__ uint32_t row_pair(const uint2 (&w)[16], int j, int pp, int i) {
+  const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
+  if constexpr (PRE) {
+    const int m = i >> 1;
+    const uint32_t d = m == 0 ? ra.x : m == 1 ? ra.y : m == 2 ? rb.x : rb.y;
+    return (i & 1) ? d >> 8 : d;
+  } else {
+    const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
+    return __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+  }
+}
+
 constexpr int GV_ROUND = 16;  // blocks per round of a workgroup: 4 waves x 4 blocks
 constexpr int GV_MAX_T = 4;   // tokens of this kernel (more take the expert tiles' E = 1 case)
 constexpr int GV_PRE_MAX_T = 4;  // tokens of the GEMV on prepacked weights
@@ -1360,13 +1379,10 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
           uint32_t bv[4];
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
-            const uint32_t p =
-                __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+            const uint32_t p = row_pair<PRE>(w, j, pp, i);
             bv[2 * pp] = (p & M_LO) | F_LO;
             bv[2 * pp + 1] = (p & M_HI) | F_HI;
           }
@@ -1399,12 +1415,9 @@ __global__ void __launch_bounds__(EX_THREADS) gemv_tok_kernel(GemvArgs g) {
       // each pair is decoded once and meets every token
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (uint32_t)(i & 3) | ((uint32_t)((i & 3) + 4) << 16);
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const uint2 ra = w[4 * j + 2 * pp], rb = w[4 * j + 2 * pp + 1];
-          const uint32_t p =
-              __builtin_amdgcn_perm(i < 4 ? rb.x : rb.y, i < 4 ? ra.x : ra.y, sel);
+          const uint32_t p = row_pair<PRE>(w, j, pp, i);
           const uint32_t lo = (p & M_LO) | F_LO, hi = (p & M_HI) | F_HI;
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
@@ -1506,14 +1519,19 @@ hipError_t launch_gemv_tiled(const GemvArgs& g, hipStream_t st) {
   // N = 34816: 2 tokens 20.6-21.4 vs 22.3-22.6 us, 4 tokens 22.3 vs 30.0 us; one token
   // 20.0 vs 18.9 us, the products of three zero rows do not pay for the saved dot2 work);
   // the same instances as launch_gemv_ex on the [K/2, N] layout, so both calls agree bitwise
-#define DQG_GT_LAUNCH(GG, NN, MM) \
-  hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true, MM>), grid, block, 0, st, h)
+  // The one-token instance on this layout needs 78 registers and would run 6 waves per SIMD;
+  // it is held at 4 workgroups per compute unit (the occupancy of the [K/2, N] instance) by
+  // reserving unused LDS up to 39 KB per workgroup: with more workgroups in flight the call
+  // is slower (measured: 6 waves per SIMD 18.85 vs 18.51 us at N = 34816).
+  constexpr size_t kT1Lds = 39 * 1024 - 9472;  // 9472 bytes: the instance's own LDS
+#define DQG_GT_LAUNCH(GG, NN, MM, LDS) \
+  hipLaunchKernelGGL((gemv_tok_kernel<GG, NN, true, MM>), grid, block, LDS, st, h)
   if (g.group == 128) {
-    if (g.T == 1) DQG_GT_LAUNCH(128, 1, false);
-    else DQG_GT_LAUNCH(128, 4, true);
+    if (g.T == 1) DQG_GT_LAUNCH(128, 1, false, kT1Lds);
+    else DQG_GT_LAUNCH(128, 4, true, 0);
   } else {
-    if (g.T == 1) DQG_GT_LAUNCH(32, 1, false);
-    else DQG_GT_LAUNCH(32, 4, true);
+    if (g.T == 1) DQG_GT_LAUNCH(32, 1, false, kT1Lds);
+    else DQG_GT_LAUNCH(32, 4, true, 0);
   }
 #undef DQG_GT_LAUNCH
   return hipGetLastError();
@@ -1544,7 +1562,9 @@ __global__ void __launch_bounds__(256) gemv_prepack_kernel(const uint8_t* __rest
       if (c < N) {
         const uint2 a = *reinterpret_cast<const uint2*>(w + (size_t)r * N + c);
         const uint2 b2 = *reinterpret_cast<const uint2*>(w + (size_t)(r + 1) * N + c);
-        v = make_uint4(a.x, a.y, b2.x, b2.y);
+        // dword m: (r, 2m), (r, 2m + 1), (r + 1, 2m), (r + 1, 2m + 1) of the 8 columns
+        v = make_uint4((a.x & 0xFFFFu) | (b2.x << 16), (a.x >> 16) | (b2.x & 0xFFFF0000u),
+                       (a.y & 0xFFFFu) | (b2.y << 16), (a.y >> 16) | (b2.y & 0xFFFF0000u));
       }
       reinterpret_cast<uint4*>(wt)[u] = v;
     } else {

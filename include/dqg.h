@@ -297,8 +297,9 @@ int packed_gemv_int4_noalloc(const uint16_t* x, int T, int K, int N, const uint8
  *   w_tiled uint8: blocks of 2048 bytes, block (t, b) = byte rows 16 b .. 16 b + 15 (32 K)
  *     of column tile t (columns 128 t .. 128 t + 127; the last tile padded with zero bytes).
  *     Inside a block, 128 units of 16 bytes, unit u = 64 h + l (h = 0, 1; l = 0 .. 63,
- *     q = l % 16, kq = l / 16) hold byte row r = 16 b + 4 kq + 2 h of columns 128 t + 8 q ..
- *     +7 (8 bytes) followed by row r + 1 of the same columns.  Blocks are ordered by step
+ *     q = l % 16, kq = l / 16) hold byte rows r = 16 b + 4 kq + 2 h and r + 1 of columns
+ *     c = 128 t + 8 q .. +7: bytes 4 m .. 4 m + 3 (m = 0 .. 3) are (r, c + 2 m),
+ *     (r, c + 2 m + 1), (r + 1, c + 2 m), (r + 1, c + 2 m + 1).  Blocks are ordered by step
  *     i = b / 16, then tile, then b: with n_i = min(16, K/32 - 16 i) blocks in step i, block
  *     (t, b) starts at byte 2048 (16 i tiles + t n_i + b - 16 i).  tiles = ceil(N / 128);
  *     K * 64 bytes per tile in all.
