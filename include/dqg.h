@@ -327,10 +327,10 @@ int packed_gemv_int4_prepack(const uint8_t* w, const uint16_t* s, int K, int N, 
  * vector-ALU dot2 tiles, 2 to 4 on fp16 matrix-core tiles with fp32 accumulation (more return
  * DQG_ERR_UNSUPPORTED; so do prepacked weights of 2 GiB or more, ceil(N/128) K 64 bytes, which
  * the kernel addresses with 32-bit offsets).  x bf16 [T, K], y bf16 [T, N].  All pointers
- * 16-byte aligned.  The workspace is that of packed_gemv_int4 for T tokens (size from packed_gemv_int4_workspace_bytes, the
- * same contract: zero-filled before first use, left zero-filled by every completed call,
- * error word bit 1 when a wait between workgroups gave up, NULL for no K split); one
- * workspace may serve both calls.  Deterministic, and the arithmetic and summation order
+ * 16-byte aligned.  The workspace is that of packed_gemv_int4 for T tokens (size from
+ * packed_gemv_int4_workspace_bytes, the same contract: zero-filled before first use, left
+ * zero-filled by every completed call, error word bit 1 when a wait between workgroups gave
+ * up, NULL for no K split); one workspace may serve both calls.  Deterministic, and the arithmetic and summation order
  * are those of packed_gemv_int4 for the same T: the two calls give bitwise identical results.
  * Calls that may run at the same time must not share a workspace.
  */
